@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV cache hot path on one MI355X.
+
+A step is one pass of the whole path for one batch of sequences: every
+sequence appends one token (host block allocator: slot, new block every 16th
+token, copy-on-write pairs), the copy-on-write block copies run, the new
+token's K/V are written into its slot, and paged decode attention runs over
+each sequence's whole cached context (plus the log-sum-exp merge when the
+sequence is split into partitions).
+
+The host allocator's results for all steps are computed before the timed
+region and uploaded, so the timed steps read resident inputs; the allocator's
+own cost is reported separately (host_alloc_us_per_step).  The timed steps are
+captured in one HIP graph and replayed once.  Several disjoint batches from
+one block pool are used in rotation so that the working set exceeds the 256 MB
+Infinity Cache and the KV reads come from HBM (stand-in for the per-layer
+caches of a real model).
+
+value = KV bytes read per step / step time (GB/s).  roofline: the decode
+kernel's algorithmic bytes per launch / its average duration (HIP events
+around a graph of back-to-back decode launches on the launch stream).
+cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged-attn decode KV-read GB/s (% of MI355X HBM peak) + decoded seqs/s"
+EB = {"f32": 4, "f16": 2, "i8": 1, "e4m3": 1}
+
+
+def _workloads():
+    from synth import workloads as W
+    return {
+        # name: (factory(replica) -> Workload, replicas, pool blocks or None)
+        "c2": (lambda r: W.c2_qwen3_32b_layer(seed_offset=r), 8, 12480),
+        "c3": (lambda r: W.c3_long_context(), 1, None),
+        "c4_i8": (lambda r: W.c4_quantized("i8"), 2, None),
+        "c4_e4m3": (lambda r: W.c4_quantized("e4m3"), 2, None),
+        "c5": (lambda r: W.c5_shared_prefix(), 2, 8192),
+        "c5_cow": (lambda r: W.c5_shared_prefix(cow_pairs=True), 2, 8192),
+        "c1": (lambda r: W.c1_tiny(), 1, None),
+    }
+
+
+def kv_bytes(lens, w) -> int:
+    """Algorithmic bytes one decode launch must move (KV, scales, q, out, tables, lens)."""
+    lens = np.asarray(lens, np.int64)
+    tok = int(lens.sum())
+    b = tok * w.num_kv_heads * 2 * w.head_dim * EB[w.cache_dtype]
+    if w.cache_dtype in ("i8", "e4m3"):
+        b += tok * w.num_kv_heads * 2 * 2
+    b += len(lens) * w.num_heads * w.head_dim * (EB[w.q_dtype] + EB[w.out_dtype])
+    b += 4 * int(np.sum((lens + 15) // 16)) + 4 * len(lens)
+    return b
+
+
+def kv_read_bytes(lens, w) -> int:
+    tok = int(np.asarray(lens, np.int64).sum())
+    b = tok * w.num_kv_heads * 2 * w.head_dim * EB[w.cache_dtype]
+    if w.cache_dtype in ("i8", "e4m3"):
+        b += tok * w.num_kv_heads * 2 * 2
+    return b
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """Time the oracle (as it stands) on the first sequences of one batch."""
+    import oracle
+    from oracle.replay import replay as oracle_replay
+    ro = oracle_replay(w)
+    n = len(w.decode_seqs)
+    lens = ro.seq_lens
+    # smallest prefix of the batch whose fp64 decode takes a measurable time
+    k = min(n, 4)
+    reps, elapsed, used = 0, 0.0, 1
+    while True:
+        t0 = time.perf_counter()
+        _, used = oracle.decode(ro.pools, ro.q[:k], ro.block_tables[:k], lens[:k],
+                                np.float32(w.scale))
+        dt = time.perf_counter() - t0
+        if dt < 0.5 and k < n and reps == 0:
+            k = min(n, k * 4)
+            continue
+        reps += 1
+        elapsed += dt
+        if elapsed >= budget_s or reps >= 3:
+            break
+    per = elapsed / reps
+    b = kv_read_bytes(lens[:k], w)
+    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": int(used),
+            "kind": "oracle",
+            "sample": f"{k} of {n} sequences of one batch ({int(lens[:k].sum())} tokens), "
+                      f"fp64, {reps} run(s), {per:.3f} s per run",
+            "seqs_per_s": round(k / per, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(_workloads()))
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="partition size in tokens (-1: the workload's, 0: library choice)")
+    ap.add_argument("--replicas", type=int, default=0, help="rotating batches (0: default)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
+              f"multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_387_amd as pkv
+    from paged_kv_cache_387_amd import driver
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pkv.lib()
+    torch.cuda.set_device(0)
+    factory, replicas, pool = _workloads()[args.workload]
+    R = args.replicas or replicas
+    ws = [factory(r) for r in range(R)]
+    w0 = ws[0]
+    K, Wm = args.steps, args.warmup
+    total_steps = Wm + K
+    growth = -(-total_steps // R) + 1
+    max_len = max(max(int(op[2]) for op in w.ops if op[0] == "allocate") for w in ws)
+    maxb = -(-(max_len + growth) // 16)
+    need_blocks = sum(sum(-(-int(op[2]) // 16) for op in w.ops if op[0] == "allocate")
+                      for w in ws)
+    num_blocks = pool or int(math.ceil((need_blocks + R * len(w0.decode_seqs) * (growth // 16 + 2))
+                                       * 1.1))
+    if pool and num_blocks == w0.num_blocks:
+        order = w0.free_order
+    else:
+        from synth import permutation, stream_key
+        order = permutation(stream_key(w0.seed, "bench_pool"), num_blocks)
+    part = w0.partition_size if args.partition < 0 else args.partition
+    print(f"# setup {args.workload}: {R} batch(es) of {w0.num_seqs} seqs, pool {num_blocks} "
+          f"blocks, table width {maxb}, partition {part}", file=sys.stderr, flush=True)
+
+    alloc = pkv.BlockAllocator(num_blocks, 16, order)
+    cache = pkv.PagedKVCache(num_blocks, w0.num_kv_heads, w0.head_dim, w0.cache_dtype)
+    OFF = 1 << 24
+    batches = []
+    for r, w in enumerate(ws):
+        driver.replay(w, alloc=alloc, cache=cache, seq_offset=r * OFF, stop_at_step=True)
+        seqs = [s + r * OFF for s in w.decode_seqs]
+        q = torch.from_numpy(w.query()).cuda()
+        rng = np.random.default_rng(r)
+        newk = torch.from_numpy(rng.standard_normal(
+            (len(seqs), w.num_kv_heads, w.head_dim)).astype(np.float16)).cuda()
+        newv = torch.from_numpy(rng.standard_normal(
+            (len(seqs), w.num_kv_heads, w.head_dim)).astype(np.float16)).cuda()
+        if w.src_dtype == "f32":
+            newk, newv = newk.float(), newv.float()
+        odt = torch.float16 if w.out_dtype == "f16" else torch.float32
+        out = torch.empty((len(seqs), w.num_heads, w.head_dim), dtype=odt, device="cuda")
+        batches.append(dict(seqs=seqs, q=q, k=newk, v=newv, out=out))
+    torch.cuda.synchronize()
+
+    # host allocator for every step, ahead of time
+    steps = []
+    t_host = 0.0
+    for i in range(total_steps):
+        b = batches[i % R]
+        t0 = time.perf_counter()
+        slots, pairs = alloc.append_slots(b["seqs"])
+        tables, lens = alloc.export_tables(b["seqs"], maxb)
+        t_host += time.perf_counter() - t0
+        steps.append(dict(b=i % R, slots=torch.from_numpy(slots).cuda(),
+                          pairs=torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
+                          if len(pairs) else None, npairs=len(pairs),
+                          tables=torch.from_numpy(tables).cuda(),
+                          lens=torch.from_numpy(lens).cuda(), lens_host=lens))
+    host_alloc_us = t_host / total_steps * 1e6
+    S, H, D, Hkv = w0.num_seqs, w0.num_heads, w0.head_dim, w0.num_kv_heads
+    workspace = pkv.alloc_workspace(S, H, Hkv, D, maxb, part)
+    scale = float(np.float32(w0.scale))
+    torch.cuda.synchronize()
+
+    def run_step(st):
+        b = batches[st["b"]]
+        if st["pairs"] is not None:
+            pkv.paged_copy_blocks(cache, st["pairs"])
+        pkv.paged_kv_write(b["k"], b["v"], st["slots"], cache)
+        pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale, out=b["out"],
+                                   partition_size=part, workspace=workspace)
+
+    for st in steps[:Wm]:
+        run_step(st)
+    torch.cuda.synchronize()
+
+    timed = steps[Wm:]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.no_graph:
+        torch.cuda.synchronize()
+        ev0.record()
+        for st in timed:
+            run_step(st)
+        ev1.record()
+        torch.cuda.synchronize()
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in timed:
+                run_step(st)
+        g.replay()                      # untimed: first launch of the graph
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+    step_ms = ev0.elapsed_time(ev1) / K
+    bytes_step = np.mean([kv_read_bytes(st["lens_host"], w0) for st in timed])
+    alg_step = np.mean([kv_bytes(st["lens_host"], w0) for st in timed])
+    value = bytes_step / (step_ms * 1e-3) / 1e9
+
+    # decode kernel alone: back-to-back launches in a graph, HIP events around it
+    last = {}
+    for st in timed:
+        last[st["b"]] = st
+    dec_steps = [last[i % R] for i in range(K)] if len(last) == R else timed
+    single_pass = pkv.workspace_bytes(S, H, Hkv, D, maxb, part) == 0
+
+    def run_decode(st):
+        b = batches[st["b"]]
+        pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale, out=b["out"],
+                                   partition_size=part, workspace=workspace)
+
+    gd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gd):
+        for st in dec_steps:
+            run_decode(st)
+    gd.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    gd.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    dec_ms = ev0.elapsed_time(ev1) / len(dec_steps)
+    dec_alg = np.mean([kv_bytes(st["lens_host"], w0) for st in dec_steps])
+    achieved = dec_alg / (dec_ms * 1e-3) / 1e9
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt")
+    if os.path.exists(tpath):
+        import hashlib
+        src = b"".join(open(os.path.join(ROOT, "paged_kv_cache_387_amd", "csrc", f), "rb").read()
+                       for f in ("decode.hip",))
+        sha = hashlib.sha256(src).hexdigest()[:16]
+        for line in open(tpath):
+            if line.startswith("traffic_bytes_per_launch") and f"source={sha}" in line:
+                traffic = int(line.split()[1])
+
+    mean_len = float(np.mean([st["lens_host"].mean() for st in timed]))
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w0.cache_dtype, "data": "synthetic",
+        "config": {"workload": w0.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": 16, "kv_dtype": w0.cache_dtype,
+                   "mean_seq_len": round(mean_len, 1), "pool_blocks": num_blocks,
+                   "rotating_batches": R, "partition_size": part,
+                   "split_k": not single_pass, "graph": not args.no_graph},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "seqs_per_s": round(S / (step_ms * 1e-3), 1),
+        "tokens_per_s": round(S / (step_ms * 1e-3), 1),
+        "host_alloc_us_per_step": round(host_alloc_us, 2),
+        "decode_kernel_ms": round(dec_ms, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": int(dec_alg)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        wb = factory(0)
+        if args.workload == "c3":
+            from synth import workloads as W
+            wb = W.c3_long_context(num_seqs=1)
+        result["cpu_baseline"] = cpu_baseline(wb, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

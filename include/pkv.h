@@ -1,0 +1,246 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged KV cache and PagedAttention decode for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (pages cited by title/site and section):
+ *  [7yue]   "KV Cache and PagedAttention (vllm-musa)", 7yue.com, m8-l2
+ *  [jsqmd]  "vLLM PagedAttention deep dive and engineering practice", jsqmd.com
+ *  [yunthe] "KV cache quantization and PagedAttention memory configuration", yunthe.com
+ *  [fairy]  "KVcache-learning" tutorial, fairy2021.github.io (chapters s01..s13)
+ *
+ * Conventions for every entry point
+ *  - Plain C types only.  Pointers documented "device" must point to device
+ *    memory of the current HIP device; "host" pointers to host memory.
+ *  - The caller owns every buffer.  The library never allocates device memory
+ *    and keeps no pointer after a call returns.  Device work is enqueued
+ *    asynchronously on `stream` (a hipStream_t passed as void*, NULL = the
+ *    default stream); buffers must stay alive until that work completes.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    negative status means nothing was enqueued (except PKV_EDEVICE, which
+ *    reports a launch failure).  No C++ exception crosses this ABI.
+ *  - Device-side contents (block tables, slot mappings, sequence lengths) are
+ *    the caller's contract; the kernels clamp or skip out-of-range values so
+ *    that no access leaves the buffers, but the numbers produced for such
+ *    entries are unspecified.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKV_OK        0
+#define PKV_EINVAL   (-1)  /* bad argument (shape, pointer, alignment, size) */
+#define PKV_ENOMEM   (-2)  /* block pool exhausted; allocator state unchanged */
+#define PKV_ENOENT   (-3)  /* unknown sequence id */
+#define PKV_EEXIST   (-4)  /* sequence id already exists */
+#define PKV_EDEVICE  (-5)  /* HIP error while launching */
+#define PKV_ENOTSUP  (-6)  /* valid but unsupported (dtype combination, head_dim, GPU arch) */
+
+/* Static text for a status code. */
+const char *pkv_strerror(int status);
+
+/* ---- element types ----------------------------------------------------- */
+#define PKV_F32   0   /* IEEE binary32 */
+#define PKV_F16   1   /* IEEE binary16 */
+#define PKV_I8    3   /* int8 code, symmetric [-127, 127], fp16 scale per (token, kv head) */
+#define PKV_E4M3  4   /* OCP 8-bit float E4M3 (bias 7, max 448), fp16 scale per (token, kv head) */
+
+/* Library version as 10000*major + 100*minor + patch. */
+int pkv_version(void);
+
+/* ========================================================================
+ * KV block pool layout (part of the ABI)
+ *
+ * A physical block holds block_size (= 16) token slots of K and of V for every
+ * kv head: "16 tokens x head_dim x num_kv_heads x 2 (K+V) x dtype bytes"
+ * [7yue, section 2].  The K pool and the V pool are separate buffers, each
+ *   [num_blocks][num_kv_heads][tile],  tile = block_size * head_dim * eb bytes
+ * (eb = element bytes: 4, 2 or 1).  Inside one tile, let j be a byte index into
+ * token t's head_dim-vector (j = d * eb + byte of element d):
+ *   K tile: byte j of token t at ((j / 16) * block_size + t) * 16 + j % 16
+ *           (16-byte columns, token-minor: the split of the K cache into
+ *           [head_dim*eb/16][block_size][16 bytes] of [7yue, section 5])
+ *   V tile: byte j of token t at ((j / 4) * block_size + t) * 4 + j % 4
+ *           (4-byte columns, token-minor)
+ * Scales (PKV_I8 / PKV_E4M3 only): fp16 [num_blocks][num_kv_heads][block_size],
+ * one array for K and one for V.  Slot s of the cache is token position
+ * s % block_size of physical block s / block_size.
+ * ======================================================================== */
+
+/* ========================================================================
+ * Host block allocator (the "Block Manager")
+ *
+ * Fixed-size blocks allocated on demand, returned when a sequence ends
+ * [7yue, section 2]; ceil(n / block_size) blocks for n tokens, capacity checked
+ * before anything is taken, blocks taken from the head of the free list and
+ * freed blocks appended at its tail [jsqmd, section 3.2]; blocks shared between
+ * sequences with copy-on-write: a sequence about to write into a shared block
+ * copies it, writes into the copy and repoints its own table, the others keep
+ * the original [fairy, s05 copy-on-write; s06 alloc / cow / free].  A block's
+ * reference count is the number of table entries that point at it; it returns
+ * to the free list when that count reaches zero.
+ *
+ * Host memory only, no GPU calls.  Not thread-safe: the caller serializes
+ * calls on one allocator.  Every failing call leaves the state unchanged.
+ * ======================================================================== */
+typedef struct pkv_alloc pkv_alloc;
+
+/* Create an allocator over blocks 0 .. num_blocks-1.  free_order (host,
+ * nullable) is a permutation of 0 .. num_blocks-1 giving the initial free-list
+ * order (NULL: ascending).  block_size must be 16.  *out receives the handle. */
+int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order,
+                     pkv_alloc **out);
+void pkv_alloc_destroy(pkv_alloc *a);
+/* Number of free blocks (>= 0), or PKV_EINVAL for a NULL handle. */
+int32_t pkv_alloc_num_free(const pkv_alloc *a);
+/* Copy up to cap free-list entries (head first) into out (host); returns the
+ * free-list length. */
+int32_t pkv_alloc_free_list(const pkv_alloc *a, int32_t *out, int32_t cap);
+/* Reference count of a block (0 = free), or PKV_EINVAL if out of range. */
+int32_t pkv_block_refcount(const pkv_alloc *a, int32_t block);
+
+/* Grow sequence seq_id (created if new) to num_tokens filled tokens, taking
+ * ceil(num_tokens/16) - (blocks held) new blocks ("allocate(seq_id, num_tokens)"
+ * of [jsqmd, section 3.2]).  If the sequence's partly filled tail block is shared
+ * and the call adds tokens to it, that block is first replaced by a private
+ * copy: *cow_src / *cow_dst (host, nullable) receive the pair to copy with
+ * paged_copy_blocks before any write; both are -1 when no copy is needed.
+ * num_tokens <= current length is a no-op.  PKV_ENOMEM if the free list is too
+ * short. */
+int pkv_seq_allocate(pkv_alloc *a, int64_t seq_id, int32_t num_tokens, int32_t *cow_src,
+                     int32_t *cow_dst);
+/* Reserve the slot of the next token of an existing sequence (a new block
+ * every 16th token [fairy, s06 decode-phase allocation]); *slot (host)
+ * receives it.  Copy-on-write as for pkv_seq_allocate. */
+int pkv_seq_append_slot(pkv_alloc *a, int64_t seq_id, int64_t *slot, int32_t *cow_src,
+                        int32_t *cow_dst);
+/* pkv_seq_append_slot for n sequences in order (host arrays).  slots[i]
+ * receives sequence i's slot; the copy pairs are written to cow_pairs as
+ * [src, dst] rows and their count to *num_cow (cow_pairs needs room for n
+ * rows).  Stops at the first failure and returns its status; *num_done
+ * (nullable) receives how many sequences were appended. */
+int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_t *slots,
+                         int32_t *cow_pairs, int32_t *num_cow, int32_t *num_done);
+/* Make child share every block of parent (reference counts + 1). */
+int pkv_seq_fork(pkv_alloc *a, int64_t parent, int64_t child);
+/* Release a sequence; blocks whose count drops to zero go to the free-list tail
+ * in logical order. */
+int pkv_seq_free(pkv_alloc *a, int64_t seq_id);
+/* Current length in tokens. */
+int pkv_seq_len(const pkv_alloc *a, int64_t seq_id, int32_t *len);
+/* Slots of token positions [start, start+count) of a sequence (host out);
+ * the positions must be < the sequence length. */
+int pkv_seq_slots(const pkv_alloc *a, int64_t seq_id, int32_t start, int32_t count,
+                  int64_t *out_slots);
+/* Block tables of n sequences as rows of max_blocks_per_seq int32 entries
+ * (host [n][max_blocks_per_seq], padded with -1) and their lengths (host [n]).
+ * PKV_EINVAL if a table is longer than max_blocks_per_seq. */
+int pkv_export_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
+                      int32_t max_blocks_per_seq, int32_t *out_block_tables,
+                      int32_t *out_seq_lens);
+
+/* ========================================================================
+ * Device operations (gfx950 HIP kernels)
+ * ======================================================================== */
+
+/* Cache write ("append the new token's K/V to the cache" [fairy, s02]; the
+ * per-token slot addressing of the block table [7yue, section 5]).
+ *   key, value:  device, [num_tokens][num_kv_heads][head_dim] of src_dtype
+ *                (PKV_F32 or PKV_F16); row i starts at element i*key_stride
+ *                (value_stride for value); a stride of 0 means num_kv_heads*head_dim.
+ *   slot_mapping: device int64 [num_tokens]; token i goes to slot
+ *                slot_mapping[i]; a negative or >= num_blocks*block_size slot
+ *                skips the token (padding).
+ *   k_cache, v_cache: device pools of cache_dtype in the layout above.
+ *   k_scale, v_scale: device fp16 scale arrays, required for PKV_I8 / PKV_E4M3
+ *                (NULL otherwise).
+ * Conversion: F16<-F16 and F32<-F32 copy bits; F16<-F32 rounds to nearest even;
+ * F32<-F16 widens.  Quantized caches (one scale per (token, kv head), separately
+ * for K and V; "KV Cache scaling factor" [fairy, s09], int8 / fp8 KV [yunthe,
+ * quantization section]):
+ *   a = max_d |x_d|;  s32 = a / 127 (int8) or a / 448 (E4M3), IEEE fp32 division;
+ *   s = fp16(s32) rounded to nearest even, stored as the scale;
+ *   s == 0 -> all codes 0;  int8 code = clamp(rint_even(x_d / s), -127, 127);
+ *   E4M3 code = nearest-even E4M3 of x_d / s, saturating at +-448.
+ *   The dequantized value code * s is exact in fp32.  Source values must be
+ *   finite (and, for PKV_F32 sources, a / 127 or a / 448 must fit in fp16).
+ * Destination slots must be distinct within one call. */
+int paged_kv_write(const void *key, const void *value, int32_t src_dtype,
+                   int64_t key_stride, int64_t value_stride,
+                   const int64_t *slot_mapping, int32_t num_tokens,
+                   void *k_cache, void *v_cache, void *k_scale, void *v_scale,
+                   int32_t cache_dtype, int32_t num_blocks, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, void *stream);
+
+/* Copy-on-write block copy [fairy, s05 copy-on-write; s06 "cow(seq_group,
+ * block_id) -> new_physical_block"]: for each row [src, dst] of block_pairs
+ * (device int32 [num_pairs][2]) copy the whole physical block src to dst -- the
+ * K and V tiles of every kv head and, for quantized caches, their scales.
+ * Rows with src or dst outside [0, num_blocks) or src == dst are skipped.
+ * Destinations must be distinct and must not be sources of the same call.
+ * Enqueue it before the paged_kv_write of the same step, on the same stream. */
+int paged_copy_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale,
+                      int32_t cache_dtype, int32_t num_blocks, const int32_t *block_pairs,
+                      int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, void *stream);
+
+/* Partition size (tokens) paged_attention_decode uses for these shapes when
+ * asked for `requested` (0 = the library's choice); a value >=
+ * max_blocks_per_seq*block_size means one pass per (sequence, kv head). */
+int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t requested);
+
+/* Bytes of device workspace paged_attention_decode needs for these shapes
+ * (0 when every sequence fits one partition). */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size);
+
+/* PagedAttention decode: each sequence's single query token attends over its
+ * cached K/V, reached through its block table [7yue, section 5 kernel entry:
+ * q [num_seqs, num_heads, head_size], block_tables [num_seqs,
+ * max_num_blocks_per_seq], seq_lens [num_seqs]; fairy, s05]:
+ *   out[s][h][:] = softmax_t(scale * q[s][h] . K[s][t]) V[s][t],  t < seq_lens[s]
+ * (the attention formula of [fairy, s01]; paging does not change the math
+ * [jsqmd, section 9]).  Query head h uses kv head h / (num_heads/num_kv_heads)
+ * (grouped-query attention, num_kv_heads <= num_heads [fairy, s11]).
+ *   out:     device [num_seqs][num_heads][head_dim] of out_dtype (F32 or F16).
+ *   query:   device [num_seqs][num_heads][head_dim], q_dtype = F32 when
+ *            cache_dtype is F32, else F16; 16-byte aligned.
+ *   k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks: the pools.
+ *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; entry i is the
+ *            physical block of tokens 16i .. 16i+15.  Entries past
+ *            ceil(seq_len/16) are never read.
+ *   seq_lens: device int32 [num_seqs], tokens already in the cache including
+ *            the one just written; 0 gives a zero output row.
+ *   head_dim 64 or 128; block_size 16; num_heads/num_kv_heads <= 16.
+ *   partition_size: tokens per work unit along the sequence (multiple of
+ *            block_size; 0 = library choice).  Longer sequences are split;
+ *            the partial results (max, sum, weighted V) are merged by a
+ *            log-sum-exp reduction ("partial accumulate, then merge",
+ *            paged_attention_v2 of [jsqmd, section 4.1]).
+ *   workspace: device, >= paged_attention_workspace_bytes(...) bytes,
+ *            256-byte aligned (may be NULL when that size is 0).
+ * Arithmetic: fp32 scores, softmax and accumulation; q.k products on MFMA from
+ * the stored values; int8/E4M3 values are dequantized exactly (code*scale). */
+int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                           const void *k_cache, const void *v_cache, const void *k_scale,
+                           const void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,244 @@
+// C ABI of libpkv: argument validation and dispatch to the gfx950 kernels.
+// Every check runs on the host before anything is enqueued.
+#include <cstring>
+#include <mutex>
+
+#include "pkv_internal.h"
+
+namespace {
+
+using namespace pkv;
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool is_cache_dtype(int t) { return t == PKV_F32 || t == PKV_F16 || t == PKV_I8 || t == PKV_E4M3; }
+bool is_quant(int t) { return t == PKV_I8 || t == PKV_E4M3; }
+
+// The kernels are built for gfx950 only: refuse any other device instead of
+// failing at launch.  Cached per device id.
+int check_device() {
+  static std::mutex mu;
+  static int state[64] = {0};   // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EDEVICE;
+  if (dev < 0 || dev >= 64) return PKV_ENOTSUP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PKV_EDEVICE;
+    state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return state[dev] == 1 ? PKV_OK : PKV_ENOTSUP;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EDEVICE; }
+
+// Partition choice: enough workgroups to cover the 256 compute units several
+// times, at least 4 blocks (one per wavefront) per partition.
+int32_t choose_part_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks,
+                           int32_t requested_tokens) {
+  if (requested_tokens > 0) {
+    int32_t pb = requested_tokens / kBlockSize;
+    return pb >= max_blocks ? max_blocks : pb;
+  }
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int64_t target_wgs = 2048;
+  int64_t parts = units >= target_wgs ? 1 : (target_wgs + units - 1) / units;
+  int64_t pb = (max_blocks + parts - 1) / parts;
+  pb = (pb + kWaves - 1) / kWaves * kWaves;
+  if (pb < kWaves) pb = kWaves;
+  return pb >= max_blocks ? max_blocks : (int32_t)pb;
+}
+
+size_t workspace_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t num_parts) {
+  if (num_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_heads * num_parts;
+  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + rows * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_strerror(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_ENOMEM: return "block pool exhausted";
+    case PKV_ENOENT: return "unknown sequence id";
+    case PKV_EEXIST: return "sequence id already exists";
+    case PKV_EDEVICE: return "HIP device error";
+    case PKV_ENOTSUP: return "unsupported configuration or device";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t requested) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      block_size != kBlockSize || requested < 0 || requested % kBlockSize)
+    return PKV_EINVAL;
+  return choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, requested) * kBlockSize;
+}
+
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || block_size != kBlockSize || partition_size < 0 ||
+      partition_size % kBlockSize)
+    return 0;
+  const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
+                                        partition_size);
+  const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
+  return workspace_for(num_seqs, num_heads, head_dim, parts);
+}
+
+int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                           const void *k_cache, const void *v_cache, const void *k_scale,
+                           const void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || partition_size < 0)
+    return PKV_EINVAL;
+  if (num_heads % num_kv_heads) return PKV_EINVAL;
+  if (block_size != kBlockSize) return PKV_ENOTSUP;
+  if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
+  if (num_heads / num_kv_heads > kMaxGroup) return PKV_ENOTSUP;
+  // grid limits: y = kv heads, z = sequences; token counts stay in int32
+  if (num_seqs > 65535 || num_kv_heads > 65535 || max_blocks_per_seq > (1 << 26))
+    return PKV_ENOTSUP;
+  if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_F16) return PKV_EINVAL;
+  if (q_dtype != (cache_dtype == PKV_F32 ? PKV_F32 : PKV_F16)) return PKV_ENOTSUP;
+  if (partition_size % kBlockSize) return PKV_EINVAL;
+  if (!(scale == scale)) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, elem_bytes(out_dtype)) || !aligned(block_tables, 4) ||
+      !aligned(seq_lens, 4))
+    return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!aligned(k_scale, 8) || !aligned(v_scale, 8)))
+    return PKV_EINVAL;
+
+  const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
+                                        partition_size);
+  const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
+  const size_t need = workspace_for(num_seqs, num_heads, head_dim, parts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return PKV_EINVAL;
+  const int dev = check_device();
+  if (dev != PKV_OK) return dev;
+
+  DecodeParams p;
+  p.out = out;
+  p.q = query;
+  p.k_cache = static_cast<const uint8_t *>(k_cache);
+  p.v_cache = static_cast<const uint8_t *>(v_cache);
+  p.k_scale = static_cast<const uint16_t *>(k_scale);
+  p.v_scale = static_cast<const uint16_t *>(v_scale);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  const size_t rows = (size_t)num_seqs * num_heads * parts;
+  p.ws_o = need ? static_cast<float *>(workspace) : nullptr;
+  p.ws_lse = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                              (rows * head_dim * sizeof(float) + 255) / 256 * 256)
+                  : nullptr;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_heads / num_kv_heads;
+  p.part_blocks = pb;
+  p.num_parts = parts;
+  p.qk_scale = scale * 1.4426950408889634f;
+  return status_of(launch_decode(p, cache_dtype, out_dtype, head_dim,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int paged_kv_write(const void *key, const void *value, int32_t src_dtype, int64_t key_stride,
+                   int64_t value_stride, const int64_t *slot_mapping, int32_t num_tokens,
+                   void *k_cache, void *v_cache, void *k_scale, void *v_scale,
+                   int32_t cache_dtype, int32_t num_blocks, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, void *stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || key_stride < 0 ||
+      value_stride < 0)
+    return PKV_EINVAL;
+  if (num_kv_heads > 65535 || (int64_t)num_blocks * kBlockSize > INT64_MAX / 2)
+    return PKV_ENOTSUP;
+  if (block_size != kBlockSize) return PKV_ENOTSUP;
+  if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16) return PKV_EINVAL;
+  if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (key_stride == 0) key_stride = row;
+  if (value_stride == 0) value_stride = row;
+  if (key_stride < row || value_stride < row) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
+  const size_t se = elem_bytes(src_dtype);
+  if (!aligned(key, se) || !aligned(value, se) || !aligned(slot_mapping, 8) ||
+      !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!aligned(k_scale, 2) || !aligned(v_scale, 2))) return PKV_EINVAL;
+  const int dev = check_device();
+  if (dev != PKV_OK) return dev;
+  WriteParams p;
+  p.key = key;
+  p.value = value;
+  p.key_stride = key_stride;
+  p.value_stride = value_stride;
+  p.slots = slot_mapping;
+  p.k_cache = static_cast<uint8_t *>(k_cache);
+  p.v_cache = static_cast<uint8_t *>(v_cache);
+  p.k_scale = static_cast<uint16_t *>(k_scale);
+  p.v_scale = static_cast<uint16_t *>(v_scale);
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.num_kv_heads = num_kv_heads;
+  return status_of(launch_write(p, src_dtype, cache_dtype, head_dim,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int paged_copy_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale,
+                      int32_t cache_dtype, int32_t num_blocks, const int32_t *block_pairs,
+                      int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, void *stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  if (block_size != kBlockSize) return PKV_ENOTSUP;
+  if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
+  if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
+    return PKV_EINVAL;
+  const int dev = check_device();
+  if (dev != PKV_OK) return dev;
+  CopyParams p;
+  p.k_cache = static_cast<uint8_t *>(k_cache);
+  p.v_cache = static_cast<uint8_t *>(v_cache);
+  p.k_scale = static_cast<uint16_t *>(k_scale);
+  p.v_scale = static_cast<uint16_t *>(v_scale);
+  p.pairs = block_pairs;
+  p.num_pairs = num_pairs;
+  p.num_blocks = num_blocks;
+  p.block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(cache_dtype);
+  p.scale_elems = is_quant(cache_dtype) ? (int64_t)num_kv_heads * kBlockSize : 0;
+  return status_of(launch_copy(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

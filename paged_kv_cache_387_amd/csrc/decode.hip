@@ -1,0 +1,450 @@
+// PagedAttention decode for gfx950 (CDNA4).
+//
+// What is computed: for each sequence s and query head h (kv head h / G),
+//   out[s][h] = softmax_t(scale * q[s][h] . K_t) V_t  over the cached tokens
+// t < seq_len, with K/V reached through the block table (logical block t/16 ->
+// physical block; "KV Cache and PagedAttention (vllm-musa)", 7yue.com,
+// section 5; "KVcache-learning", fairy2021.github.io, s01 and s05).  Long
+// sequences are split into partitions whose partial results are merged with a
+// log-sum-exp reduction ("partial accumulate, then merge" of paged_attention_v2,
+// "vLLM PagedAttention deep dive", jsqmd.com, section 4.1).
+//
+// Work decomposition.  One workgroup = 4 wavefronts handles one (partition,
+// kv head, sequence).  Wave w takes blocks first+w, first+w+4, ... of the
+// partition.  For one 16-token block a wave computes
+//   S^T[t][h] = K[t] . q[h]      one 16x16 MFMA tile: rows = the block's 16
+//                                 tokens, columns = the G <= 16 query heads of
+//                                 the GQA group (columns >= G have q = 0)
+//   online softmax per column (running max m, partial sum l, fp32, base 2)
+//   O^T[d][h] += V^T[d][t] P^T[t][h]   MFMA tiles of 16 head_dim rows
+// The MFMA accumulator layout puts column h = lane % 16 and rows
+// 4*(lane/16)+v (v = 0..3) in lane `lane`; the same registers are the P^T
+// operand of the P.V MFMA (k index = token), so scores never move between
+// lanes except for two cross-row reductions (max over the 16 tokens).
+//
+// Pool layout (see include/pkv.h): a (block, kv head) tile of K stores each
+// token's vector as 16-byte columns, token-minor: 16-byte load number i of lane
+// (r = lane%16, g = lane/16) reads column 4i+g of token r at byte (64i+lane)*16
+// -- one contiguous 1 KiB per wave instruction.  V stores 4-byte columns,
+// token-minor: load i of lane (r, g) reads tokens 4g..4g+3 of column 16i+r at
+// byte (16i+r)*64 + 16g -- again 1 KiB contiguous per instruction.
+//
+// Data types: fp32 KV uses 16x16x4 f32 MFMAs; fp16 KV uses 16x16x32 f16 (q.K)
+// and 16x16x16 f16 (P.V); int8 / E4M3 codes are widened exactly to fp16 and use
+// the fp16 MFMAs, the K scale multiplies the scores and the V scale is folded
+// into P (P' = p * s_v * 64 in fp16; the factor 64 keeps P' out of fp16's
+// subnormal range and is divided out at the end).
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr float kPvBoost = 64.0f;   // fold factor for quantized V scales
+
+template <int KV> struct Kv;
+template <> struct Kv<PKV_F32> { static constexpr int EB = 4; };
+template <> struct Kv<PKV_F16> { static constexpr int EB = 2; };
+template <> struct Kv<PKV_I8> { static constexpr int EB = 1; };
+template <> struct Kv<PKV_E4M3> { static constexpr int EB = 1; };
+
+__device__ __forceinline__ u4 load16(const uint8_t *p) {
+  return *reinterpret_cast<const u4 *>(p);
+}
+
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+// Element bit-casts go through a by-value scalar: __builtin_bit_cast applied
+// directly to a subscripted ext_vector element (vec[j]) compiled to element 0
+// with this compiler.
+__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Two codes (bytes b0, b1 already placed as 0x00b1_00b0 or b1<<24|b0<<8 forms
+// below) to two exact fp16 values.
+// int8: bytes biased by +128 in the low byte of each half, 0x64 in the high
+// byte give 1024 + (c + 128); subtracting 1152 recovers c exactly.
+__device__ __forceinline__ h2 i8pair_to_h2(uint32_t biased_lo_bytes) {
+  return as_h2(biased_lo_bytes | 0x64006400u) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+}
+// E4M3: byte b in the high byte of each half (b << 8).  fp16 bits
+// sign<<15 | (b & 0x7f)<<7 hold the value 2^-8 times the E4M3 value (both
+// exponent fields line up, the biases differ by 8); multiplying by 256 is exact.
+__device__ __forceinline__ h2 e4m3pair_to_h2(uint32_t hi_bytes) {
+  uint32_t bits = (hi_bytes & 0x80008000u) | ((hi_bytes >> 1) & 0x3F803F80u);
+  return as_h2(bits) * h2{(_Float16)256.0f, (_Float16)256.0f};
+}
+
+// 16 codes (one K column) -> two h8 (codes 0-7, 8-15), exact.
+template <int KV>
+__device__ __forceinline__ void codes16_to_h8(u4 w, h8 &lo, h8 &hi) {
+  uint32_t out[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t x = w[k];
+    if constexpr (KV == PKV_I8) {
+      uint32_t u = x ^ 0x80808080u;
+      out[2 * k] = as_u32(i8pair_to_h2(__builtin_amdgcn_perm(0u, u, 0x0c010c00u)));
+      out[2 * k + 1] = as_u32(i8pair_to_h2(__builtin_amdgcn_perm(0u, u, 0x0c030c02u)));
+    } else {
+      out[2 * k] = as_u32(e4m3pair_to_h2(__builtin_amdgcn_perm(0u, x, 0x010c000cu)));
+      out[2 * k + 1] = as_u32(e4m3pair_to_h2(__builtin_amdgcn_perm(0u, x, 0x030c020cu)));
+    }
+  }
+  lo = __builtin_bit_cast(h8, u4{out[0], out[1], out[2], out[3]});
+  hi = __builtin_bit_cast(h8, u4{out[4], out[5], out[6], out[7]});
+}
+
+// Byte e of each of the 4 words (4 tokens of one V column) -> h4, exact.
+template <int KV, int E>
+__device__ __forceinline__ h4 vcodes_to_h4(u4 w) {
+  // perm(src0, src1, sel): result byte i = byte sel[i] of (src0:src1), src1 = bytes 0-3.
+  uint32_t a, b;
+  if constexpr (KV == PKV_I8) {
+    constexpr uint32_t sel = 0x0c000c00u | (uint32_t)(E + 4) << 16 | (uint32_t)E;
+    a = __builtin_amdgcn_perm(w[1] ^ 0x80808080u, w[0] ^ 0x80808080u, sel);
+    b = __builtin_amdgcn_perm(w[3] ^ 0x80808080u, w[2] ^ 0x80808080u, sel);
+    return __builtin_bit_cast(h4, u2{as_u32(i8pair_to_h2(a)), as_u32(i8pair_to_h2(b))});
+  } else {
+    constexpr uint32_t sel = 0x000c000cu | (uint32_t)(E + 4) << 24 | (uint32_t)E << 8;
+    a = __builtin_amdgcn_perm(w[1], w[0], sel);
+    b = __builtin_amdgcn_perm(w[3], w[2], sel);
+    return __builtin_bit_cast(h4, u2{as_u32(e4m3pair_to_h2(a)), as_u32(e4m3pair_to_h2(b))});
+  }
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void *out, size_t idx, float v) {
+  if constexpr (OUT == PKV_F32)
+    reinterpret_cast<float *>(out)[idx] = v;
+  else
+    reinterpret_cast<_Float16 *>(out)[idx] = (_Float16)v;
+}
+
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+template <int KV, int D, int OUT>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
+  constexpr int EB = Kv<KV>::EB;
+  constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
+  constexpr int TILE = kBlockSize * D * EB;   // bytes of one (block, kv head) tile
+  constexpr int NL = D * EB / 64;             // 16-byte loads per lane per K (and V) tile
+  constexpr int NACC = D / 16;                // 16x16 output tiles
+  constexpr int E = 4 / EB;                   // head_dim elements per V word
+  constexpr int LDS_ROW = D + 4;
+
+  __shared__ float lds_o[kWaves][kMaxGroup][LDS_ROW];
+  __shared__ float lds_m[kWaves][kMaxGroup];
+  __shared__ float lds_l[kWaves][kMaxGroup];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int G = p.group;
+  const int H = p.num_heads;
+
+  int L = p.seq_lens[s];
+  L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int nparts_s = (nblk + p.part_blocks - 1) / p.part_blocks;
+  const int first = part * p.part_blocks;
+  if (first >= nblk) {
+    if (part == 0) {  // empty sequence: zero output rows
+      for (int e = threadIdx.x; e < G * D; e += 64 * kWaves)
+        store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
+    }
+    return;
+  }
+  const int last = min(first + p.part_blocks, nblk);
+
+  // ---- q fragment: B operand of the q.K MFMAs (column r = head kvh*G + r) ----
+  const bool head_ok = r < G;
+  const size_t qrow = ((size_t)s * H + kvh * G + (head_ok ? r : 0)) * D;
+  float qf32[NL][4];
+  h8 qf16[NL][QUANT ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if constexpr (KV == PKV_F32) {
+      const float *qp = reinterpret_cast<const float *>(p.q) + qrow + (4 * i + g) * 4;
+      u4 raw = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp)) : u4{0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) qf32[i][jj] = as_f32(raw[jj]);
+    } else if constexpr (KV == PKV_F16) {
+      const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 8;
+      u4 raw = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp)) : u4{0, 0, 0, 0};
+      qf16[i][0] = __builtin_bit_cast(h8, raw);
+    } else {
+      const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 16;
+      u4 r0 = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp)) : u4{0, 0, 0, 0};
+      u4 r1 = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp + 8)) : u4{0, 0, 0, 0};
+      qf16[i][0] = __builtin_bit_cast(h8, r0);
+      qf16[i][QUANT ? 1 : 0] = __builtin_bit_cast(h8, r1);
+    }
+  }
+
+  // ---- per-wave running state ----
+  float m = -INFINITY;   // running max of column r (base-2 scaled scores)
+  float l = 0.0f;        // partial sum of this lane's 4 rows
+  f4 acc[NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t *table = p.block_tables + (size_t)s * p.max_blocks;
+  const size_t kv_head_off = (size_t)kvh * TILE;
+  const size_t block_stride = (size_t)p.num_kv_heads * TILE;
+
+  struct Tile {
+    u4 k[NL];
+    u4 v[NL];
+    u2 ks, vs;   // fp16 scales of tokens 4g..4g+3 (quantized only)
+    bool ok;
+  };
+
+  auto issue = [&](int blk, Tile &t) {
+    int phys = table[blk];
+    t.ok = (unsigned)phys < (unsigned)p.num_blocks;
+    phys = t.ok ? phys : 0;
+    const uint8_t *kb = p.k_cache + (size_t)phys * block_stride + kv_head_off;
+    const uint8_t *vb = p.v_cache + (size_t)phys * block_stride + kv_head_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) t.k[i] = load16(kb + (size_t)(64 * i + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) t.v[i] = load16(vb + (size_t)(16 * i + r) * 64 + 16 * g);
+    if constexpr (QUANT) {
+      const size_t so = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize + 4 * g;
+      t.ks = *reinterpret_cast<const u2 *>(p.k_scale + so);
+      t.vs = *reinterpret_cast<const u2 *>(p.v_scale + so);
+    }
+  };
+
+  auto consume = [&](int blk, Tile &t) {
+    // q.K for the block: S^T[token 4g+v][head r] in sc[v]
+    f4 sc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if constexpr (KV == PKV_F32) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(t.k[i][jj]), qf32[i][jj], sc, 0, 0,
+                                                    0);
+      } else if constexpr (KV == PKV_F16) {
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, t.k[i]), qf16[i][0],
+                                                    sc, 0, 0, 0);
+      } else {
+        h8 lo, hi;
+        codes16_to_h8<KV>(t.k[i], lo, hi);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, qf16[i][0], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qf16[i][QUANT ? 1 : 0], sc, 0, 0, 0);
+      }
+    }
+    if (!t.ok) return;  // table entry outside the pool: block skipped
+    const int tok0 = blk * kBlockSize + 4 * g;
+    const bool partial = (blk + 1) * kBlockSize > L;   // uniform per wave
+    float x[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float f = sc[v] * p.qk_scale;
+      if constexpr (QUANT) {
+        uint32_t word = t.ks[v >> 1];
+        f *= (float)as_h2(word)[v & 1];
+      }
+      x[v] = (partial && tok0 + v >= L) ? -INFINITY : f;
+    }
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, xor16(bm));
+    bm = fmaxf(bm, xor32(bm));
+    const float mn = fmaxf(m, bm);
+    const float alpha = exp2f(m - mn);   // m = -inf on the first block: 0
+    float pr[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pr[v] = exp2f(x[v] - mn);
+    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = mn;
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+
+    // P.V: the lane's pr[v] is P^T[token 4g+v][head r], the B operand as is.
+    u4 vw[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      vw[i] = t.v[i];
+      if (partial) {   // unwritten slots may hold anything: zero them
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vw[i][v] = (tok0 + v < L) ? vw[i][v] : 0u;
+      }
+    }
+    if constexpr (KV == PKV_F32) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(vw[i][jj]), pr[jj], acc[i], 0,
+                                                        0, 0);
+    } else if constexpr (KV == PKV_F16) {
+      const h4 pb = h4{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        // word v = token 4g+v, halves (dim 2c, dim 2c+1) of column c = 16i + r
+        const uint32_t lo01 = __builtin_amdgcn_perm(vw[i][1], vw[i][0], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(vw[i][3], vw[i][2], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(vw[i][1], vw[i][0], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(vw[i][3], vw[i][2], 0x07060302u);
+        acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(h4, u2{lo01, lo23}), pb, acc[2 * i], 0, 0, 0);
+        acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(h4, u2{hi01, hi23}), pb, acc[2 * i + 1], 0, 0, 0);
+      }
+    } else {
+      // unwritten slots may hold a NaN scale: select, do not multiply by p = 0
+      float ps[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sv = (float)as_h2(t.vs[v >> 1])[v & 1];
+        ps[v] = (partial && tok0 + v >= L) ? 0.0f : pr[v] * sv * kPvBoost;
+      }
+      const h4 pb = h4{(_Float16)ps[0], (_Float16)ps[1], (_Float16)ps[2], (_Float16)ps[3]};
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        acc[4 * i + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 0>(vw[i]), pb,
+                                                               acc[4 * i + 0], 0, 0, 0);
+        acc[4 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 1>(vw[i]), pb,
+                                                               acc[4 * i + 1], 0, 0, 0);
+        acc[4 * i + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 2>(vw[i]), pb,
+                                                               acc[4 * i + 2], 0, 0, 0);
+        acc[4 * i + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 3>(vw[i]), pb,
+                                                               acc[4 * i + 3], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- block loop, one block in flight ahead of the one being consumed ----
+  const int nb_w = (last - first > w) ? (last - first - w + kWaves - 1) / kWaves : 0;
+  if (nb_w > 0) {
+    Tile ta, tb;
+    issue(first + w, ta);
+    int it = 0;
+    while (true) {
+      if (it + 1 < nb_w) issue(first + w + (it + 1) * kWaves, tb);
+      consume(first + w + it * kWaves, ta);
+      if (++it >= nb_w) break;
+      if (it + 1 < nb_w) issue(first + w + (it + 1) * kWaves, ta);
+      consume(first + w + it * kWaves, tb);
+      if (++it >= nb_w) break;
+    }
+  }
+
+  // ---- combine the 4 waves through LDS ----
+  l += xor16(l);
+  l += xor32(l);
+  if (g == 0) {
+    lds_m[w][r] = m;
+    lds_l[w][r] = l;
+  }
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) {
+    const int i = a / E, e = a % E;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) lds_o[w][r][E * (16 * i + 4 * g + v) + e] = acc[a][v];
+  }
+  __syncthreads();
+
+  const bool direct = nparts_s == 1;
+  for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) {
+    const int hh = e / D, d = e % D;
+    float M = lds_m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, lds_m[ww][hh]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float c = exp2f(lds_m[ww][hh] - M);
+      num += c * lds_o[ww][hh][d];
+      den += c * lds_l[ww][hh];
+    }
+    float o = num / den;
+    if constexpr (QUANT) o *= (1.0f / kPvBoost);
+    const int h = kvh * G + hh;
+    if (direct) {
+      store_out<OUT>(p.out, ((size_t)s * H + h) * D + d, o);
+    } else {
+      const size_t slot = ((size_t)s * H + h) * p.num_parts + part;
+      p.ws_o[slot * D + d] = o;
+      if (d == 0) p.ws_lse[slot] = M + log2f(den);
+    }
+  }
+}
+
+// Log-sum-exp merge of the partitions of sequences that used more than one.
+template <int D, int OUT>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+  const int kvh = blockIdx.x, s = blockIdx.y;
+  int L = p.seq_lens[s];
+  L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int np = (nblk + p.part_blocks - 1) / p.part_blocks;
+  if (np <= 1) return;   // written directly by the decode kernel
+  const int G = p.group;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int hh = e / D, d = e % D;
+    const int h = kvh * G + hh;
+    const size_t base = ((size_t)s * p.num_heads + h) * p.num_parts;
+    float M = -INFINITY;
+    for (int q = 0; q < np; ++q) M = fmaxf(M, p.ws_lse[base + q]);
+    float num = 0.f, den = 0.f;
+    for (int q = 0; q < np; ++q) {
+      const float c = exp2f(p.ws_lse[base + q] - M);
+      num += c * p.ws_o[(base + q) * D + d];
+      den += c;
+    }
+    store_out<OUT>(p.out, ((size_t)s * p.num_heads + h) * D + d, num / den);
+  }
+}
+
+template <int KV, int D, int OUT>
+hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
+  dim3 grid(p.num_parts, p.num_kv_heads, p.num_seqs);
+  hipLaunchKernelGGL((decode_kernel<KV, D, OUT>), grid, dim3(64 * kWaves), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.num_parts <= 1) return err;
+  hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_kv_heads, p.num_seqs), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t launch_out(const DecodeParams &p, int out_dtype, hipStream_t stream) {
+  return out_dtype == PKV_F32 ? launch_typed<KV, D, PKV_F32>(p, stream)
+                              : launch_typed<KV, D, PKV_F16>(p, stream);
+}
+
+template <int KV>
+hipError_t launch_d(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream) {
+  return head_dim == 64 ? launch_out<KV, 64>(p, out_dtype, stream)
+                        : launch_out<KV, 128>(p, out_dtype, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, int head_dim,
+                         hipStream_t stream) {
+  switch (cache_dtype) {
+    case PKV_F32: return launch_d<PKV_F32>(p, out_dtype, head_dim, stream);
+    case PKV_F16: return launch_d<PKV_F16>(p, out_dtype, head_dim, stream);
+    case PKV_I8: return launch_d<PKV_I8>(p, out_dtype, head_dim, stream);
+    default: return launch_d<PKV_E4M3>(p, out_dtype, head_dim, stream);
+  }
+}
+
+}  // namespace pkv

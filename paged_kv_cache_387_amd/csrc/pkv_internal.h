@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP translation units of libpkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;   // tokens per physical block
+constexpr int kWaves = 4;        // wavefronts per decode workgroup
+constexpr int kMaxGroup = 16;    // query heads per kv head (MFMA column count)
+
+inline int elem_bytes(int dtype) {
+  return dtype == PKV_F32 ? 4 : dtype == PKV_F16 ? 2 : 1;
+}
+
+struct DecodeParams {
+  void *out;
+  const void *q;
+  const uint8_t *k_cache;
+  const uint8_t *v_cache;
+  const uint16_t *k_scale;
+  const uint16_t *v_scale;
+  const int32_t *block_tables;
+  const int32_t *seq_lens;
+  float *ws_o;      // [S][H][num_parts][D] normalized partial outputs
+  float *ws_lse;    // [S][H][num_parts] base-2 log-sum-exp of the partial
+  int num_blocks;
+  int max_blocks;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;        // num_heads / num_kv_heads
+  int part_blocks;  // blocks per partition
+  int num_parts;    // partitions in the grid (ceil(max_blocks / part_blocks))
+  float qk_scale;   // scale * log2(e): scores are kept in base 2
+};
+
+struct WriteParams {
+  const void *key;
+  const void *value;
+  int64_t key_stride;
+  int64_t value_stride;
+  const int64_t *slots;
+  uint8_t *k_cache;
+  uint8_t *v_cache;
+  uint16_t *k_scale;
+  uint16_t *v_scale;
+  int num_tokens;
+  int num_blocks;
+  int num_kv_heads;
+};
+
+struct CopyParams {
+  uint8_t *k_cache;
+  uint8_t *v_cache;
+  uint16_t *k_scale;
+  uint16_t *v_scale;
+  const int32_t *pairs;
+  int num_pairs;
+  int num_blocks;
+  int64_t block_bytes;   // K (or V) bytes of one physical block, all kv heads
+  int64_t scale_elems;   // fp16 scales of one physical block, all kv heads (0: none)
+};
+
+hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, int head_dim,
+                         hipStream_t stream);
+hipError_t launch_write(const WriteParams &p, int src_dtype, int cache_dtype, int head_dim,
+                        hipStream_t stream);
+hipError_t launch_copy(const CopyParams &p, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,128 @@
+"""Replay an allocator/write op script through libpkv.
+
+A script is a list of ops (see `synth.workloads`): ("allocate", seq, n),
+("fork", parent, child), ("free", seq), ("append", seq), ("write", seq, start,
+count) and a ("step",) marker.  Before the marker every op runs on its own;
+after it, the appends run as one batched allocator call, their copy-on-write
+pairs as one `paged_copy_blocks` launch and the writes as one `paged_kv_write`
+launch -- the order a decode step uses on one stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import BlockAllocator, PagedKVCache, paged_copy_blocks, paged_kv_write
+
+
+@dataclass
+class Replay:
+    alloc: BlockAllocator
+    cache: PagedKVCache
+    block_tables: object        # int32 device [S, max_blocks]
+    seq_lens: object            # int32 device [S]
+    query: object               # device [S, H, D]
+    tables_host: np.ndarray
+    lens_host: np.ndarray
+    step_slots: np.ndarray
+    step_pairs: np.ndarray
+    log: list = field(default_factory=list)
+
+
+# positions of sequence ids in each op
+_SEQ_FIELDS = {"allocate": (1,), "fork": (1, 2), "free": (1,), "append": (1,), "write": (1,)}
+
+
+def _to_dev(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to("cuda", non_blocking=False)
+
+
+def replay(w, fill_byte: int | None = 0xFF, stream=None, alloc: BlockAllocator | None = None,
+           cache: PagedKVCache | None = None, seq_offset: int = 0,
+           stop_at_step: bool = False) -> Replay:
+    """Run the script of workload `w`.  `alloc` / `cache` may be shared between
+    several replays (sequence ids are shifted by `seq_offset`); with
+    `stop_at_step` the ops after the ("step",) marker are left out."""
+    if alloc is None:
+        alloc = BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+    if cache is None:
+        cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype,
+                             w.block_size, fill_byte=fill_byte)
+    log, step_slots, step_pairs = [], [], []
+    ops = [tuple([o[0]] + [x + seq_offset if k in _SEQ_FIELDS.get(o[0], ()) else x
+                           for k, x in enumerate(o[1:], start=1)]) for o in w.ops]
+    in_step = False
+    i = 0
+    while i < len(ops):
+        op = ops[i]
+        kind = op[0]
+        if kind == "step":
+            if stop_at_step:
+                break
+            in_step = True
+        elif kind == "allocate":
+            pair = alloc.allocate(op[1], op[2])
+            log.append((op, "ok", pair))
+            if pair is not None:
+                paged_copy_blocks(cache, _to_dev(np.array([pair], np.int32)), stream=stream)
+        elif kind == "fork":
+            alloc.fork(op[1], op[2])
+            log.append((op, "ok", None))
+        elif kind == "free":
+            alloc.free(op[1])
+            log.append((op, "ok", None))
+        elif kind == "append":
+            j = i
+            while j < len(ops) and ops[j][0] == "append" and (in_step or j == i):
+                j += 1
+            seqs = [o[1] for o in ops[i:j]]
+            slots, pairs = alloc.append_slots(seqs)
+            for o, s in zip(ops[i:j], slots.tolist()):
+                log.append((o, "ok", s))
+            if in_step:
+                step_slots.extend(slots.tolist())
+                step_pairs.extend(pairs.tolist())
+            if len(pairs):
+                paged_copy_blocks(cache, _to_dev(pairs.astype(np.int32)), stream=stream)
+            i = j
+            continue
+        elif kind == "write":
+            j = i
+            while j < len(ops) and ops[j][0] == "write" and (in_step or j == i):
+                j += 1
+            ks, vs, ss = [], [], []
+            for o in ops[i:j]:
+                seq, start, count = o[1], o[2], o[3]
+                ss.append(alloc.slots(seq, start, count))
+                owner = w.owner_of(seq - seq_offset, start)
+                ks.append(w.kv_rows("k", owner, start, count))
+                vs.append(w.kv_rows("v", owner, start, count))
+            paged_kv_write(_to_dev(np.concatenate(ks)), _to_dev(np.concatenate(vs)),
+                           _to_dev(np.concatenate(ss).astype(np.int64)), cache, stream=stream)
+            i = j
+            continue
+        else:
+            raise ValueError(op)
+        i += 1
+    tables, lens = alloc.export_tables([s + seq_offset for s in w.decode_seqs],
+                                       w.max_blocks_per_seq)
+    return Replay(alloc=alloc, cache=cache, block_tables=_to_dev(tables),
+                  seq_lens=_to_dev(lens), query=_to_dev(w.query()), tables_host=tables,
+                  lens_host=lens, step_slots=np.asarray(step_slots, np.int64),
+                  step_pairs=np.asarray(step_pairs, np.int32).reshape(-1, 2), log=log)
+
+
+def decode(r: Replay, w, partition_size: int | None = None, out_dtype=None, stream=None):
+    import torch
+    from . import paged_attention_decode
+    odt = {"f32": torch.float32, "f16": torch.float16}[w.out_dtype] if out_dtype is None \
+        else out_dtype
+    ps = w.partition_size if partition_size is None else partition_size
+    return paged_attention_decode(r.query, r.cache, r.block_tables, r.seq_lens,
+                                  float(np.float32(w.scale)), out_dtype=odt, partition_size=ps,
+                                  stream=stream)

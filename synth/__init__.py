@@ -51,12 +51,39 @@ def uniform01(key, start: int, count: int) -> np.ndarray:
     return (u64(key, start, count) >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
 
 
-def normal(key, start: int, count: int) -> np.ndarray:
-    """Standard normals; normal i uses draws 2i and 2i+1 (cosine branch only)."""
-    raw = u64(key, 2 * start, 2 * count).reshape(count, 2)
+def _normal_pairs(key, p0: int, npairs: int) -> np.ndarray:
+    """Box-Muller pairs p0 .. p0+npairs-1: pair p uses draws 2p, 2p+1 and yields
+    normals 2p (cosine branch) and 2p+1 (sine branch)."""
+    raw = u64(key, 2 * p0, 2 * npairs).reshape(npairs, 2)
     u1 = ((raw[:, 0] >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53  # (0, 1]
-    u2 = (raw[:, 1] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
-    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
+    ang = (raw[:, 1] >> np.uint64(11)).astype(np.float64) * (2.0 ** -53 * 2.0 * np.pi)
+    rad = np.sqrt(-2.0 * np.log(u1))
+    out = np.empty((npairs, 2), np.float64)
+    np.multiply(rad, np.cos(ang), out=out[:, 0])
+    np.multiply(rad, np.sin(ang), out=out[:, 1])
+    return out.reshape(-1)
+
+
+_CHUNK_PAIRS = 1 << 21
+
+
+def normal(key, start: int, count: int) -> np.ndarray:
+    """Standard normals start .. start+count-1 of stream `key`."""
+    if count <= 0:
+        return np.empty(0, np.float64)
+    p0, p1 = start // 2, (start + count + 1) // 2
+    npairs = p1 - p0
+    if npairs <= _CHUNK_PAIRS:
+        z = _normal_pairs(key, p0, npairs)
+    else:  # independent chunks of a counter-based stream: same values, several threads
+        from concurrent.futures import ThreadPoolExecutor
+        bounds = list(range(p0, p1, _CHUNK_PAIRS)) + [p1]
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            parts = list(ex.map(lambda ab: _normal_pairs(key, ab[0], ab[1] - ab[0]),
+                                zip(bounds[:-1], bounds[1:])))
+        z = np.concatenate(parts)
+    off = start - 2 * p0
+    return z[off:off + count]
 
 
 def randint(key, start: int, count: int, lo: int, hi: int) -> np.ndarray:

@@ -57,6 +57,7 @@ class Workload:
     partition_size: int = 0           # 0: library default
     content_owner: dict = field(default_factory=dict)  # seq -> list of (pos_lo, pos_hi, owner)
     description: str = ""
+    memo: dict | None = None          # set to {} to keep generated K/V rows for reuse
 
     @property
     def num_seqs(self) -> int:
@@ -76,10 +77,16 @@ class Workload:
     def kv_rows(self, which: str, owner: int, start: int, count: int) -> np.ndarray:
         """K ('k') or V ('v') values of positions [start, start+count) owned by `owner`,
         [count, num_kv_heads, head_dim] in the source dtype."""
+        mk = (which, owner, start, count)
+        if self.memo is not None and mk in self.memo:
+            return self.memo[mk]
         key = stream_key(self.seed, "kv", which, owner)
         row = self.num_kv_heads * self.head_dim
         x = normal(key, start * row, count * row).reshape(count, self.num_kv_heads, self.head_dim)
-        return x.astype(NP_DTYPE[self.src_dtype])
+        x = x.astype(NP_DTYPE[self.src_dtype])
+        if self.memo is not None:
+            self.memo[mk] = x
+        return x
 
     def writes(self):
         """(seq, start, count) of every write in the script, in order."""

@@ -1,0 +1,112 @@
+"""The C-ABI library loads and exports every symbol include/pkv.h declares;
+host-side argument validation (no device work is reached).  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_387_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(pkv_\w+|paged_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_header_declares_what_the_binding_lists():
+    assert _declared() == sorted(pkv.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pkv.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_strerror_and_version():
+    assert pkv.strerror(0) == "ok"
+    for st in (-1, -2, -3, -4, -5, -6):
+        assert pkv.strerror(st) and pkv.strerror(st) != "unknown status"
+    assert pkv.lib().pkv_version() >= 100
+
+
+def test_partition_and_workspace_sizes():
+    # explicit 512-token partitions over 2048-block tables: 64 partitions
+    assert pkv.partition_size(8, 8, 2048, requested=512) == 512
+    ws = pkv.workspace_bytes(8, 64, 8, 128, 2048, partition_size=512)
+    rows = 8 * 64 * 64
+    assert ws == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    # a partition at least as long as the table means a single pass, no workspace
+    assert pkv.partition_size(4, 2, 7, requested=4096) == 7 * 16
+    assert pkv.workspace_bytes(4, 8, 2, 64, 7, partition_size=4096) == 0
+    # the automatic choice is a multiple of 4 blocks (one per wavefront) or the whole table
+    for S, Hkv, mb in [(32, 8, 48), (8, 8, 2048), (64, 8, 512), (1, 1, 3)]:
+        p = pkv.partition_size(S, Hkv, mb)
+        assert p % 16 == 0 and (p // 16 == mb or (p // 16) % 4 == 0)
+    assert pkv.lib().paged_attention_partition_size(1, 1, 4, 16, 24) == pkv.EINVAL
+
+
+def _decode_status(**kw):
+    args = dict(out=1 << 20, out_dtype=pkv.F16, query=1 << 20, q_dtype=pkv.F16,
+                k_cache=1 << 20, v_cache=1 << 20, k_scale=None, v_scale=None,
+                cache_dtype=pkv.F16, num_blocks=64, block_tables=1 << 20, max_blocks=8,
+                seq_lens=1 << 20, num_seqs=2, num_heads=8, num_kv_heads=2, head_dim=128,
+                block_size=16, scale=0.1, partition_size=0, workspace=None, ws_bytes=0)
+    args.update(kw)
+    P = ctypes.c_void_p
+    a = args
+    return pkv.lib().paged_attention_decode(
+        P(a["out"]), a["out_dtype"], P(a["query"]), a["q_dtype"], P(a["k_cache"]),
+        P(a["v_cache"]), P(a["k_scale"]), P(a["v_scale"]), a["cache_dtype"], a["num_blocks"],
+        P(a["block_tables"]), a["max_blocks"], P(a["seq_lens"]), a["num_seqs"],
+        a["num_heads"], a["num_kv_heads"], a["head_dim"], a["block_size"], a["scale"],
+        a["partition_size"], P(a["workspace"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), pkv.ENOTSUP),
+    (dict(block_size=32), pkv.ENOTSUP),
+    (dict(num_heads=9), pkv.EINVAL),
+    (dict(num_heads=64, num_kv_heads=2), pkv.ENOTSUP),       # group of 32 > 16
+    (dict(q_dtype=pkv.F32), pkv.ENOTSUP),
+    (dict(out_dtype=pkv.I8), pkv.EINVAL),
+    (dict(cache_dtype=7), pkv.EINVAL),
+    (dict(cache_dtype=pkv.I8), pkv.EINVAL),                 # scales missing
+    (dict(query=(1 << 20) + 8), pkv.EINVAL),                 # misaligned
+    (dict(partition_size=24), pkv.EINVAL),
+    (dict(partition_size=64), pkv.EINVAL),                   # needs a workspace
+    (dict(num_seqs=-1), pkv.EINVAL),
+    (dict(seq_lens=None), pkv.EINVAL),
+    (dict(scale=float("nan")), pkv.EINVAL),
+    (dict(num_seqs=0), pkv.OK),                              # nothing to do
+])
+def test_decode_argument_validation(kw, status):
+    assert _decode_status(**kw) == status
+
+
+def test_write_and_copy_argument_validation():
+    L = pkv.lib()
+    P = ctypes.c_void_p
+    b = P(1 << 20)
+    # head_dim 96 unsupported; block size 8 unsupported; bad src dtype; stride < row
+    assert L.paged_kv_write(b, b, pkv.F16, 0, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 96,
+                            16, None) == pkv.ENOTSUP
+    assert L.paged_kv_write(b, b, pkv.F16, 0, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 64,
+                            8, None) == pkv.ENOTSUP
+    assert L.paged_kv_write(b, b, pkv.I8, 0, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 64,
+                            16, None) == pkv.EINVAL
+    assert L.paged_kv_write(b, b, pkv.F16, 64, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 64,
+                            16, None) == pkv.EINVAL
+    assert L.paged_kv_write(b, b, pkv.F16, 0, 0, b, 4, b, b, None, None, pkv.E4M3, 8, 2, 64,
+                            16, None) == pkv.EINVAL
+    assert L.paged_kv_write(b, b, pkv.F16, 0, 0, b, 0, b, b, None, None, pkv.F16, 8, 2, 64,
+                            16, None) == pkv.OK
+    assert L.paged_copy_blocks(b, b, None, None, pkv.I8, 8, b, 1, 2, 64, 16, None) == pkv.EINVAL
+    assert L.paged_copy_blocks(b, b, None, None, pkv.F16, 8, b, 0, 2, 64, 16, None) == pkv.OK
+    assert L.paged_copy_blocks(b, b, None, None, pkv.F16, 8, b, -1, 2, 64, 16, None) == pkv.EINVAL
