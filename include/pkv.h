@@ -198,7 +198,8 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t requested);
 
 /* Bytes of device workspace paged_attention_decode needs for these shapes
- * (0 when every sequence fits one partition). */
+ * (0 when every sequence fits one partition): the partial outputs and their
+ * log-sum-exps, fp32. */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                        int32_t num_kv_heads, int32_t head_dim,
                                        int32_t max_blocks_per_seq, int32_t block_size,
@@ -228,7 +229,9 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *            log-sum-exp reduction ("partial accumulate, then merge",
  *            paged_attention_v2 of [jsqmd, section 4.1]).
  *   workspace: device, >= paged_attention_workspace_bytes(...) bytes,
- *            256-byte aligned (may be NULL when that size is 0).
+ *            256-byte aligned (may be NULL when that size is 0); its contents
+ *            on entry do not matter.  Calls that share a workspace must not
+ *            run concurrently (same stream, or otherwise ordered).
  * Arithmetic: fp32 scores, softmax and accumulation; q.k products on MFMA from
  * the stored values; int8/E4M3 values are dequantized exactly (code*scale). */
 int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
@@ -239,6 +242,24 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            float scale, int32_t partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* ========================================================================
+ * Bandwidth diagnostics (measurement helpers, not part of the method)
+ *
+ * A plain streaming read and a plain copy of `bytes` contiguous bytes with
+ * 16-byte accesses over `workgroups` workgroups of 256 threads (grid-stride).
+ * They measure the achievable HBM bandwidth next to the decode kernel's, and
+ * give a copy of known size for scaling hardware byte counters.  src and dst
+ * are device pointers, 16-byte aligned, bytes a multiple of 16; sink is a
+ * device uint32 array of `workgroups` entries that the read writes only in
+ * the astronomically unlikely case that the XOR of the data hits a fixed
+ * value (it exists so the loads cannot be optimized away).  The buffers of a
+ * copy must not overlap.  Asynchronous on `stream`.
+ * ======================================================================== */
+int pkv_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups,
+                    void *stream);
+int pkv_stream_copy(void *dst, const void *src, size_t bytes, int32_t workgroups,
+                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,7 @@ EXPORTS = [
     "pkv_seq_fork", "pkv_seq_free", "pkv_seq_len", "pkv_seq_slots", "pkv_export_tables",
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
     "paged_attention_workspace_bytes", "paged_attention_decode",
+    "pkv_stream_read", "pkv_stream_copy",
 ]
 
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "paged_attention_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
             "paged_attention_decode": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32, P, i32,
                                         i32, i32, i32, i32, f32, i32, P, sz, P], ctypes.c_int),
+            "pkv_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
+            "pkv_stream_copy": ([P, P, sz, i32, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -367,3 +370,25 @@ def paged_attention_decode(query, cache: PagedKVCache, block_tables, seq_lens, s
         cache.block_size, float(scale), partition_size, ws_ptr, ws_len, _stream_ptr(stream)),
         "paged_attention_decode")
     return out
+
+
+# ---------------------------------------------------------------------------
+# bandwidth diagnostics
+# ---------------------------------------------------------------------------
+
+def stream_read(src, sink, workgroups: int, stream=None):
+    """Plain streaming read of the bytes of `src` (measurement helper)."""
+    torch = _torch()
+    n = src.numel() * src.element_size()
+    _check(lib().pkv_stream_read(_dev(src, "src"), n,
+                                 _dev(sink, "sink", torch.int32, workgroups), workgroups,
+                                 _stream_ptr(stream)), "pkv_stream_read")
+
+
+def stream_copy(dst, src, workgroups: int, stream=None):
+    """Plain copy of the bytes of `src` into `dst` (measurement helper)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(lib().pkv_stream_copy(_dev(dst, "dst"), _dev(src, "src"), n, workgroups,
+                                 _stream_ptr(stream)), "pkv_stream_copy")

@@ -33,8 +33,18 @@ int check_device() {
 
 int status_of(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EDEVICE; }
 
-// Partition choice: enough workgroups to cover the 256 compute units several
-// times, at least 4 blocks (one per wavefront) per partition.
+// Tuning constants of the automatic partition choice: tokens are split so
+// that the grid holds about kTargetWorkgroups workgroups, each partition at
+// least kMinPartBlocks blocks long.
+#ifndef PKV_TARGET_WORKGROUPS
+#define PKV_TARGET_WORKGROUPS 1024
+#endif
+#ifndef PKV_MIN_PART_BLOCKS
+#define PKV_MIN_PART_BLOCKS 64
+#endif
+constexpr int64_t kTargetWorkgroups = PKV_TARGET_WORKGROUPS;
+constexpr int32_t kMinPartBlocks = PKV_MIN_PART_BLOCKS;
+
 int32_t choose_part_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks,
                            int32_t requested_tokens) {
   if (requested_tokens > 0) {
@@ -42,19 +52,29 @@ int32_t choose_part_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_b
     return pb >= max_blocks ? max_blocks : pb;
   }
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  const int64_t target_wgs = 2048;
-  int64_t parts = units >= target_wgs ? 1 : (target_wgs + units - 1) / units;
+  int64_t parts = units >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + units - 1) / units;
   int64_t pb = (max_blocks + parts - 1) / parts;
+  if (pb < kMinPartBlocks) pb = kMinPartBlocks;
   pb = (pb + kWaves - 1) / kWaves * kWaves;
-  if (pb < kWaves) pb = kWaves;
   return pb >= max_blocks ? max_blocks : (int32_t)pb;
 }
 
-size_t workspace_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t num_parts) {
-  if (num_parts <= 1) return 0;
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace: [partial outputs][partial lse], each part 256-byte aligned.
+struct WorkspaceLayout {
+  size_t o_off, lse_off, total;
+};
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t num_parts) {
+  WorkspaceLayout w{0, 0, 0};
+  if (num_parts <= 1) return w;
   const size_t rows = (size_t)num_seqs * num_heads * num_parts;
-  const size_t o_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
-  return o_bytes + rows * sizeof(float);
+  w.o_off = 0;
+  w.lse_off = round256(rows * head_dim * sizeof(float));
+  w.total = w.lse_off + rows * sizeof(float);
+  return w;
 }
 
 }  // namespace
@@ -96,7 +116,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
   const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
                                         partition_size);
   const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
-  return workspace_for(num_seqs, num_heads, head_dim, parts);
+  return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
 }
 
 int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
@@ -135,7 +155,11 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
                                         partition_size);
   const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
-  const size_t need = workspace_for(num_seqs, num_heads, head_dim, parts);
+  if ((int64_t)num_seqs * num_heads > INT32_MAX || (int64_t)num_seqs * num_kv_heads > INT32_MAX ||
+      decode_grid(num_seqs * num_kv_heads, parts) > INT32_MAX)
+    return PKV_ENOTSUP;
+  const WorkspaceLayout wl = workspace_layout(num_seqs, num_heads, head_dim, parts);
+  const size_t need = wl.total;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PKV_EINVAL;
   const int dev = check_device();
@@ -150,11 +174,9 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   p.v_scale = static_cast<const uint16_t *>(v_scale);
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
-  const size_t rows = (size_t)num_seqs * num_heads * parts;
-  p.ws_o = need ? static_cast<float *>(workspace) : nullptr;
-  p.ws_lse = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                              (rows * head_dim * sizeof(float) + 255) / 256 * 256)
-                  : nullptr;
+  char *ws = static_cast<char *>(workspace);
+  p.ws_o = need ? reinterpret_cast<float *>(ws + wl.o_off) : nullptr;
+  p.ws_lse = need ? reinterpret_cast<float *>(ws + wl.lse_off) : nullptr;
   p.num_blocks = num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.num_seqs = num_seqs;
@@ -163,6 +185,7 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   p.group = num_heads / num_kv_heads;
   p.part_blocks = pb;
   p.num_parts = parts;
+  p.num_units = num_seqs * num_kv_heads;
   p.qk_scale = scale * 1.4426950408889634f;
   return status_of(launch_decode(p, cache_dtype, out_dtype, head_dim,
                                  static_cast<hipStream_t>(stream)));

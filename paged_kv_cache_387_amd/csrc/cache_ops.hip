@@ -60,26 +60,33 @@ __global__ __launch_bounds__(64) void write_kernel(WriteParams p) {
   const int i = blockIdx.x;
   const int kvh = blockIdx.y;
   const int lane = threadIdx.x;
+  const int64_t ks = p.key_stride, vs = p.value_stride;
+
+  // The source rows and the slot are independent loads: issue all of them
+  // before the slot is examined.
+  float xs[2][PER];
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void *src = which ? p.value : p.key;
+    const size_t row = (size_t)i * (which ? vs : ks) + (size_t)kvh * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane * PER + k;
+      if constexpr (SRC == PKV_F32)
+        xs[which][k] = reinterpret_cast<const float *>(src)[row + d];
+      else
+        xs[which][k] = (float)reinterpret_cast<const _Float16 *>(src)[row + d];
+    }
+  }
   const int64_t slot = p.slots[i];
   if (slot < 0 || slot >= (int64_t)p.num_blocks * kBlockSize) return;
   const int64_t blk = slot / kBlockSize;
   const int t = (int)(slot % kBlockSize);
   const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * TILE;
-  const int64_t ks = p.key_stride, vs = p.value_stride;
 
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const void *src = which ? p.value : p.key;
-    const size_t row = (size_t)i * (which ? vs : ks) + (size_t)kvh * D;
-    float x[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int d = lane * PER + k;
-      if constexpr (SRC == PKV_F32)
-        x[k] = reinterpret_cast<const float *>(src)[row + d];
-      else
-        x[k] = (float)reinterpret_cast<const _Float16 *>(src)[row + d];
-    }
+    const float *x = xs[which];
     uint8_t *pool = (which ? p.v_cache : p.k_cache) + tile;
     if constexpr (KV == PKV_F32 || KV == PKV_F16) {
 #pragma unroll

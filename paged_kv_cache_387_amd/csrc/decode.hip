@@ -59,6 +59,11 @@ template <> struct Kv<PKV_E4M3> { static constexpr int EB = 1; };
 __device__ __forceinline__ u4 load16(const uint8_t *p) {
   return *reinterpret_cast<const u4 *>(p);
 }
+// K/V tiles are read once per step: non-temporal loads keep them from
+// displacing reusable lines (tables, q, shared blocks) and stream faster.
+__device__ __forceinline__ u4 load16_stream(const uint8_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u4 *>(p));
+}
 
 __device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
 // Element bit-casts go through a by-value scalar: __builtin_bit_cast applied
@@ -131,8 +136,24 @@ __device__ __forceinline__ void store_out(void *out, size_t idx, float v) {
 __device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Tiles of K/V (and scales) one wavefront keeps in flight: the ring of
+// prefetched blocks is NB deep.  Registers per tile: 2 * NL * 4 (+4 scales).
+#ifndef PKV_PREFETCH_F32
+#define PKV_PREFETCH_F32 2
+#endif
+#ifndef PKV_PREFETCH_F16
+#define PKV_PREFETCH_F16 3
+#endif
+#ifndef PKV_PREFETCH_Q8
+#define PKV_PREFETCH_Q8 6
+#endif
+template <int KV> struct Prefetch { static constexpr int NB = PKV_PREFETCH_F16; };
+template <> struct Prefetch<PKV_F32> { static constexpr int NB = PKV_PREFETCH_F32; };
+template <> struct Prefetch<PKV_I8> { static constexpr int NB = PKV_PREFETCH_Q8; };
+template <> struct Prefetch<PKV_E4M3> { static constexpr int NB = PKV_PREFETCH_Q8; };
+
 template <int KV, int D, int OUT>
-__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) {
   constexpr int EB = Kv<KV>::EB;
   constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
   constexpr int TILE = kBlockSize * D * EB;   // bytes of one (block, kv head) tile
@@ -140,6 +161,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
   constexpr int NACC = D / 16;                // 16x16 output tiles
   constexpr int E = 4 / EB;                   // head_dim elements per V word
   constexpr int LDS_ROW = D + 4;
+  constexpr int NB = Prefetch<KV>::NB;
 
   __shared__ float lds_o[kWaves][kMaxGroup][LDS_ROW];
   __shared__ float lds_m[kWaves][kMaxGroup];
@@ -149,17 +171,59 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+
+  // Workgroup -> (unit, partition).  Workgroups are dealt to the dies round
+  // robin, so all partitions of unit u get ids on die u % kXcds: blocks that
+  // several sequences share (a common prefix) are read through one die's L2
+  // when those sequences' units sit on one die.
+  const int bid = blockIdx.x;
+  const int die_slot = bid / kXcds;
+  const int part = die_slot % p.num_parts;
+  const int u = (die_slot / p.num_parts) * kXcds + bid % kXcds;
+  if (u >= p.num_units) return;
+  const int s = u / p.num_kv_heads;
+  const int kvh = u - s * p.num_kv_heads;
   const int G = p.group;
   const int H = p.num_heads;
+
+  const int first = part * p.part_blocks;
+  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks + first + w;
+
+  // Loads that do not depend on the sequence length go first, so that they
+  // overlap with the read of seq_lens: the table entries of the wave's first
+  // 64 blocks (one per lane; lanes past the row's end re-read its last entry)
+  // and the q fragment (B operand of the q.K MFMAs, column r = head kvh*G+r;
+  // columns r >= G repeat head kvh*G and their results are never stored).
+  int tv_next;
+  {
+    const int col = first + w + lane * kWaves;
+    tv_next = trow[(col < p.max_blocks ? col : p.max_blocks - 1) - first - w];
+  }
+  const size_t qrow = ((size_t)s * H + kvh * G + (r < G ? r : 0)) * D;
+  float qf32[NL][4];
+  h8 qf16[NL][QUANT ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if constexpr (KV == PKV_F32) {
+      const float *qp = reinterpret_cast<const float *>(p.q) + qrow + (4 * i + g) * 4;
+      const u4 raw = load16(reinterpret_cast<const uint8_t *>(qp));
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) qf32[i][jj] = as_f32(raw[jj]);
+    } else if constexpr (KV == PKV_F16) {
+      const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 8;
+      qf16[i][0] = __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp)));
+    } else {
+      const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 16;
+      qf16[i][0] = __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp)));
+      qf16[i][QUANT ? 1 : 0] =
+          __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp + 8)));
+    }
+  }
 
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int nparts_s = (nblk + p.part_blocks - 1) / p.part_blocks;
-  const int first = part * p.part_blocks;
   if (first >= nblk) {
     if (part == 0) {  // empty sequence: zero output rows
       for (int e = threadIdx.x; e < G * D; e += 64 * kWaves)
@@ -169,30 +233,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
   }
   const int last = min(first + p.part_blocks, nblk);
 
-  // ---- q fragment: B operand of the q.K MFMAs (column r = head kvh*G + r) ----
-  const bool head_ok = r < G;
-  const size_t qrow = ((size_t)s * H + kvh * G + (head_ok ? r : 0)) * D;
-  float qf32[NL][4];
-  h8 qf16[NL][QUANT ? 2 : 1];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    if constexpr (KV == PKV_F32) {
-      const float *qp = reinterpret_cast<const float *>(p.q) + qrow + (4 * i + g) * 4;
-      u4 raw = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp)) : u4{0, 0, 0, 0};
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) qf32[i][jj] = as_f32(raw[jj]);
-    } else if constexpr (KV == PKV_F16) {
-      const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 8;
-      u4 raw = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp)) : u4{0, 0, 0, 0};
-      qf16[i][0] = __builtin_bit_cast(h8, raw);
-    } else {
-      const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 16;
-      u4 r0 = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp)) : u4{0, 0, 0, 0};
-      u4 r1 = head_ok ? load16(reinterpret_cast<const uint8_t *>(qp + 8)) : u4{0, 0, 0, 0};
-      qf16[i][0] = __builtin_bit_cast(h8, r0);
-      qf16[i][QUANT ? 1 : 0] = __builtin_bit_cast(h8, r1);
-    }
-  }
+  // Blocks of this wave: first + w + k * kWaves, k < nb_w, walked in chunks of
+  // 64 whose table entries are held one per lane (readlane picks entry j).
+  const int nb_part = last - first;
+  const int nb_w = nb_part > w ? (nb_part - w + kWaves - 1) / kWaves : 0;
+  auto load_tv = [&](int c0) {
+    const int nc = min(64, nb_w - c0);
+    const int tj = lane < nc ? lane : nc - 1;
+    return trow[(size_t)(c0 + tj) * kWaves];
+  };
 
   // ---- per-wave running state ----
   float m = -INFINITY;   // running max of column r (base-2 scaled scores)
@@ -201,7 +250,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t *table = p.block_tables + (size_t)s * p.max_blocks;
   const size_t kv_head_off = (size_t)kvh * TILE;
   const size_t block_stride = (size_t)p.num_kv_heads * TILE;
 
@@ -212,16 +260,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
     bool ok;
   };
 
-  auto issue = [&](int blk, Tile &t) {
-    int phys = table[blk];
+  // Start the loads of a block whose table entry is lane j of tv.
+  auto issue = [&](int tv, int j, Tile &t) {
+    int phys = __builtin_amdgcn_readlane(tv, j);
     t.ok = (unsigned)phys < (unsigned)p.num_blocks;
     phys = t.ok ? phys : 0;
     const uint8_t *kb = p.k_cache + (size_t)phys * block_stride + kv_head_off;
     const uint8_t *vb = p.v_cache + (size_t)phys * block_stride + kv_head_off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) t.k[i] = load16(kb + (size_t)(64 * i + lane) * 16);
+    for (int i = 0; i < NL; ++i) t.k[i] = load16_stream(kb + (size_t)(64 * i + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) t.v[i] = load16(vb + (size_t)(16 * i + r) * 64 + 16 * g);
+    for (int i = 0; i < NL; ++i) t.v[i] = load16_stream(vb + (size_t)(16 * i + r) * 64 + 16 * g);
     if constexpr (QUANT) {
       const size_t so = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize + 4 * g;
       t.ks = *reinterpret_cast<const u2 *>(p.k_scale + so);
@@ -229,6 +278,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
     }
   };
 
+  // Fold block blk (its tile already loaded) into the running state.
   auto consume = [&](int blk, Tile &t) {
     // q.K for the block: S^T[token 4g+v][head r] in sc[v]
     f4 sc = f4{0.f, 0.f, 0.f, 0.f};
@@ -329,23 +379,41 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
     }
   };
 
-  // ---- block loop, one block in flight ahead of the one being consumed ----
-  const int nb_w = (last - first > w) ? (last - first - w + kWaves - 1) / kWaves : 0;
-  if (nb_w > 0) {
-    Tile ta, tb;
-    issue(first + w, ta);
-    int it = 0;
-    while (true) {
-      if (it + 1 < nb_w) issue(first + w + (it + 1) * kWaves, tb);
-      consume(first + w + it * kWaves, ta);
-      if (++it >= nb_w) break;
-      if (it + 1 < nb_w) issue(first + w + (it + 1) * kWaves, ta);
-      consume(first + w + it * kWaves, tb);
-      if (++it >= nb_w) break;
+  // ---- block loop: a ring of NB tiles, each refilled right after use ----
+  // The wave's blocks are walked in chunks of up to 64 (one table entry per
+  // lane).  Within a chunk the steady-state rounds issue every load
+  // unconditionally, so the compiler's wait counts stay exact and NB - 1
+  // tiles remain in flight while one is consumed; only the last round of a
+  // chunk guards its loads.
+  for (int c0 = 0; c0 < nb_w; c0 += 64) {
+    const int nc = min(64, nb_w - c0);
+    const int tv = tv_next;
+    const int blk0 = first + w + c0 * kWaves;   // block of chunk entry 0
+    Tile ring[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) issue(tv, j < nc ? j : nc - 1, ring[j]);
+    int k0 = 0;
+    for (; k0 + 2 * NB <= nc; k0 += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        consume(blk0 + (k0 + j) * kWaves, ring[j]);
+        issue(tv, k0 + j + NB, ring[j]);
+      }
     }
+    // last round: the ring holds entries k0 .. k0+NB-1 (those < nc), at most
+    // NB - 1 further entries remain to be loaded
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (k0 + j < nc) consume(blk0 + (k0 + j) * kWaves, ring[j]);
+      if (k0 + j + NB < nc) issue(tv, k0 + j + NB, ring[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (k0 + NB + j < nc) consume(blk0 + (k0 + NB + j) * kWaves, ring[j]);
+    if (c0 + 64 < nb_w) tv_next = load_tv(c0 + 64);
   }
 
-  // ---- combine the 4 waves through LDS ----
+  // ---- combine the waves through LDS ----
   l += xor16(l);
   l += xor32(l);
   if (g == 0) {
@@ -379,47 +447,83 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeParams p) {
     if (direct) {
       store_out<OUT>(p.out, ((size_t)s * H + h) * D + d, o);
     } else {
-      const size_t slot = ((size_t)s * H + h) * p.num_parts + part;
-      p.ws_o[slot * D + d] = o;
-      if (d == 0) p.ws_lse[slot] = M + log2f(den);
+      const size_t row = ((size_t)s * H + h) * p.num_parts + part;
+      p.ws_o[row * D + d] = o;
+      if (d == 0) p.ws_lse[row] = M + log2f(den);
     }
   }
 }
 
-// Log-sum-exp merge of the partitions of sequences that used more than one.
+// Log-sum-exp merge of the partitions of sequences that used more than one:
+// one workgroup of kMergeThreads per (sequence, query head).  Thread t sums
+// partitions q = t / D, t / D + QG, ... of output element d = t % D; the loop
+// is unrolled so that its loads are in flight together.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
 template <int D, int OUT>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  const int kvh = blockIdx.x, s = blockIdx.y;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
+  constexpr int QG = kMergeThreads / D;   // partition groups
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float part_num[QG][D];
+  __shared__ float part_den[QG];
+  const int row = blockIdx.x;              // s * H + h
+  const int s = row / p.num_heads;
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int np = (nblk + p.part_blocks - 1) / p.part_blocks;
   if (np <= 1) return;   // written directly by the decode kernel
-  const int G = p.group;
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int hh = e / D, d = e % D;
-    const int h = kvh * G + hh;
-    const size_t base = ((size_t)s * p.num_heads + h) * p.num_parts;
-    float M = -INFINITY;
-    for (int q = 0; q < np; ++q) M = fmaxf(M, p.ws_lse[base + q]);
-    float num = 0.f, den = 0.f;
-    for (int q = 0; q < np; ++q) {
-      const float c = exp2f(p.ws_lse[base + q] - M);
-      num += c * p.ws_o[(base + q) * D + d];
-      den += c;
+  const int t = threadIdx.x;
+  const size_t base = (size_t)row * p.num_parts;
+  const float *lse = p.ws_lse + base;
+  const float *o = p.ws_o + base * D;
+
+  float M = -INFINITY;
+  for (int q = t; q < np; q += kMergeThreads) M = fmaxf(M, lse[q]);
+  M = wave_max64(M);
+  if ((t & 63) == 0) red[t >> 6] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
+
+  const int qg = t / D, d = t % D;
+  float num = 0.f, den = 0.f;
+#pragma unroll 8
+  for (int q = qg; q < np; q += QG) {
+    const float c = exp2f(lse[q] - M);
+    num += c * o[(size_t)q * D + d];
+    den += c;
+  }
+  part_num[qg][d] = num;
+  if (d == 0) part_den[qg] = den;
+  __syncthreads();
+  if (t < D) {
+    float n = 0.f, z = 0.f;
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      n += part_num[i][t];
+      z += part_den[i];
     }
-    store_out<OUT>(p.out, ((size_t)s * p.num_heads + h) * D + d, num / den);
+    store_out<OUT>(p.out, (size_t)row * D + t, n / z);
   }
 }
 
 template <int KV, int D, int OUT>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
-  dim3 grid(p.num_parts, p.num_kv_heads, p.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<KV, D, OUT>), grid, dim3(64 * kWaves), 0, stream, p);
+  const int64_t grid = decode_grid(p.num_units, p.num_parts);
+  hipLaunchKernelGGL((decode_kernel<KV, D, OUT>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
+                     stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.num_parts <= 1) return err;
-  hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_kv_heads, p.num_seqs), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_seqs * p.num_heads),
+                     dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

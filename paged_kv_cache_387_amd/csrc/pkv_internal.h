@@ -11,8 +11,12 @@
 namespace pkv {
 
 constexpr int kBlockSize = 16;   // tokens per physical block
-constexpr int kWaves = 4;        // wavefronts per decode workgroup
+#ifndef PKV_WAVES
+#define PKV_WAVES 4
+#endif
+constexpr int kWaves = PKV_WAVES;  // wavefronts per decode workgroup
 constexpr int kMaxGroup = 16;    // query heads per kv head (MFMA column count)
+constexpr int kXcds = 8;         // accelerator complex dies: workgroup i runs on die i % 8
 
 inline int elem_bytes(int dtype) {
   return dtype == PKV_F32 ? 4 : dtype == PKV_F16 ? 2 : 1;
@@ -37,8 +41,15 @@ struct DecodeParams {
   int group;        // num_heads / num_kv_heads
   int part_blocks;  // blocks per partition
   int num_parts;    // partitions in the grid (ceil(max_blocks / part_blocks))
+  int num_units;    // num_seqs * num_kv_heads
   float qk_scale;   // scale * log2(e): scores are kept in base 2
 };
+
+// Grid of the decode kernel: one workgroup per (unit, partition), units
+// padded to a multiple of kXcds.
+inline int64_t decode_grid(int num_units, int num_parts) {
+  return (int64_t)((num_units + kXcds - 1) / kXcds) * kXcds * num_parts;
+}
 
 struct WriteParams {
   const void *key;
