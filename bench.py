@@ -144,6 +144,79 @@ def pmc_copy(nbytes: int = 1 << 30, reps: int = 5) -> int:
     return 0
 
 
+# Sources that determine what one paged_attention_decode call moves: the
+# counter-based traffic figure is used only while these are unchanged.
+DECODE_SOURCES = ("decode.hip", "api.hip", "pkv_internal.h")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_387_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per paged_attention_decode call from the committed counter
+    summary of this workload, or None if absent or taken on other sources."""
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(tpath):
+        return None
+    sha = decode_source_hash()
+    for line in open(tpath):
+        if line.startswith("traffic_bytes_per_launch") and f"source={sha}" in line:
+            return int(line.split()[1])
+    return None
+
+
+def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                      commands):
+    """Write profiles/traffic_<workload>.txt from rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE counter CSVs of the decode run and of the copy calibration run
+    (bench.py --pmc-copy, 1 GiB).  Counters are KiB per dispatch; each is scaled
+    by (true bytes of the copy) / (what the counter read for the copy)."""
+    import csv
+    import collections
+
+    def per_kernel(path):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    def copy_value(path):
+        vals = [v for k, vs in per_kernel(path).items() if "stream_copy_kernel" in k for v in vs]
+        return sum(vals) / len(vals)
+
+    nbytes = 1 << 30
+    f_scale = nbytes / 1024.0 / copy_value(copy_fetch_csv)
+    w_scale = nbytes / 1024.0 / copy_value(copy_write_csv)
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    lines, total = [], 0.0
+    for name in sorted(fetch):
+        if "decode_kernel" not in name and "merge_kernel" not in name:
+            continue
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write.get(name, [0.0])) / max(1, len(write.get(name, [])))
+        b = (fk * f_scale + wk * w_scale) * 1024.0
+        total += b
+        lines.append(f"  {name}\n    dispatches {len(fetch[name])}  FETCH_SIZE {fk:.1f} KiB  "
+                     f"WRITE_SIZE {wk:.1f} KiB  -> {b / 1e6:.3f} MB per dispatch (scaled)")
+    out = [f"# HBM traffic per paged_attention_decode call, workload {workload}",
+           "# commands (run from the repository root on the GPU host):"]
+    out += [f"#   {c}" for c in commands]
+    out += [f"copy calibration: 1 GiB copy reads FETCH_SIZE {copy_value(copy_fetch_csv):.1f} KiB, "
+            f"WRITE_SIZE {copy_value(copy_write_csv):.1f} KiB -> scale fetch x{f_scale:.4f}, "
+            f"write x{w_scale:.4f}", "kernels:"] + lines
+    out.append(f"traffic_bytes_per_launch {int(round(total))} source={decode_source_hash()}")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,7 +233,15 @@ def main():
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run the plain copy kernel (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.txt from rocprofv3 counter CSVs "
+                         "(no GPU needed)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize-traffic: command line that produced a CSV")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        return summarize_traffic(args.workload, *args.summarize_traffic, args.command)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
               f"multi-GPU path.", file=sys.stderr)
@@ -302,16 +383,7 @@ def main():
     dec_alg = np.mean([kv_bytes(st["lens_host"], w0) for st in dec_steps])
     achieved = dec_alg / (dec_ms * 1e-3) / 1e9
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt")
-    if os.path.exists(tpath):
-        import hashlib
-        src = b"".join(open(os.path.join(ROOT, "paged_kv_cache_387_amd", "csrc", f), "rb").read()
-                       for f in ("decode.hip",))
-        sha = hashlib.sha256(src).hexdigest()[:16]
-        for line in open(tpath):
-            if line.startswith("traffic_bytes_per_launch") and f"source={sha}" in line:
-                traffic = int(line.split()[1])
+    traffic = read_traffic(args.workload)
 
     mean_len = float(np.mean([st["lens_host"].mean() for st in timed]))
     result = {
