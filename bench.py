@@ -6,7 +6,9 @@ sequence appends one token (host block allocator: slot, new block every 16th
 token, copy-on-write pairs), the copy-on-write block copies run, the new
 token's K/V are written into its slot, and paged decode attention runs over
 each sequence's whole cached context (plus the log-sum-exp merge when the
-sequence is split into partitions).
+sequence is split into partitions).  By default the device part of a step is
+one paged_decode_step call (copy, write and decode fused in one launch);
+--unfused runs paged_copy_blocks + paged_kv_write + paged_attention_decode.
 
 The host allocator's results for all steps are computed before the timed
 region and uploaded, so the timed steps read resident inputs; the allocator's
@@ -227,6 +229,9 @@ def main():
                     help="partition size in tokens (-1: the workload's, 0: library choice)")
     ap.add_argument("--replicas", type=int, default=0, help="rotating batches (0: default)")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as copy + write + decode launches instead of the fused "
+                         "paged_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-ceiling", action="store_true",
@@ -306,10 +311,11 @@ def main():
     for i in range(total_steps):
         b = batches[i % R]
         t0 = time.perf_counter()
-        slots, pairs = alloc.append_slots(b["seqs"])
+        slots, pairs, src = alloc.append_slots(b["seqs"], with_src=True)
         tables, lens = alloc.export_tables(b["seqs"], maxb)
         t_host += time.perf_counter() - t0
         steps.append(dict(b=i % R, slots=torch.from_numpy(slots).cuda(),
+                          cow_src=torch.from_numpy(src.astype(np.int32)).cuda(),
                           pairs=torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
                           if len(pairs) else None, npairs=len(pairs),
                           tables=torch.from_numpy(tables).cuda(),
@@ -322,11 +328,16 @@ def main():
 
     def run_step(st):
         b = batches[st["b"]]
-        if st["pairs"] is not None:
-            pkv.paged_copy_blocks(cache, st["pairs"])
-        pkv.paged_kv_write(b["k"], b["v"], st["slots"], cache)
-        pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale, out=b["out"],
-                                   partition_size=part, workspace=workspace)
+        if args.unfused:
+            if st["pairs"] is not None:
+                pkv.paged_copy_blocks(cache, st["pairs"])
+            pkv.paged_kv_write(b["k"], b["v"], st["slots"], cache)
+            pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale,
+                                       out=b["out"], partition_size=part, workspace=workspace)
+        else:
+            pkv.paged_decode_step(b["q"], b["k"], b["v"], cache, st["tables"], st["lens"], scale,
+                                  cow_src=st["cow_src"], out=b["out"], partition_size=part,
+                                  workspace=workspace)
 
     for st in steps[:Wm]:
         run_step(st)
@@ -394,7 +405,8 @@ def main():
                    "head_dim": D, "block_size": 16, "kv_dtype": w0.cache_dtype,
                    "mean_seq_len": round(mean_len, 1), "pool_blocks": num_blocks,
                    "rotating_batches": R, "partition_size": part,
-                   "split_k": not single_pass, "graph": not args.no_graph},
+                   "split_k": not single_pass, "graph": not args.no_graph,
+                   "fused_step": not args.unfused},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(S / (step_ms * 1e-3), 1),
         "tokens_per_s": round(S / (step_ms * 1e-3), 1),

@@ -123,10 +123,13 @@ int pkv_seq_append_slot(pkv_alloc *a, int64_t seq_id, int64_t *slot, int32_t *co
 /* pkv_seq_append_slot for n sequences in order (host arrays).  slots[i]
  * receives sequence i's slot; the copy pairs are written to cow_pairs as
  * [src, dst] rows and their count to *num_cow (cow_pairs needs room for n
- * rows).  Stops at the first failure and returns its status; *num_done
- * (nullable) receives how many sequences were appended. */
+ * rows); cow_src (nullable, [n]) receives for each sequence the source block
+ * of its copy (the destination is its new tail block), -1 if none -- the form
+ * paged_decode_step takes.  Stops at the first failure and returns its
+ * status; *num_done (nullable) receives how many sequences were appended. */
 int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_t *slots,
-                         int32_t *cow_pairs, int32_t *num_cow, int32_t *num_done);
+                         int32_t *cow_pairs, int32_t *num_cow, int32_t *cow_src,
+                         int32_t *num_done);
 /* Make child share every block of parent (reference counts + 1). */
 int pkv_seq_fork(pkv_alloc *a, int64_t parent, int64_t child);
 /* Release a sequence; blocks whose count drops to zero go to the free-list tail
@@ -242,6 +245,34 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            float scale, int32_t partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* Fused decode step: for every sequence s with L = seq_lens[s] > 0,
+ *   1. if cow_src (nullable, device int32 [num_seqs]) has cow_src[s] >= 0,
+ *      copy block cow_src[s] into the sequence's tail block
+ *      block_tables[s][(L-1)/16] (copy-on-write [fairy, s05]);
+ *   2. write the sequence's new token -- row s of key / value, device
+ *      [num_seqs][num_kv_heads][head_dim] of src_dtype -- at position L - 1,
+ *      i.e. slot block_tables[s][(L-1)/16] * 16 + (L-1) % 16, quantizing as
+ *      paged_kv_write does ("append the new token's K/V" [fairy, s02]);
+ *   3. compute out exactly as paged_attention_decode does, over all L tokens
+ *      including the new one.
+ * One launch (plus the merge when sequences are split) instead of
+ * paged_copy_blocks + paged_kv_write + paged_attention_decode, with the same
+ * results.  The copy and write of a sequence's kv head are done by the
+ * workgroup that reads that tail block.  src_dtype is PKV_F32 for an fp32
+ * cache and PKV_F16 otherwise.  The tail blocks written must be distinct
+ * sequences' own blocks (the allocator guarantees this: a shared tail is
+ * copied first); other sequences may share the copy sources.  Other arguments
+ * and errors as paged_attention_decode (the pools are written here). */
+int paged_decode_step(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                      const void *key, const void *value, int32_t src_dtype,
+                      const int32_t *cow_src, void *k_cache, void *v_cache, void *k_scale,
+                      void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream);
 
 /* ========================================================================
  * Bandwidth diagnostics (measurement helpers, not part of the method)

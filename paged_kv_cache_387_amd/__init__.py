@@ -30,7 +30,7 @@ EXPORTS = [
     "pkv_block_refcount", "pkv_seq_allocate", "pkv_seq_append_slot", "pkv_seq_append_slots",
     "pkv_seq_fork", "pkv_seq_free", "pkv_seq_len", "pkv_seq_slots", "pkv_export_tables",
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
-    "paged_attention_workspace_bytes", "paged_attention_decode",
+    "paged_attention_workspace_bytes", "paged_attention_decode", "paged_decode_step",
     "pkv_stream_read", "pkv_stream_copy",
 ]
 
@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
             "pkv_block_refcount": ([P, i32], i32),
             "pkv_seq_allocate": ([P, i64, i32, P, P], ctypes.c_int),
             "pkv_seq_append_slot": ([P, i64, P, P, P], ctypes.c_int),
-            "pkv_seq_append_slots": ([P, P, i32, P, P, P, P], ctypes.c_int),
+            "pkv_seq_append_slots": ([P, P, i32, P, P, P, P, P], ctypes.c_int),
             "pkv_seq_fork": ([P, i64, i64], ctypes.c_int),
             "pkv_seq_free": ([P, i64], ctypes.c_int),
             "pkv_seq_len": ([P, i64, P], ctypes.c_int),
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
             "paged_attention_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
             "paged_attention_decode": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32, P, i32,
                                         i32, i32, i32, i32, f32, i32, P, sz, P], ctypes.c_int),
+            "paged_decode_step": ([P, i32, P, i32, P, P, i32, P, P, P, P, P, i32, i32, P, i32,
+                                   P, i32, i32, i32, i32, i32, f32, i32, P, sz, P],
+                                  ctypes.c_int),
             "pkv_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
             "pkv_stream_copy": ([P, P, sz, i32, P], ctypes.c_int),
         }
@@ -154,15 +157,20 @@ class BlockAllocator:
                                          ctypes.byref(dst)), "pkv_seq_append_slot")
         return slot.value, (None if src.value < 0 else (src.value, dst.value))
 
-    def append_slots(self, seqs):
+    def append_slots(self, seqs, with_src: bool = False):
+        """Append one token to each sequence: returns (slots, copy pairs [n, 2])
+        and, with with_src, each sequence's copy source block (-1: none)."""
         ids = np.ascontiguousarray(seqs, dtype=np.int64)
         n = len(ids)
         slots = np.empty(max(n, 1), np.int64)
         pairs = np.empty((max(n, 1), 2), np.int32)
+        src = np.empty(max(n, 1), np.int32)
         ncow, done = ctypes.c_int32(), ctypes.c_int32()
         _check(lib().pkv_seq_append_slots(self._h, _np_ptr(ids), n, _np_ptr(slots),
-                                          _np_ptr(pairs), ctypes.byref(ncow),
+                                          _np_ptr(pairs), ctypes.byref(ncow), _np_ptr(src),
                                           ctypes.byref(done)), "pkv_seq_append_slots")
+        if with_src:
+            return slots[:n], pairs[:ncow.value], src[:n]
         return slots[:n], pairs[:ncow.value]
 
     def fork(self, parent: int, child: int):
@@ -369,6 +377,57 @@ def paged_attention_decode(query, cache: PagedKVCache, block_tables, seq_lens, s
         _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
         cache.block_size, float(scale), partition_size, ws_ptr, ws_len, _stream_ptr(stream)),
         "paged_attention_decode")
+    return out
+
+
+def paged_decode_step(query, key, value, cache: PagedKVCache, block_tables, seq_lens,
+                      scale: float, cow_src=None, out=None, out_dtype=None,
+                      partition_size: int = 0, workspace=None, stream=None):
+    """One fused decode step: copy-on-write of each sequence's tail block from
+    cow_src[s] (int32 device [S], -1 none; optional), the new token key[s] /
+    value[s] ([S, num_kv_heads, head_dim]) written at position seq_lens[s]-1,
+    then paged decode attention over all seq_lens[s] tokens."""
+    torch = _torch()
+    S, H, D = query.shape
+    q_dt = {torch.float32: F32, torch.float16: F16}.get(query.dtype)
+    src = {torch.float32: F32, torch.float16: F16}.get(key.dtype)
+    if q_dt is None or src is None or value.dtype != key.dtype:
+        raise ValueError("query/key/value must be float32 or float16")
+    if tuple(key.shape) != (S, cache.num_kv_heads, D) or value.shape != key.shape:
+        raise ValueError(f"key/value must be [{S}, {cache.num_kv_heads}, {D}]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    maxb = block_tables.shape[1]
+    if out is None:
+        odt = out_dtype if out_dtype is not None else query.dtype
+        out = torch.empty((S, H, D), dtype=odt, device=query.device)
+    o_dt = {torch.float32: F32, torch.float16: F16}.get(out.dtype)
+    if o_dt is None or tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be float32/float16 [num_seqs, num_heads, head_dim]")
+    if D != cache.head_dim or H % cache.num_kv_heads:
+        raise ValueError("query shape does not match the cache")
+    need = workspace_bytes(S, H, cache.num_kv_heads, D, maxb, partition_size)
+    if need > 0 and workspace is None:
+        workspace = alloc_workspace(S, H, cache.num_kv_heads, D, maxb, partition_size,
+                                    device=query.device)
+    ws_ptr, ws_len = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", numel=need)
+        ws_len = workspace.numel() * workspace.element_size()
+    nbytes = cache_bytes(cache.num_blocks, cache.num_kv_heads, D, cache.cache_dtype,
+                         cache.block_size)
+    ks, vs = cache._scales()
+    row = S * cache.num_kv_heads * D
+    _check(lib().paged_decode_step(
+        _dev(out, "out"), o_dt, _dev(query, "query"), q_dt,
+        _dev(key, "key", numel=row), _dev(value, "value", numel=row), src,
+        None if cow_src is None else _dev(cow_src, "cow_src", torch.int32, S),
+        _dev(cache.k, "k_cache", numel=nbytes), _dev(cache.v, "v_cache", numel=nbytes), ks, vs,
+        cache.cache_dtype, cache.num_blocks,
+        _dev(block_tables, "block_tables", torch.int32, S * maxb), maxb,
+        _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
+        cache.block_size, float(scale), partition_size, ws_ptr, ws_len, _stream_ptr(stream)),
+        "paged_decode_step")
     return out
 
 

@@ -186,7 +186,8 @@ int pkv_seq_append_slot(pkv_alloc *a, int64_t seq_id, int64_t *slot, int32_t *co
 }
 
 int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_t *slots,
-                         int32_t *cow_pairs, int32_t *num_cow, int32_t *num_done) {
+                         int32_t *cow_pairs, int32_t *num_cow, int32_t *cow_src,
+                         int32_t *num_done) {
   if (num_done) *num_done = 0;
   if (num_cow) *num_cow = 0;
   if (!a || n < 0 || (n > 0 && (!seq_ids || !slots || !cow_pairs || !num_cow)))
@@ -196,6 +197,7 @@ int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_
     int32_t src, dst;
     const int st = pkv_seq_append_slot(a, seq_ids[i], &slots[i], &src, &dst);
     if (st != PKV_OK) return st;
+    if (cow_src) cow_src[i] = src;
     if (src >= 0) {
       cow_pairs[2 * ncow] = src;
       cow_pairs[2 * ncow + 1] = dst;

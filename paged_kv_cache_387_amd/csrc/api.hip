@@ -119,14 +119,19 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
   return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
 }
 
-int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
-                           const void *k_cache, const void *v_cache, const void *k_scale,
-                           const void *v_scale, int32_t cache_dtype, int32_t num_blocks,
-                           const int32_t *block_tables, int32_t max_blocks_per_seq,
-                           const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                           float scale, int32_t partition_size, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and parameter set-up shared by paged_attention_decode and
+// paged_decode_step.  Returns PKV_OK and fills *pp, or an error status.
+int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *query,
+                   int32_t q_dtype, const void *k_cache, const void *v_cache,
+                   const void *k_scale, const void *v_scale, int32_t cache_dtype,
+                   int32_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                   int32_t partition_size, void *workspace, size_t workspace_bytes) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || partition_size < 0)
     return PKV_EINVAL;
@@ -134,9 +139,8 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   if (block_size != kBlockSize) return PKV_ENOTSUP;
   if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
   if (num_heads / num_kv_heads > kMaxGroup) return PKV_ENOTSUP;
-  // grid limits: y = kv heads, z = sequences; token counts stay in int32
-  if (num_seqs > 65535 || num_kv_heads > 65535 || max_blocks_per_seq > (1 << 26))
-    return PKV_ENOTSUP;
+  // token counts stay in int32
+  if (max_blocks_per_seq > (1 << 26)) return PKV_ENOTSUP;
   if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
   if (out_dtype != PKV_F32 && out_dtype != PKV_F16) return PKV_EINVAL;
   if (q_dtype != (cache_dtype == PKV_F32 ? PKV_F32 : PKV_F16)) return PKV_ENOTSUP;
@@ -165,7 +169,7 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   const int dev = check_device();
   if (dev != PKV_OK) return dev;
 
-  DecodeParams p;
+  DecodeParams p{};
   p.out = out;
   p.q = query;
   p.k_cache = static_cast<const uint8_t *>(k_cache);
@@ -187,8 +191,64 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   p.num_parts = parts;
   p.num_units = num_seqs * num_kv_heads;
   p.qk_scale = scale * 1.4426950408889634f;
+  *pp = p;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                           const void *k_cache, const void *v_cache, const void *k_scale,
+                           const void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           float scale, int32_t partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  DecodeParams p{};
+  const int st = prepare_decode(&p, out, out_dtype, query, q_dtype, k_cache, v_cache, k_scale,
+                                v_scale, cache_dtype, num_blocks, block_tables,
+                                max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads,
+                                head_dim, block_size, scale, partition_size, workspace,
+                                workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
   return status_of(launch_decode(p, cache_dtype, out_dtype, head_dim,
                                  static_cast<hipStream_t>(stream)));
+}
+
+int paged_decode_step(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                      const void *key, const void *value, int32_t src_dtype,
+                      const int32_t *cow_src, void *k_cache, void *v_cache, void *k_scale,
+                      void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  DecodeParams p{};
+  const int st = prepare_decode(&p, out, out_dtype, query, q_dtype, k_cache, v_cache, k_scale,
+                                v_scale, cache_dtype, num_blocks, block_tables,
+                                max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads,
+                                head_dim, block_size, scale, partition_size, workspace,
+                                workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (src_dtype != (cache_dtype == PKV_F32 ? PKV_F32 : PKV_F16)) return PKV_ENOTSUP;
+  if (num_seqs == 0) return PKV_OK;
+  if (!key || !value) return PKV_EINVAL;
+  if (!aligned(key, elem_bytes(src_dtype)) || !aligned(value, elem_bytes(src_dtype)) ||
+      !aligned(cow_src, 4))
+    return PKV_EINVAL;
+  p.key_new = key;
+  p.value_new = value;
+  p.cow_src = cow_src;
+  p.k_cache_w = static_cast<uint8_t *>(k_cache);
+  p.v_cache_w = static_cast<uint8_t *>(v_cache);
+  p.k_scale_w = static_cast<uint16_t *>(k_scale);
+  p.v_scale_w = static_cast<uint16_t *>(v_scale);
+  return status_of(launch_decode_step(p, cache_dtype, src_dtype, out_dtype, head_dim,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int paged_kv_write(const void *key, const void *value, int32_t src_dtype, int64_t key_stride,

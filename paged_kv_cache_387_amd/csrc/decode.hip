@@ -36,7 +36,7 @@
 // subnormal range and is divided out at the end).
 #include <cmath>
 
-#include "pkv_internal.h"
+#include "kv_write.h"
 
 namespace pkv {
 namespace {
@@ -152,7 +152,9 @@ template <> struct Prefetch<PKV_F32> { static constexpr int NB = PKV_PREFETCH_F3
 template <> struct Prefetch<PKV_I8> { static constexpr int NB = PKV_PREFETCH_Q8; };
 template <> struct Prefetch<PKV_E4M3> { static constexpr int NB = PKV_PREFETCH_Q8; };
 
-template <int KV, int D, int OUT>
+// SRC < 0: decode only.  SRC = PKV_F16 / PKV_F32: fused decode step, the new
+// token's K/V (of that type) is written first (see DecodeParams).
+template <int KV, int D, int OUT, int SRC>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) {
   constexpr int EB = Kv<KV>::EB;
   constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
@@ -242,6 +244,46 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     const int tj = lane < nc ? lane : nc - 1;
     return trow[(size_t)(c0 + tj) * kWaves];
   };
+
+  // ---- fused step: copy-on-write of the tail block, then the new token ----
+  // Only the wave that consumes the tail block touches it: it copies the
+  // (block, kv head) slice from cow_src[s] if asked, writes the new token at
+  // position L - 1, and waits for its stores before any of its tile loads,
+  // so its load of the tail tile sees them.  Other sequences may read the
+  // copy source concurrently; nothing else writes these bytes.
+  if constexpr (SRC >= 0) {
+    const int tail = nblk - 1;
+    if (tail >= first && tail < last && w == (tail - first) % kWaves) {
+      const int phys = p.block_tables[(size_t)s * p.max_blocks + tail];
+      if ((unsigned)phys < (unsigned)p.num_blocks) {
+        const size_t tile = ((size_t)phys * p.num_kv_heads + kvh) * TILE;
+        const size_t sc = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize;
+        const int src = p.cow_src ? p.cow_src[s] : -1;
+        if ((unsigned)src < (unsigned)p.num_blocks && src != phys) {
+          const size_t stile = ((size_t)src * p.num_kv_heads + kvh) * TILE;
+          copy_bytes_wave(p.k_cache_w + tile, p.k_cache_w + stile, TILE, lane);
+          copy_bytes_wave(p.v_cache_w + tile, p.v_cache_w + stile, TILE, lane);
+          if constexpr (QUANT) {
+            const size_t ssc = ((size_t)src * p.num_kv_heads + kvh) * kBlockSize;
+            if (lane < kBlockSize) {
+              p.k_scale_w[sc + lane] = p.k_scale_w[ssc + lane];
+              p.v_scale_w[sc + lane] = p.v_scale_w[ssc + lane];
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0);   // the copy lands before the token overwrites its slot
+        }
+        const int t = (L - 1) % kBlockSize;
+        constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
+        const size_t row = ((size_t)s * p.num_kv_heads + kvh) * D * esz;
+        write_token_wave<SRC, KV, D>(static_cast<const uint8_t *>(p.key_new) + row,
+                                     static_cast<const uint8_t *>(p.value_new) + row,
+                                     p.k_cache_w + tile, p.v_cache_w + tile,
+                                     QUANT ? p.k_scale_w + sc + t : nullptr,
+                                     QUANT ? p.v_scale_w + sc + t : nullptr, t, lane);
+        __builtin_amdgcn_s_waitcnt(0);     // stores complete before this wave's tile loads
+      }
+    }
+  }
 
   // ---- per-wave running state ----
   float m = -INFINITY;   // running max of column r (base-2 scaled scores)
@@ -515,11 +557,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   }
 }
 
-template <int KV, int D, int OUT>
+template <int KV, int D, int OUT, int SRC>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = decode_grid(p.num_units, p.num_parts);
-  hipLaunchKernelGGL((decode_kernel<KV, D, OUT>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
-                     stream, p);
+  hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC>), dim3((unsigned)grid), dim3(64 * kWaves),
+                     0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.num_parts <= 1) return err;
   hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_seqs * p.num_heads),
@@ -527,16 +569,16 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KV, int D>
+template <int KV, int D, int SRC>
 hipError_t launch_out(const DecodeParams &p, int out_dtype, hipStream_t stream) {
-  return out_dtype == PKV_F32 ? launch_typed<KV, D, PKV_F32>(p, stream)
-                              : launch_typed<KV, D, PKV_F16>(p, stream);
+  return out_dtype == PKV_F32 ? launch_typed<KV, D, PKV_F32, SRC>(p, stream)
+                              : launch_typed<KV, D, PKV_F16, SRC>(p, stream);
 }
 
-template <int KV>
+template <int KV, int SRC>
 hipError_t launch_d(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream) {
-  return head_dim == 64 ? launch_out<KV, 64>(p, out_dtype, stream)
-                        : launch_out<KV, 128>(p, out_dtype, stream);
+  return head_dim == 64 ? launch_out<KV, 64, SRC>(p, out_dtype, stream)
+                        : launch_out<KV, 128, SRC>(p, out_dtype, stream);
 }
 
 }  // namespace
@@ -544,10 +586,22 @@ hipError_t launch_d(const DecodeParams &p, int out_dtype, int head_dim, hipStrea
 hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, int head_dim,
                          hipStream_t stream) {
   switch (cache_dtype) {
-    case PKV_F32: return launch_d<PKV_F32>(p, out_dtype, head_dim, stream);
-    case PKV_F16: return launch_d<PKV_F16>(p, out_dtype, head_dim, stream);
-    case PKV_I8: return launch_d<PKV_I8>(p, out_dtype, head_dim, stream);
-    default: return launch_d<PKV_E4M3>(p, out_dtype, head_dim, stream);
+    case PKV_F32: return launch_d<PKV_F32, -1>(p, out_dtype, head_dim, stream);
+    case PKV_F16: return launch_d<PKV_F16, -1>(p, out_dtype, head_dim, stream);
+    case PKV_I8: return launch_d<PKV_I8, -1>(p, out_dtype, head_dim, stream);
+    default: return launch_d<PKV_E4M3, -1>(p, out_dtype, head_dim, stream);
+  }
+}
+
+// New tokens are fp32 for an fp32 cache and fp16 otherwise (checked by the caller).
+hipError_t launch_decode_step(const DecodeParams &p, int cache_dtype, int src_dtype,
+                              int out_dtype, int head_dim, hipStream_t stream) {
+  (void)src_dtype;
+  switch (cache_dtype) {
+    case PKV_F32: return launch_d<PKV_F32, PKV_F32>(p, out_dtype, head_dim, stream);
+    case PKV_F16: return launch_d<PKV_F16, PKV_F16>(p, out_dtype, head_dim, stream);
+    case PKV_I8: return launch_d<PKV_I8, PKV_F16>(p, out_dtype, head_dim, stream);
+    default: return launch_d<PKV_E4M3, PKV_F16>(p, out_dtype, head_dim, stream);
   }
 }
 

@@ -1,0 +1,128 @@
+// Device helpers shared by the cache-write kernel and the fused decode step:
+// writing one token's K/V vectors of one kv head into its slot (with int8 /
+// E4M3 quantization), and copying one (block, kv head) slice of the pools.
+//
+// Quantized caches keep one fp16 scale per (token, kv head), separately for
+// K and V ("KV Cache scaling factor", "KVcache-learning",
+// fairy2021.github.io, s09; int8 / fp8 KV cache, yunthe.com, quantization
+// section):  a = max_d |x_d|,  s = fp16(a / 127) or fp16(a / 448) (IEEE fp32
+// division, round to nearest even),  code = clamp(rint(x / s), -127, 127) or
+// the nearest-even E4M3 value of x / s saturated at +-448; s == 0 gives
+// zero codes.
+#pragma once
+
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+template <int KV> constexpr int ebytes() { return KV == PKV_F32 ? 4 : KV == PKV_F16 ? 2 : 1; }
+
+// E4M3 (OCP 8-bit float: bias 7, 3 mantissa bits, max 448, no infinities),
+// nearest-even, saturating at +-448.  Works on the binary32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a == a)) return 0x7Fu;                       // NaN
+  if (a >= 448.0f) return sign | 0x7Eu;              // saturate
+  if (a < 0.015625f)                                 // below 2^-6: step 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t u = __float_as_uint(a);
+  uint32_t ex = (u >> 23) - 127u + 7u;               // 1 .. 15
+  uint32_t keep = (u >> 20) & 7u;                    // top 3 mantissa bits
+  const uint32_t rest = u & 0xFFFFFu;                // 20 dropped bits
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) { keep = 0u; ++ex; }
+  return sign | (ex << 3) | keep;
+}
+
+__device__ __forceinline__ float wave_max_all(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Byte offsets inside a (block, kv head) tile (pool layout of pkv.h).
+__device__ __forceinline__ size_t k_byte(int t, int j) {
+  return (size_t)((j >> 4) * kBlockSize + t) * 16 + (j & 15);
+}
+__device__ __forceinline__ size_t v_byte(int t, int j) {
+  return (size_t)((j >> 2) * kBlockSize + t) * 4 + (j & 3);
+}
+
+// One wavefront writes token slot t of the K and V tiles of one (block, kv
+// head): src rows k_row / v_row hold D elements of SRC type; the scale
+// pointers address the slot's fp16 scale (quantized caches only).  Lane l
+// owns elements l*D/64 .. (l+1)*D/64 - 1.  The source loads are issued before
+// anything else so they overlap.
+template <int SRC, int KV, int D>
+__device__ __forceinline__ void write_token_wave(const void *k_row, const void *v_row,
+                                                 uint8_t *k_tile, uint8_t *v_tile,
+                                                 uint16_t *k_scale, uint16_t *v_scale, int t,
+                                                 int lane) {
+  constexpr int EB = ebytes<KV>();
+  constexpr int PER = D / 64;
+  float xs[2][PER];
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void *src = which ? v_row : k_row;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane * PER + k;
+      if constexpr (SRC == PKV_F32)
+        xs[which][k] = reinterpret_cast<const float *>(src)[d];
+      else
+        xs[which][k] = (float)reinterpret_cast<const _Float16 *>(src)[d];
+    }
+  }
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float *x = xs[which];
+    uint8_t *tile = which ? v_tile : k_tile;
+    if constexpr (KV == PKV_F32 || KV == PKV_F16) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = (lane * PER + k) * EB;
+        const size_t off = which ? v_byte(t, j) : k_byte(t, j);
+        if constexpr (KV == PKV_F32)
+          *reinterpret_cast<float *>(tile + off) = x[k];
+        else
+          *reinterpret_cast<_Float16 *>(tile + off) = (_Float16)x[k];
+      }
+    } else {
+      float a = 0.0f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) a = fmaxf(a, fabsf(x[k]));
+      a = wave_max_all(a);
+      const float qmax = (KV == PKV_I8) ? 127.0f : 448.0f;
+      const _Float16 s16 = (_Float16)(a / qmax);   // IEEE fp32 division, RNE to fp16
+      const float s = (float)s16;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int j = lane * PER + k;
+        uint32_t code = 0u;
+        if (s != 0.0f) {
+          const float y = x[k] / s;
+          if constexpr (KV == PKV_I8)
+            code = (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f) & 0xFFu;
+          else
+            code = e4m3_encode_sat(y);
+        }
+        tile[which ? v_byte(t, j) : k_byte(t, j)] = (uint8_t)code;
+      }
+      if (lane == 0) *(which ? v_scale : k_scale) = __builtin_bit_cast(uint16_t, s16);
+    }
+  }
+}
+
+// One wavefront copies `bytes` (a multiple of 16) from src to dst with
+// 16-byte accesses.
+__device__ __forceinline__ void copy_bytes_wave(uint8_t *dst, const uint8_t *src, int bytes,
+                                                int lane) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  for (int o = lane * 16; o < bytes; o += 64 * 16)
+    *reinterpret_cast<v4 *>(dst + o) = *reinterpret_cast<const v4 *>(src + o);
+}
+
+}  // namespace pkv

@@ -43,6 +43,16 @@ struct DecodeParams {
   int num_parts;    // partitions in the grid (ceil(max_blocks / part_blocks))
   int num_units;    // num_seqs * num_kv_heads
   float qk_scale;   // scale * log2(e): scores are kept in base 2
+  // Fused decode step only: the new token of each sequence (row s of
+  // key_new / value_new, [S][Hkv][D]) is written at position seq_len - 1
+  // after copying block cow_src[s] into the tail block (cow_src nullable).
+  const void *key_new;
+  const void *value_new;
+  const int32_t *cow_src;
+  uint8_t *k_cache_w;
+  uint8_t *v_cache_w;
+  uint16_t *k_scale_w;
+  uint16_t *v_scale_w;
 };
 
 // Grid of the decode kernel: one workgroup per (unit, partition), units
@@ -80,6 +90,8 @@ struct CopyParams {
 
 hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, int head_dim,
                          hipStream_t stream);
+hipError_t launch_decode_step(const DecodeParams &p, int cache_dtype, int src_dtype,
+                              int out_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_write(const WriteParams &p, int src_dtype, int cache_dtype, int head_dim,
                         hipStream_t stream);
 hipError_t launch_copy(const CopyParams &p, hipStream_t stream);

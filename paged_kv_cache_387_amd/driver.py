@@ -126,3 +126,26 @@ def decode(r: Replay, w, partition_size: int | None = None, out_dtype=None, stre
     return paged_attention_decode(r.query, r.cache, r.block_tables, r.seq_lens,
                                   float(np.float32(w.scale)), out_dtype=odt, partition_size=ps,
                                   stream=stream)
+
+
+def fused_step(r: Replay, w, partition_size: int | None = None, out_dtype=None, stream=None,
+               seq_offset: int = 0):
+    """Run the step of workload `w` (replayed up to its ("step",) marker into
+    `r`) as one paged_decode_step call: the allocator appends one token per
+    decode sequence, then copy-on-write, the write and the decode run fused.
+    Returns (out, slots, copy pairs, tables, lens)."""
+    import torch
+    from synth.workloads import step_rows
+    from . import paged_decode_step
+    seqs = [s + seq_offset for s in w.decode_seqs]
+    slots, pairs, src = r.alloc.append_slots(seqs, with_src=True)
+    tables, lens = r.alloc.export_tables(seqs, w.max_blocks_per_seq)
+    k, v = step_rows(w)
+    odt = {"f32": torch.float32, "f16": torch.float16}[w.out_dtype] if out_dtype is None \
+        else out_dtype
+    ps = w.partition_size if partition_size is None else partition_size
+    out = paged_decode_step(r.query, _to_dev(k), _to_dev(v), r.cache, _to_dev(tables),
+                            _to_dev(lens), float(np.float32(w.scale)),
+                            cow_src=_to_dev(src.astype(np.int32)), out_dtype=odt,
+                            partition_size=ps, stream=stream)
+    return out, slots, pairs, tables, lens

@@ -227,6 +227,44 @@ def custom(name: str, lens, H: int, Hkv: int, D: int, cache_dtype: str = "f16",
                    partition_size=partition_size)
 
 
+def with_decode_step(w: Workload) -> Workload:
+    """The same workload followed by one decode step: every decode sequence
+    appends one token (position = its current length) and writes it."""
+    import copy
+    lens = {}
+    for op in w.ops:
+        if op[0] == "step":
+            raise ValueError("workload already has a step")
+        if op[0] == "allocate":
+            lens[op[1]] = max(lens.get(op[1], 0), op[2])
+        elif op[0] == "fork":
+            lens[op[2]] = lens.get(op[1], 0)
+        elif op[0] == "append":
+            lens[op[1]] = lens.get(op[1], 0) + 1
+    w2 = copy.copy(w)
+    w2.ops = list(w.ops) + [("step",)] + [("append", s) for s in w.decode_seqs] + \
+        [("write", s, lens.get(s, 0), 1) for s in w.decode_seqs]
+    w2.max_blocks_per_seq = max(w.max_blocks_per_seq,
+                                max(-(-(lens.get(s, 0) + 1) // 16) for s in w.decode_seqs))
+    w2.name = w.name + "_step"
+    w2.memo = None
+    return w2
+
+
+def step_rows(w: Workload):
+    """K and V rows [S, Hkv, D] of the tokens the step of `w` writes, in
+    decode-sequence order (the step's write ops)."""
+    after = w.ops[w.ops.index(("step",)) + 1:]
+    writes = {op[1]: op[2] for op in after if op[0] == "write"}
+    ks, vs = [], []
+    for s in w.decode_seqs:
+        pos = writes[s]
+        owner = w.owner_of(s, pos)
+        ks.append(w.kv_rows("k", owner, pos, 1)[0])
+        vs.append(w.kv_rows("v", owner, pos, 1)[0])
+    return np.stack(ks), np.stack(vs)
+
+
 CONFIGS = {
     "c1": c1_tiny,
     "c2": c2_qwen3_32b_layer,
