@@ -33,28 +33,25 @@ int check_device() {
 
 int status_of(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EDEVICE; }
 
-// Tuning constants of the automatic partition choice: tokens are split so
-// that the grid holds about kTargetWorkgroups workgroups, each partition at
-// least kMinPartBlocks blocks long.
-#ifndef PKV_TARGET_WORKGROUPS
-#define PKV_TARGET_WORKGROUPS 1024
-#endif
-#ifndef PKV_MIN_PART_BLOCKS
-#define PKV_MIN_PART_BLOCKS 64
-#endif
-constexpr int64_t kTargetWorkgroups = PKV_TARGET_WORKGROUPS;
-constexpr int32_t kMinPartBlocks = PKV_MIN_PART_BLOCKS;
+// Automatic partition choice: a quarter of the table's width, clamped to
+// [kMinPartBlocks, kMaxPartBlocks] blocks and rounded up to a multiple of the
+// wave count.  Short sequences (up to 1024 tokens) run in a single pass;
+// long ones are split into pieces of at most 4096 tokens so that sequences
+// of very different lengths still spread evenly over the compute units.
+constexpr int32_t kMinPartBlocks = 64;
+constexpr int32_t kMaxPartBlocks = 256;
 
 int32_t choose_part_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks,
                            int32_t requested_tokens) {
+  (void)num_seqs;
+  (void)num_kv_heads;
   if (requested_tokens > 0) {
     int32_t pb = requested_tokens / kBlockSize;
     return pb >= max_blocks ? max_blocks : pb;
   }
-  const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  int64_t parts = units >= kTargetWorkgroups ? 1 : (kTargetWorkgroups + units - 1) / units;
-  int64_t pb = (max_blocks + parts - 1) / parts;
+  int64_t pb = (max_blocks + 3) / 4;
   if (pb < kMinPartBlocks) pb = kMinPartBlocks;
+  if (pb > kMaxPartBlocks) pb = kMaxPartBlocks;
   pb = (pb + kWaves - 1) / kWaves * kWaves;
   return pb >= max_blocks ? max_blocks : (int32_t)pb;
 }
@@ -115,7 +112,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
     return 0;
   const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
                                         partition_size);
-  const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
+  const int32_t parts = odd_up((max_blocks_per_seq + pb - 1) / pb);
   return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
 }
 
@@ -158,7 +155,7 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
 
   const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
                                         partition_size);
-  const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
+  const int32_t parts = odd_up((max_blocks_per_seq + pb - 1) / pb);
   if ((int64_t)num_seqs * num_heads > INT32_MAX || (int64_t)num_seqs * num_kv_heads > INT32_MAX ||
       decode_grid(num_seqs * num_kv_heads, parts) > INT32_MAX)
     return PKV_ENOTSUP;

@@ -175,13 +175,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   const int g = lane >> 4;
 
   // Workgroup -> (unit, partition).  Workgroups are dealt to the dies round
-  // robin, so all partitions of unit u get ids on die u % kXcds: blocks that
-  // several sequences share (a common prefix) are read through one die's L2
-  // when those sequences' units sit on one die.
+  // robin, so unit u runs on die u % kXcds (with 8 kv heads: one kv head per
+  // die, whose L2 then serves the blocks that sequences share).  Ids go
+  // partition-major: workgroups resident together work on the same region of
+  // their sequences, so a shared prefix is read while it is still cached.
+  // The unit-group count is odd (unit_groups), so the partitions of one unit
+  // land on different compute units.
   const int bid = blockIdx.x;
   const int die_slot = bid / kXcds;
-  const int part = die_slot % p.num_parts;
-  const int u = (die_slot / p.num_parts) * kXcds + bid % kXcds;
+  const int ugroups = unit_groups(p.num_units);
+  const int part = die_slot / ugroups;
+  const int u = (die_slot % ugroups) * kXcds + bid % kXcds;
   if (u >= p.num_units) return;
   const int s = u / p.num_kv_heads;
   const int kvh = u - s * p.num_kv_heads;
@@ -248,40 +252,52 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   // ---- fused step: copy-on-write of the tail block, then the new token ----
   // Only the wave that consumes the tail block touches it: it copies the
   // (block, kv head) slice from cow_src[s] if asked, writes the new token at
-  // position L - 1, and waits for its stores before any of its tile loads,
-  // so its load of the tail tile sees them.  Other sequences may read the
-  // copy source concurrently; nothing else writes these bytes.
+  // position L - 1, and waits for its stores before it issues the load of the
+  // tail tile, so that load sees them.  When the tail tile is not among the
+  // wave's first NB loads, the write runs after those are issued and overlaps
+  // with them.  Other sequences may read the copy source concurrently;
+  // nothing else writes these bytes.
+  bool step_pending = false;
+  auto step_write = [&]() {
+    if constexpr (SRC >= 0) {
+      const int tail = nblk - 1;
+      const int phys = p.block_tables[(size_t)s * p.max_blocks + tail];
+      if ((unsigned)phys >= (unsigned)p.num_blocks) return;
+      const size_t tile = ((size_t)phys * p.num_kv_heads + kvh) * TILE;
+      const size_t sc = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize;
+      const int src = p.cow_src ? p.cow_src[s] : -1;
+      if ((unsigned)src < (unsigned)p.num_blocks && src != phys) {
+        const size_t stile = ((size_t)src * p.num_kv_heads + kvh) * TILE;
+        copy_bytes_wave(p.k_cache_w + tile, p.k_cache_w + stile, TILE, lane);
+        copy_bytes_wave(p.v_cache_w + tile, p.v_cache_w + stile, TILE, lane);
+        if constexpr (QUANT) {
+          const size_t ssc = ((size_t)src * p.num_kv_heads + kvh) * kBlockSize;
+          if (lane < kBlockSize) {
+            p.k_scale_w[sc + lane] = p.k_scale_w[ssc + lane];
+            p.v_scale_w[sc + lane] = p.v_scale_w[ssc + lane];
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the copy lands before the token overwrites its slot
+      }
+      const int t = (L - 1) % kBlockSize;
+      constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
+      const size_t row = ((size_t)s * p.num_kv_heads + kvh) * D * esz;
+      write_token_wave<SRC, KV, D>(static_cast<const uint8_t *>(p.key_new) + row,
+                                   static_cast<const uint8_t *>(p.value_new) + row,
+                                   p.k_cache_w + tile, p.v_cache_w + tile,
+                                   QUANT ? p.k_scale_w + sc + t : nullptr,
+                                   QUANT ? p.v_scale_w + sc + t : nullptr, t, lane);
+      __builtin_amdgcn_s_waitcnt(0);     // stores complete before the tail tile is loaded
+    }
+  };
   if constexpr (SRC >= 0) {
     const int tail = nblk - 1;
     if (tail >= first && tail < last && w == (tail - first) % kWaves) {
-      const int phys = p.block_tables[(size_t)s * p.max_blocks + tail];
-      if ((unsigned)phys < (unsigned)p.num_blocks) {
-        const size_t tile = ((size_t)phys * p.num_kv_heads + kvh) * TILE;
-        const size_t sc = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize;
-        const int src = p.cow_src ? p.cow_src[s] : -1;
-        if ((unsigned)src < (unsigned)p.num_blocks && src != phys) {
-          const size_t stile = ((size_t)src * p.num_kv_heads + kvh) * TILE;
-          copy_bytes_wave(p.k_cache_w + tile, p.k_cache_w + stile, TILE, lane);
-          copy_bytes_wave(p.v_cache_w + tile, p.v_cache_w + stile, TILE, lane);
-          if constexpr (QUANT) {
-            const size_t ssc = ((size_t)src * p.num_kv_heads + kvh) * kBlockSize;
-            if (lane < kBlockSize) {
-              p.k_scale_w[sc + lane] = p.k_scale_w[ssc + lane];
-              p.v_scale_w[sc + lane] = p.v_scale_w[ssc + lane];
-            }
-          }
-          __builtin_amdgcn_s_waitcnt(0);   // the copy lands before the token overwrites its slot
-        }
-        const int t = (L - 1) % kBlockSize;
-        constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
-        const size_t row = ((size_t)s * p.num_kv_heads + kvh) * D * esz;
-        write_token_wave<SRC, KV, D>(static_cast<const uint8_t *>(p.key_new) + row,
-                                     static_cast<const uint8_t *>(p.value_new) + row,
-                                     p.k_cache_w + tile, p.v_cache_w + tile,
-                                     QUANT ? p.k_scale_w + sc + t : nullptr,
-                                     QUANT ? p.v_scale_w + sc + t : nullptr, t, lane);
-        __builtin_amdgcn_s_waitcnt(0);     // stores complete before this wave's tile loads
-      }
+      // the tail is this wave's last block, entry nb_w - 1 of its walk
+      if (nb_w - 1 < Prefetch<KV>::NB)
+        step_write();
+      else
+        step_pending = true;
     }
   }
 
@@ -343,40 +359,52 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     }
     if (!t.ok) return;  // table entry outside the pool: block skipped
     const int tok0 = blk * kBlockSize + 4 * g;
-    const bool partial = (blk + 1) * kBlockSize > L;   // uniform per wave
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float f = sc[v] * p.qk_scale;
-      if constexpr (QUANT) {
-        uint32_t word = t.ks[v >> 1];
-        f *= (float)as_h2(word)[v & 1];
+      x[v] = sc[v] * p.qk_scale;
+      if constexpr (QUANT) x[v] *= (float)as_h2(t.ks[v >> 1])[v & 1];
+    }
+    u4 vw[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vw[i] = t.v[i];
+    u2 vs = t.vs;
+    // Only a sequence's last block can be partial (uniform per wave).  Its
+    // unwritten slots may hold anything, NaN included: their scores become
+    // -inf and their V words (and V scales) zero.
+    if (__builtin_expect((blk + 1) * kBlockSize > L, 0)) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool valid = tok0 + v < L;
+        x[v] = valid ? x[v] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) vw[i][v] = valid ? vw[i][v] : 0u;
       }
-      x[v] = (partial && tok0 + v >= L) ? -INFINITY : f;
+      if constexpr (QUANT) {
+        const uint32_t keep0 = (tok0 + 0 < L ? 0xFFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
+        const uint32_t keep1 = (tok0 + 2 < L ? 0xFFFFu : 0u) | (tok0 + 3 < L ? 0xFFFF0000u : 0u);
+        vs = u2{vs[0] & keep0, vs[1] & keep1};
+      }
     }
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     bm = fmaxf(bm, xor16(bm));
     bm = fmaxf(bm, xor32(bm));
     const float mn = fmaxf(m, bm);
-    const float alpha = exp2f(m - mn);   // m = -inf on the first block: 0
+    // Rescale only when some column's running max rose (m = -inf before the
+    // first block, so the first block always rescales: alpha = 0).
+    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
+      const float alpha = exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+      m = mn;
+    }
     float pr[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) pr[v] = exp2f(x[v] - mn);
-    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = mn;
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+    for (int v = 0; v < 4; ++v) pr[v] = exp2f(x[v] - m);
+    l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     // P.V: the lane's pr[v] is P^T[token 4g+v][head r], the B operand as is.
-    u4 vw[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      vw[i] = t.v[i];
-      if (partial) {   // unwritten slots may hold anything: zero them
-#pragma unroll
-        for (int v = 0; v < 4; ++v) vw[i][v] = (tok0 + v < L) ? vw[i][v] : 0u;
-      }
-    }
     if constexpr (KV == PKV_F32) {
 #pragma unroll
       for (int i = 0; i < NL; ++i)
@@ -399,13 +427,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
             __builtin_bit_cast(h4, u2{hi01, hi23}), pb, acc[2 * i + 1], 0, 0, 0);
       }
     } else {
-      // unwritten slots may hold a NaN scale: select, do not multiply by p = 0
       float ps[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float sv = (float)as_h2(t.vs[v >> 1])[v & 1];
-        ps[v] = (partial && tok0 + v >= L) ? 0.0f : pr[v] * sv * kPvBoost;
-      }
+      for (int v = 0; v < 4; ++v) ps[v] = pr[v] * (float)as_h2(vs[v >> 1])[v & 1] * kPvBoost;
       const h4 pb = h4{(_Float16)ps[0], (_Float16)ps[1], (_Float16)ps[2], (_Float16)ps[3]};
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
@@ -434,6 +458,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     Tile ring[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) issue(tv, j < nc ? j : nc - 1, ring[j]);
+    if (step_pending) {   // overlaps with the loads just issued
+      step_write();
+      step_pending = false;
+    }
     int k0 = 0;
     for (; k0 + 2 * NB <= nc; k0 += NB) {
 #pragma unroll

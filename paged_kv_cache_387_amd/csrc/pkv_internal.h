@@ -55,10 +55,20 @@ struct DecodeParams {
   uint16_t *v_scale_w;
 };
 
-// Grid of the decode kernel: one workgroup per (unit, partition), units
-// padded to a multiple of kXcds.
+// Workgroups land on a die's compute units roughly round robin by id, and
+// the die and compute-unit counts are powers of two.  A count that strides
+// the grid (partitions per unit, unit groups per die) is therefore padded to
+// an odd number: a unit's partitions then spread over different compute units
+// instead of aliasing onto the same ones.  Padding slots are empty
+// workgroups that exit at once.
+__host__ __device__ inline int odd_up(int n) { return n > 1 && n % 2 == 0 ? n + 1 : n; }
+
+// Unit groups per die: units are dealt to dies u % kXcds.
+__host__ __device__ inline int unit_groups(int num_units) { return odd_up((num_units + kXcds - 1) / kXcds); }
+
+// Grid of the decode kernel: one workgroup per (unit group, die, partition).
 inline int64_t decode_grid(int num_units, int num_parts) {
-  return (int64_t)((num_units + kXcds - 1) / kXcds) * kXcds * num_parts;
+  return (int64_t)unit_groups(num_units) * kXcds * num_parts;
 }
 
 struct WriteParams {

@@ -40,7 +40,9 @@ def test_partition_and_workspace_sizes():
     # explicit 512-token partitions over 2048-block tables: 64 partitions
     assert pkv.partition_size(8, 8, 2048, requested=512) == 512
     ws = pkv.workspace_bytes(8, 64, 8, 128, 2048, partition_size=512)
-    rows = 8 * 64 * 64
+    # 64 partitions, padded to an odd count (65) so that a unit's partitions
+    # do not alias onto the same compute units
+    rows = 8 * 64 * 65
     assert ws == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
     # a partition at least as long as the table means a single pass, no workspace
     assert pkv.partition_size(4, 2, 7, requested=4096) == 7 * 16
