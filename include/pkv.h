@@ -66,8 +66,12 @@ int pkv_version(void);
  *   K tile: byte j of token t at ((j / 16) * block_size + t) * 16 + j % 16
  *           (16-byte columns, token-minor: the split of the K cache into
  *           [head_dim*eb/16][block_size][16 bytes] of [7yue, section 5])
- *   V tile: byte j of token t at ((j / 4) * block_size + t) * 4 + j % 4
- *           (4-byte columns, token-minor)
+ *   V tile, PKV_F32 / PKV_F16: byte j of token t at
+ *           ((j / 4) * block_size + t) * 4 + j % 4   (4-byte columns, token-minor)
+ *   V tile, PKV_I8 / PKV_E4M3 (one byte per element, j = d): element d of
+ *           token t at ((d / 4) * (block_size / 4) + t / 4) * 16 + (d % 4) * 4
+ *           + t % 4  (16-byte groups of 4 elements x 4 tokens; each 4-byte word
+ *           holds one element of 4 consecutive tokens)
  * Scales (PKV_I8 / PKV_E4M3 only): fp16 [num_blocks][num_kv_heads][block_size],
  * one array for K and one for V.  Slot s of the cache is token position
  * s % block_size of physical block s / block_size.

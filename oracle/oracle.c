@@ -50,7 +50,9 @@
  *   eb = bytes per element.  Inside a tile, byte j of token t's D-vector
  *   (j = d * eb + byte-in-element) lives at
  *     K: ((j / 16) * BS + t) * 16 + j % 16     (16-byte columns, token-minor)
- *     V: ((j /  4) * BS + t) *  4 + j %  4     ( 4-byte columns, token-minor)
+ *     V, eb 2 or 4: ((j / 4) * BS + t) * 4 + j % 4   (4-byte columns, token-minor)
+ *     V, eb 1 (int8 / E4M3): ((d / 4) * (BS / 4) + t / 4) * 16 + (d % 4) * 4 + t % 4
+ *        (16-byte groups of 4 elements x 4 tokens, token-minor inside)
  *   scales: fp16 [num_blocks][Hkv][BS].
  */
 #include <math.h>
@@ -170,7 +172,12 @@ static size_t orc_tile_base(int64_t b, int kvh, int Hkv, int BS, int D, int eb)
 }
 
 static size_t orc_k_byte(int t, int j, int BS) { return ((size_t)(j / 16) * BS + t) * 16 + j % 16; }
-static size_t orc_v_byte(int t, int j, int BS) { return ((size_t)(j / 4) * BS + t) * 4 + j % 4; }
+static size_t orc_v_byte(int t, int j, int BS, int eb)
+{
+    if (eb == 1)
+        return ((size_t)(j / 4) * (BS / 4) + t / 4) * 16 + (j % 4) * 4 + t % 4;
+    return ((size_t)(j / 4) * BS + t) * 4 + j % 4;
+}
 
 /* Value of element d of token slot t in tile (b, kvh); is_v selects the V layout. */
 static double orc_load(const uint8_t *pool, const uint16_t *scales, int kind, int is_v,
@@ -181,7 +188,7 @@ static double orc_load(const uint8_t *pool, const uint16_t *scales, int kind, in
     unsigned char raw[4];
     for (int k = 0; k < eb; k++) {
         int j = d * eb + k;
-        raw[k] = pool[base + (is_v ? orc_v_byte(t, j, BS) : orc_k_byte(t, j, BS))];
+        raw[k] = pool[base + (is_v ? orc_v_byte(t, j, BS, eb) : orc_k_byte(t, j, BS))];
     }
     switch (kind) {
     case ORC_F32: { float f; memcpy(&f, raw, 4); return (double)f; }
@@ -199,7 +206,7 @@ static void orc_store_raw(uint8_t *pool, int is_v, size_t base, int t, int d, in
 {
     for (int k = 0; k < eb; k++) {
         int j = d * eb + k;
-        pool[base + (is_v ? orc_v_byte(t, j, BS) : orc_k_byte(t, j, BS))] = raw[k];
+        pool[base + (is_v ? orc_v_byte(t, j, BS, eb) : orc_k_byte(t, j, BS))] = raw[k];
     }
 }
 

@@ -25,15 +25,20 @@
 // Pool layout (see include/pkv.h): a (block, kv head) tile of K stores each
 // token's vector as 16-byte columns, token-minor: 16-byte load number i of lane
 // (r = lane%16, g = lane/16) reads column 4i+g of token r at byte (64i+lane)*16
-// -- one contiguous 1 KiB per wave instruction.  V stores 4-byte columns,
-// token-minor: load i of lane (r, g) reads tokens 4g..4g+3 of column 16i+r at
-// byte (16i+r)*64 + 16g -- again 1 KiB contiguous per instruction.
+// -- one contiguous 1 KiB per wave instruction.  V of 2- and 4-byte elements
+// stores 4-byte columns, token-minor: load i of lane (r, g) reads tokens
+// 4g..4g+3 of column 16i+r at byte (16i+r)*64 + 16g.  V of 1-byte elements
+// stores 16-byte groups (4 elements x 4 tokens): load i of lane (r, g) reads
+// group (16i+r, g) at byte ((16i+r)*4 + g)*16, whose word e holds element
+// 4(16i+r)+e of tokens 4g..4g+3 -- an MFMA operand as it stands.  Again 1 KiB
+// contiguous per instruction.
 //
 // Data types: fp32 KV uses 16x16x4 f32 MFMAs; fp16 KV uses 16x16x32 f16 (q.K)
-// and 16x16x16 f16 (P.V); int8 / E4M3 codes are widened exactly to fp16 and use
-// the fp16 MFMAs, the K scale multiplies the scores and the V scale is folded
-// into P (P' = p * s_v * 64 in fp16; the factor 64 keeps P' out of fp16's
-// subnormal range and is divided out at the end).
+// and 16x16x16 f16 (P.V); int8 / E4M3 codes are widened exactly to fp16 (int8
+// by a byte permute under an fp16 exponent, E4M3 by the gfx950 fp8
+// conversion) and use the fp16 MFMAs, the K scale multiplies the scores and
+// the V scale is folded into P (P' = p * s_v * 64 in fp16; the factor 64 keeps
+// P' out of fp16's subnormal range and is divided out at the end).
 #include <cmath>
 
 #include "kv_write.h"
@@ -72,57 +77,47 @@ __device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, 
 __device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Two codes (bytes b0, b1 already placed as 0x00b1_00b0 or b1<<24|b0<<8 forms
-// below) to two exact fp16 values.
-// int8: bytes biased by +128 in the low byte of each half, 0x64 in the high
-// byte give 1024 + (c + 128); subtracting 1152 recovers c exactly.
-__device__ __forceinline__ h2 i8pair_to_h2(uint32_t biased_lo_bytes) {
-  return as_h2(biased_lo_bytes | 0x64006400u) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+// int8 codes to fp16, biased: a byte u = c + 128 (the code with its sign bit
+// flipped) under the exponent byte 0x64 is the fp16 value 1024 + u = c + 1152,
+// exact; one v_perm takes two such bytes and the 0x64 bytes from a constant
+// register.  The bias is taken out of the dot products instead of the codes:
+// q.(c + 1152) = q.c + 1152 * sum(q) per head, and sum_t P'_t (c_t + 1152) =
+// P'.c + 1152 * sum_t P'_t, with sum_t P'_t from one more MFMA on a ones
+// operand (it sums exactly the fp16 weights the P.V MFMA multiplies).
+constexpr uint32_t kExp64 = 0x64646464u;
+constexpr float kI8Bias = 1152.0f;
+__device__ __forceinline__ h2 i8_pair(uint32_t flipped, uint32_t sel) {
+  return as_h2(__builtin_amdgcn_perm(kExp64, flipped, sel));
 }
-// E4M3: byte b in the high byte of each half (b << 8).  fp16 bits
-// sign<<15 | (b & 0x7f)<<7 hold the value 2^-8 times the E4M3 value (both
-// exponent fields line up, the biases differ by 8); multiplying by 256 is exact.
-__device__ __forceinline__ h2 e4m3pair_to_h2(uint32_t hi_bytes) {
-  uint32_t bits = (hi_bytes & 0x80008000u) | ((hi_bytes >> 1) & 0x3F803F80u);
-  return as_h2(bits) * h2{(_Float16)256.0f, (_Float16)256.0f};
+// perm selectors: bytes 0,1 (resp. 2,3) of src1 under 0x64 from src0
+constexpr uint32_t kSelLo = 0x04010400u;
+constexpr uint32_t kSelHi = 0x04030402u;
+
+// E4M3 codes to exact fp16 with the gfx950 conversion (scale 1.0): two codes
+// (the low or high half of a word) per instruction.
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, bool hi) {
+  return as_u32(hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+
+// 4 codes of one word (in order) -> h4, exact.
+template <int KV>
+__device__ __forceinline__ h4 codes4_to_h4(uint32_t w) {
+  if constexpr (KV == PKV_I8) {
+    const uint32_t f = w ^ 0x80808080u;
+    return __builtin_bit_cast(h4, u2{as_u32(i8_pair(f, kSelLo)), as_u32(i8_pair(f, kSelHi))});
+  } else {
+    return __builtin_bit_cast(h4, u2{e4m3_pair(w, false), e4m3_pair(w, true)});
+  }
 }
 
 // 16 codes (one K column) -> two h8 (codes 0-7, 8-15), exact.
 template <int KV>
 __device__ __forceinline__ void codes16_to_h8(u4 w, h8 &lo, h8 &hi) {
-  uint32_t out[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t x = w[k];
-    if constexpr (KV == PKV_I8) {
-      uint32_t u = x ^ 0x80808080u;
-      out[2 * k] = as_u32(i8pair_to_h2(__builtin_amdgcn_perm(0u, u, 0x0c010c00u)));
-      out[2 * k + 1] = as_u32(i8pair_to_h2(__builtin_amdgcn_perm(0u, u, 0x0c030c02u)));
-    } else {
-      out[2 * k] = as_u32(e4m3pair_to_h2(__builtin_amdgcn_perm(0u, x, 0x010c000cu)));
-      out[2 * k + 1] = as_u32(e4m3pair_to_h2(__builtin_amdgcn_perm(0u, x, 0x030c020cu)));
-    }
-  }
-  lo = __builtin_bit_cast(h8, u4{out[0], out[1], out[2], out[3]});
-  hi = __builtin_bit_cast(h8, u4{out[4], out[5], out[6], out[7]});
-}
-
-// Byte e of each of the 4 words (4 tokens of one V column) -> h4, exact.
-template <int KV, int E>
-__device__ __forceinline__ h4 vcodes_to_h4(u4 w) {
-  // perm(src0, src1, sel): result byte i = byte sel[i] of (src0:src1), src1 = bytes 0-3.
-  uint32_t a, b;
-  if constexpr (KV == PKV_I8) {
-    constexpr uint32_t sel = 0x0c000c00u | (uint32_t)(E + 4) << 16 | (uint32_t)E;
-    a = __builtin_amdgcn_perm(w[1] ^ 0x80808080u, w[0] ^ 0x80808080u, sel);
-    b = __builtin_amdgcn_perm(w[3] ^ 0x80808080u, w[2] ^ 0x80808080u, sel);
-    return __builtin_bit_cast(h4, u2{as_u32(i8pair_to_h2(a)), as_u32(i8pair_to_h2(b))});
-  } else {
-    constexpr uint32_t sel = 0x000c000cu | (uint32_t)(E + 4) << 24 | (uint32_t)E << 8;
-    a = __builtin_amdgcn_perm(w[1], w[0], sel);
-    b = __builtin_amdgcn_perm(w[3], w[2], sel);
-    return __builtin_bit_cast(h4, u2{as_u32(e4m3pair_to_h2(a)), as_u32(e4m3pair_to_h2(b))});
-  }
+  const h4 a = codes4_to_h4<KV>(w[0]), b = codes4_to_h4<KV>(w[1]);
+  const h4 c = codes4_to_h4<KV>(w[2]), d = codes4_to_h4<KV>(w[3]);
+  lo = h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  hi = h8{c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
 }
 
 template <int OUT>
@@ -226,6 +221,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     }
   }
 
+  // int8: 1152 * (sum of head r's q), taken out of the biased q.K scores
+  float qbias = 0.0f;
+  if constexpr (KV == PKV_I8) {
+    float qs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs += (float)qf16[i][h][e];
+    qs += xor16(qs);
+    qs += xor32(qs);
+    qbias = kI8Bias * qs;
+  }
+
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
@@ -307,6 +317,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   f4 acc[NACC];
 #pragma unroll
   for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 accp = f4{0.f, 0.f, 0.f, 0.f};   // int8: sum_t P'_t of column r (every row)
 
   const size_t kv_head_off = (size_t)kvh * TILE;
   const size_t block_stride = (size_t)p.num_kv_heads * TILE;
@@ -362,7 +373,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      x[v] = sc[v] * p.qk_scale;
+      if constexpr (KV == PKV_I8)
+        x[v] = (sc[v] - qbias) * p.qk_scale;
+      else
+        x[v] = sc[v] * p.qk_scale;
       if constexpr (QUANT) x[v] *= (float)as_h2(t.ks[v >> 1])[v & 1];
     }
     u4 vw[NL];
@@ -377,8 +391,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
       for (int v = 0; v < 4; ++v) {
         const bool valid = tok0 + v < L;
         x[v] = valid ? x[v] : -INFINITY;
+        if constexpr (!QUANT) {   // word v holds token 4g+v
 #pragma unroll
-        for (int i = 0; i < NL; ++i) vw[i][v] = valid ? vw[i][v] : 0u;
+          for (int i = 0; i < NL; ++i) vw[i][v] = valid ? vw[i][v] : 0u;
+        }
+      }
+      if constexpr (QUANT) {      // byte v of every word holds token 4g+v
+        uint32_t keep = 0u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) keep |= (tok0 + v < L ? 0xFFu : 0u) << (8 * v);
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vw[i][e] &= keep;
       }
       if constexpr (QUANT) {
         const uint32_t keep0 = (tok0 + 0 < L ? 0xFFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
@@ -397,6 +422,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
       l *= alpha;
 #pragma unroll
       for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+      if constexpr (KV == PKV_I8) accp *= alpha;
       m = mn;
     }
     float pr[4];
@@ -431,17 +457,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int v = 0; v < 4; ++v) ps[v] = pr[v] * (float)as_h2(vs[v >> 1])[v & 1] * kPvBoost;
       const h4 pb = h4{(_Float16)ps[0], (_Float16)ps[1], (_Float16)ps[2], (_Float16)ps[3]};
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        acc[4 * i + 0] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 0>(vw[i]), pb,
-                                                               acc[4 * i + 0], 0, 0, 0);
-        acc[4 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 1>(vw[i]), pb,
-                                                               acc[4 * i + 1], 0, 0, 0);
-        acc[4 * i + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 2>(vw[i]), pb,
-                                                               acc[4 * i + 2], 0, 0, 0);
-        acc[4 * i + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(vcodes_to_h4<KV, 3>(vw[i]), pb,
-                                                               acc[4 * i + 3], 0, 0, 0);
+      if constexpr (KV == PKV_I8) {
+        const h4 ones = h4{(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+        accp = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accp, 0, 0, 0);
       }
+      // word e of load i: element 4(16i+r)+e of tokens 4g..4g+3 (1-byte V layout)
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[4 * i + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(codes4_to_h4<KV>(vw[i][e]), pb,
+                                                                 acc[4 * i + e], 0, 0, 0);
     }
   };
 
@@ -484,6 +510,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   }
 
   // ---- combine the waves through LDS ----
+  if constexpr (KV == PKV_I8) {
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[a] -= kI8Bias * accp;
+  }
   l += xor16(l);
   l += xor32(l);
   if (g == 0) {

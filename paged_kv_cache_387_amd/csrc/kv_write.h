@@ -43,12 +43,19 @@ __device__ __forceinline__ float wave_max_all(float x) {
   return x;
 }
 
-// Byte offsets inside a (block, kv head) tile (pool layout of pkv.h).
+// Byte offsets inside a (block, kv head) tile (pool layout of pkv.h).  For
+// V, 2- and 4-byte elements use 4-byte columns, token-minor; 1-byte elements
+// use 16-byte groups of 4 elements x 4 tokens, so that each 4-byte word holds
+// one element of 4 consecutive tokens.
 __device__ __forceinline__ size_t k_byte(int t, int j) {
   return (size_t)((j >> 4) * kBlockSize + t) * 16 + (j & 15);
 }
+template <int EB>
 __device__ __forceinline__ size_t v_byte(int t, int j) {
-  return (size_t)((j >> 2) * kBlockSize + t) * 4 + (j & 3);
+  if constexpr (EB == 1)
+    return (size_t)((j >> 2) * (kBlockSize / 4) + (t >> 2)) * 16 + (j & 3) * 4 + (t & 3);
+  else
+    return (size_t)((j >> 2) * kBlockSize + t) * 4 + (j & 3);
 }
 
 // One wavefront writes token slot t of the K and V tiles of one (block, kv
@@ -84,7 +91,7 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int j = (lane * PER + k) * EB;
-        const size_t off = which ? v_byte(t, j) : k_byte(t, j);
+        const size_t off = which ? v_byte<EB>(t, j) : k_byte(t, j);
         if constexpr (KV == PKV_F32)
           *reinterpret_cast<float *>(tile + off) = x[k];
         else
@@ -109,7 +116,7 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
           else
             code = e4m3_encode_sat(y);
         }
-        tile[which ? v_byte(t, j) : k_byte(t, j)] = (uint8_t)code;
+        tile[which ? v_byte<1>(t, j) : k_byte(t, j)] = (uint8_t)code;
       }
       if (lane == 0) *(which ? v_scale : k_scale) = __builtin_bit_cast(uint16_t, s16);
     }

@@ -264,8 +264,10 @@ def test_layout_offsets_golden(golden_dir):
                 assert np.frombuffer(raw, np.float32)[0] == np.float32(val)
             elif dt == "f16":
                 assert np.frombuffer(raw, np.float16)[0] == np.float16(val)
-            else:
+            elif dt == "i8":
                 assert np.frombuffer(raw, np.int8)[0] == np.sign(val) * 127
+            else:   # the amax element maps to +-448: E4M3 code 0x7E with the sign bit
+                assert raw[0] == (0x7E | (0x80 if val < 0 else 0))
         if "scale_index" in c:
             assert np.nonzero(pools.k_scale)[0].tolist() == [c["scale_index"]]
 
