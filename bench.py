@@ -65,7 +65,7 @@ def kv_bytes(lens, w) -> int:
     if w.cache_dtype in ("i8", "e4m3"):
         b += tok * w.num_kv_heads * 2 * 2
     b += len(lens) * w.num_heads * w.head_dim * (EB[w.q_dtype] + EB[w.out_dtype])
-    b += 4 * int(np.sum((lens + 15) // 16)) + 4 * len(lens)
+    b += 4 * int(np.sum((lens + w.block_size - 1) // w.block_size)) + 4 * len(lens)
     return b
 
 
@@ -228,6 +228,8 @@ def main():
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's, 0: library choice)")
     ap.add_argument("--replicas", type=int, default=0, help="rotating batches (0: default)")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="tokens per physical block (the pool keeps its token capacity)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as copy + write + decode launches instead of the fused "
@@ -265,16 +267,21 @@ def main():
         return pmc_copy()
     factory, replicas, pool = _workloads()[args.workload]
     R = args.replicas or replicas
+    bs = args.block_size
     ws = [factory(r) for r in range(R)]
+    if bs != 16:
+        from synth.workloads import with_block_size
+        ws = [with_block_size(w, bs) for w in ws]
+        pool = pool and -(-pool * 16 // bs)   # the same token capacity
     w0 = ws[0]
     K, Wm = args.steps, args.warmup
     total_steps = Wm + K
     growth = -(-total_steps // R) + 1
     max_len = max(max(int(op[2]) for op in w.ops if op[0] == "allocate") for w in ws)
-    maxb = -(-(max_len + growth) // 16)
-    need_blocks = sum(sum(-(-int(op[2]) // 16) for op in w.ops if op[0] == "allocate")
+    maxb = -(-(max_len + growth) // bs)
+    need_blocks = sum(sum(-(-int(op[2]) // bs) for op in w.ops if op[0] == "allocate")
                       for w in ws)
-    num_blocks = pool or int(math.ceil((need_blocks + R * len(w0.decode_seqs) * (growth // 16 + 2))
+    num_blocks = pool or int(math.ceil((need_blocks + R * len(w0.decode_seqs) * (growth // bs + 2))
                                        * 1.1))
     if pool and num_blocks == w0.num_blocks:
         order = w0.free_order
@@ -285,8 +292,9 @@ def main():
     print(f"# setup {args.workload}: {R} batch(es) of {w0.num_seqs} seqs, pool {num_blocks} "
           f"blocks, table width {maxb}, partition {part}", file=sys.stderr, flush=True)
 
-    alloc = pkv.BlockAllocator(num_blocks, 16, order)
-    cache = pkv.PagedKVCache(num_blocks, w0.num_kv_heads, w0.head_dim, w0.cache_dtype)
+    alloc = pkv.BlockAllocator(num_blocks, bs, order)
+    cache = pkv.PagedKVCache(num_blocks, w0.num_kv_heads, w0.head_dim, w0.cache_dtype,
+                             block_size=bs)
     OFF = 1 << 24
     batches = []
     for r, w in enumerate(ws):
@@ -322,7 +330,7 @@ def main():
                           lens=torch.from_numpy(lens).cuda(), lens_host=lens))
     host_alloc_us = t_host / total_steps * 1e6
     S, H, D, Hkv = w0.num_seqs, w0.num_heads, w0.head_dim, w0.num_kv_heads
-    workspace = pkv.alloc_workspace(S, H, Hkv, D, maxb, part)
+    workspace = pkv.alloc_workspace(S, H, Hkv, D, maxb, part, block_size=bs)
     scale = float(np.float32(w0.scale))
     torch.cuda.synchronize()
 
@@ -373,7 +381,7 @@ def main():
     for st in timed:
         last[st["b"]] = st
     dec_steps = [last[i % R] for i in range(K)] if len(last) == R else timed
-    single_pass = pkv.workspace_bytes(S, H, Hkv, D, maxb, part) == 0
+    single_pass = pkv.workspace_bytes(S, H, Hkv, D, maxb, part, bs) == 0
 
     def run_decode(st):
         b = batches[st["b"]]
@@ -402,7 +410,7 @@ def main():
         "warmup": Wm, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w0.cache_dtype, "data": "synthetic",
         "config": {"workload": w0.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": 16, "kv_dtype": w0.cache_dtype,
+                   "head_dim": D, "block_size": bs, "kv_dtype": w0.cache_dtype,
                    "mean_seq_len": round(mean_len, 1), "pool_blocks": num_blocks,
                    "rotating_batches": R, "partition_size": part,
                    "split_k": not single_pass, "graph": not args.no_graph,

@@ -57,21 +57,24 @@ int pkv_version(void);
 /* ========================================================================
  * KV block pool layout (part of the ABI)
  *
- * A physical block holds block_size (= 16) token slots of K and of V for every
- * kv head: "16 tokens x head_dim x num_kv_heads x 2 (K+V) x dtype bytes"
- * [7yue, section 2].  The K pool and the V pool are separate buffers, each
- *   [num_blocks][num_kv_heads][tile],  tile = block_size * head_dim * eb bytes
- * (eb = element bytes: 4, 2 or 1).  Inside one tile, let j be a byte index into
- * token t's head_dim-vector (j = d * eb + byte of element d):
- *   K tile: byte j of token t at ((j / 16) * block_size + t) * 16 + j % 16
+ * A physical block holds block_size (8, 16 or 32) token slots of K and of V
+ * for every kv head: "16 tokens x head_dim x num_kv_heads x 2 (K+V) x dtype
+ * bytes" [7yue, section 2].  The K pool and the V pool are separate buffers,
+ * each [num_blocks][num_kv_heads][slice], slice = block_size * head_dim * eb
+ * bytes (eb = element bytes: 4, 2 or 1).  A slice is a run of tiles of
+ * TB = min(block_size, 16) tokens (two tiles for 32-token blocks), each
+ * TB * head_dim * eb bytes; token t of the block is position u = t % TB of
+ * tile t / TB.  Inside a tile, let j be a byte index into the token's
+ * head_dim-vector (j = d * eb + byte of element d):
+ *   K tile: byte j of token u at ((j / 16) * TB + u) * 16 + j % 16
  *           (16-byte columns, token-minor: the split of the K cache into
  *           [head_dim*eb/16][block_size][16 bytes] of [7yue, section 5])
- *   V tile, PKV_F32 / PKV_F16: byte j of token t at
- *           ((j / 4) * block_size + t) * 4 + j % 4   (4-byte columns, token-minor)
+ *   V tile, PKV_F32 / PKV_F16: byte j of token u at
+ *           ((j / 4) * TB + u) * 4 + j % 4   (4-byte columns, token-minor)
  *   V tile, PKV_I8 / PKV_E4M3 (one byte per element, j = d): element d of
- *           token t at ((d / 4) * (block_size / 4) + t / 4) * 16 + (d % 4) * 4
- *           + t % 4  (16-byte groups of 4 elements x 4 tokens; each 4-byte word
- *           holds one element of 4 consecutive tokens)
+ *           token u at ((d / 4) * (TB / 4) + u / 4) * 16 + (d % 4) * 4 + u % 4
+ *           (16-byte groups of 4 elements x 4 tokens; each 4-byte word holds
+ *           one element of 4 consecutive tokens)
  * Scales (PKV_I8 / PKV_E4M3 only): fp16 [num_blocks][num_kv_heads][block_size],
  * one array for K and one for V.  Slot s of the cache is token position
  * s % block_size of physical block s / block_size.

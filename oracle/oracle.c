@@ -46,12 +46,14 @@
  *
  * Pool layout (the library's documented ABI layout, re-derived here from its
  * description, not shared):
- *   tile (b, kvh) of K or V starts at byte ((b * Hkv + kvh) * BS * D * eb),
- *   eb = bytes per element.  Inside a tile, byte j of token t's D-vector
- *   (j = d * eb + byte-in-element) lives at
- *     K: ((j / 16) * BS + t) * 16 + j % 16     (16-byte columns, token-minor)
- *     V, eb 2 or 4: ((j / 4) * BS + t) * 4 + j % 4   (4-byte columns, token-minor)
- *     V, eb 1 (int8 / E4M3): ((d / 4) * (BS / 4) + t / 4) * 16 + (d % 4) * 4 + t % 4
+ *   the slice (b, kvh) of K or V starts at byte ((b * Hkv + kvh) * BS * D * eb),
+ *   eb = bytes per element.  A slice is a run of tiles of TB = min(BS, 16)
+ *   tokens (one tile for BS <= 16, two for BS = 32), each TB * D * eb bytes.
+ *   Token t is position u = t % TB of tile t / TB; inside its tile, byte j of
+ *   its D-vector (j = d * eb + byte-in-element) lives at
+ *     K: ((j / 16) * TB + u) * 16 + j % 16     (16-byte columns, token-minor)
+ *     V, eb 2 or 4: ((j / 4) * TB + u) * 4 + j % 4   (4-byte columns, token-minor)
+ *     V, eb 1 (int8 / E4M3): ((d / 4) * (TB / 4) + u / 4) * 16 + (d % 4) * 4 + u % 4
  *        (16-byte groups of 4 elements x 4 tokens, token-minor inside)
  *   scales: fp16 [num_blocks][Hkv][BS].
  */
@@ -171,12 +173,21 @@ static size_t orc_tile_base(int64_t b, int kvh, int Hkv, int BS, int D, int eb)
     return ((size_t)b * Hkv + kvh) * (size_t)BS * D * eb;
 }
 
-static size_t orc_k_byte(int t, int j, int BS) { return ((size_t)(j / 16) * BS + t) * 16 + j % 16; }
-static size_t orc_v_byte(int t, int j, int BS, int eb)
+static int orc_tile_rows(int BS) { return BS < 16 ? BS : 16; }
+
+static size_t orc_k_byte(int t, int j, int BS, int D, int eb)
 {
+    int TB = orc_tile_rows(BS), u = t % TB;
+    return (size_t)(t / TB) * TB * D * eb + ((size_t)(j / 16) * TB + u) * 16 + j % 16;
+}
+
+static size_t orc_v_byte(int t, int j, int BS, int D, int eb)
+{
+    int TB = orc_tile_rows(BS), u = t % TB;
+    size_t tile = (size_t)(t / TB) * TB * D * eb;
     if (eb == 1)
-        return ((size_t)(j / 4) * (BS / 4) + t / 4) * 16 + (j % 4) * 4 + t % 4;
-    return ((size_t)(j / 4) * BS + t) * 4 + j % 4;
+        return tile + ((size_t)(j / 4) * (TB / 4) + u / 4) * 16 + (j % 4) * 4 + u % 4;
+    return tile + ((size_t)(j / 4) * TB + u) * 4 + j % 4;
 }
 
 /* Value of element d of token slot t in tile (b, kvh); is_v selects the V layout. */
@@ -188,7 +199,7 @@ static double orc_load(const uint8_t *pool, const uint16_t *scales, int kind, in
     unsigned char raw[4];
     for (int k = 0; k < eb; k++) {
         int j = d * eb + k;
-        raw[k] = pool[base + (is_v ? orc_v_byte(t, j, BS, eb) : orc_k_byte(t, j, BS))];
+        raw[k] = pool[base + (is_v ? orc_v_byte(t, j, BS, D, eb) : orc_k_byte(t, j, BS, D, eb))];
     }
     switch (kind) {
     case ORC_F32: { float f; memcpy(&f, raw, 4); return (double)f; }
@@ -202,11 +213,11 @@ static double orc_load(const uint8_t *pool, const uint16_t *scales, int kind, in
 }
 
 static void orc_store_raw(uint8_t *pool, int is_v, size_t base, int t, int d, int eb,
-                          const unsigned char *raw, int BS)
+                          const unsigned char *raw, int BS, int D)
 {
     for (int k = 0; k < eb; k++) {
         int j = d * eb + k;
-        pool[base + (is_v ? orc_v_byte(t, j, BS, eb) : orc_k_byte(t, j, BS))] = raw[k];
+        pool[base + (is_v ? orc_v_byte(t, j, BS, D, eb) : orc_k_byte(t, j, BS, D, eb))] = raw[k];
     }
 }
 
@@ -235,12 +246,12 @@ int orc_write(const float *key, const float *value, const int64_t *slot_mapping,
                         unsigned char raw[4];
                         if (cache_kind == ORC_F32) memcpy(raw, &x[d], 4);
                         else { uint16_t h = orc_f32_to_f16(x[d]); memcpy(raw, &h, 2); }
-                        orc_store_raw(pool, which, base, t, d, eb, raw, BS);
+                        orc_store_raw(pool, which, base, t, d, eb, raw, BS, D);
                     }
                 } else {
                     uint16_t s16;
                     orc_quantize_row(x, D, cache_kind, codes, &s16);
-                    for (int d = 0; d < D; d++) orc_store_raw(pool, which, base, t, d, 1, &codes[d], BS);
+                    for (int d = 0; d < D; d++) orc_store_raw(pool, which, base, t, d, 1, &codes[d], BS, D);
                     (which ? v_scale : k_scale)[((size_t)b * Hkv + kvh) * BS + t] = s16;
                 }
             }

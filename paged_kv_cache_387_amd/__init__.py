@@ -331,9 +331,9 @@ def workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: 
 
 
 def alloc_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                    partition_size=0, device="cuda"):
+                    partition_size=0, device="cuda", block_size: int = BLOCK_SIZE):
     n = workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                        partition_size)
+                        partition_size, block_size)
     torch = _torch()
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
@@ -358,10 +358,10 @@ def paged_attention_decode(query, cache: PagedKVCache, block_tables, seq_lens, s
         raise ValueError("out must be float32/float16 [num_seqs, num_heads, head_dim]")
     if D != cache.head_dim or H % cache.num_kv_heads:
         raise ValueError("query shape does not match the cache")
-    need = workspace_bytes(S, H, cache.num_kv_heads, D, maxb, partition_size)
+    need = workspace_bytes(S, H, cache.num_kv_heads, D, maxb, partition_size, cache.block_size)
     if need > 0 and workspace is None:
         workspace = alloc_workspace(S, H, cache.num_kv_heads, D, maxb, partition_size,
-                                    device=query.device)
+                                    device=query.device, block_size=cache.block_size)
     ws_ptr, ws_len = None, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace", numel=need)
@@ -406,10 +406,10 @@ def paged_decode_step(query, key, value, cache: PagedKVCache, block_tables, seq_
         raise ValueError("out must be float32/float16 [num_seqs, num_heads, head_dim]")
     if D != cache.head_dim or H % cache.num_kv_heads:
         raise ValueError("query shape does not match the cache")
-    need = workspace_bytes(S, H, cache.num_kv_heads, D, maxb, partition_size)
+    need = workspace_bytes(S, H, cache.num_kv_heads, D, maxb, partition_size, cache.block_size)
     if need > 0 and workspace is None:
         workspace = alloc_workspace(S, H, cache.num_kv_heads, D, maxb, partition_size,
-                                    device=query.device)
+                                    device=query.device, block_size=cache.block_size)
     ws_ptr, ws_len = None, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace", numel=need)

@@ -104,7 +104,8 @@ extern "C" {
 
 int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order,
                      pkv_alloc **out) {
-  if (!out || num_blocks <= 0 || block_size != 16) return PKV_EINVAL;
+  if (!out || num_blocks <= 0 || (block_size != 8 && block_size != 16 && block_size != 32))
+    return PKV_EINVAL;
   *out = nullptr;
   pkv_alloc *a = new (std::nothrow) pkv_alloc();
   if (!a) return PKV_ENOMEM;

@@ -33,27 +33,45 @@ int check_device() {
 
 int status_of(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EDEVICE; }
 
-// Automatic partition choice: a quarter of the table's width, clamped to
-// [kMinPartBlocks, kMaxPartBlocks] blocks and rounded up to a multiple of the
-// wave count.  Short sequences (up to 1024 tokens) run in a single pass;
-// long ones are split into pieces of at most 4096 tokens so that sequences
-// of very different lengths still spread evenly over the compute units.
-constexpr int32_t kMinPartBlocks = 64;
-constexpr int32_t kMaxPartBlocks = 256;
+bool valid_block_size(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; }
 
-int32_t choose_part_blocks(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks,
-                           int32_t requested_tokens) {
-  (void)num_seqs;
-  (void)num_kv_heads;
+// Decode tiles (16 tokens) a table row of max_blocks blocks can hold.
+int64_t max_tiles_of(int32_t max_blocks, int32_t block_size) {
+  return ((int64_t)max_blocks * block_size + kTile - 1) / kTile;
+}
+
+// Partition sizes in tokens must be whole tiles and whole blocks.
+bool valid_partition(int32_t tokens, int32_t block_size) {
+  const int32_t unit = block_size > kTile ? block_size : kTile;
+  return tokens >= 0 && tokens % unit == 0;
+}
+
+// Automatic partition choice: a quarter of the table's width, clamped to
+// [kMinPartTiles, kMaxPartTiles] tiles and rounded up to a multiple of the
+// wave count (which keeps 32-token blocks whole).  Short sequences (up to
+// 1024 tokens) run in a single pass; long ones are split into pieces of at
+// most 4096 tokens so that sequences of very different lengths still spread
+// evenly over the compute units.
+constexpr int64_t kMinPartTiles = 64;
+constexpr int64_t kMaxPartTiles = 256;
+
+int32_t choose_part_tiles(int32_t max_blocks, int32_t block_size, int32_t requested_tokens) {
+  const int64_t mt = max_tiles_of(max_blocks, block_size);
+  int64_t pt;
   if (requested_tokens > 0) {
-    int32_t pb = requested_tokens / kBlockSize;
-    return pb >= max_blocks ? max_blocks : pb;
+    pt = requested_tokens / kTile;
+  } else {
+    pt = (mt + 3) / 4;
+    if (pt < kMinPartTiles) pt = kMinPartTiles;
+    if (pt > kMaxPartTiles) pt = kMaxPartTiles;
+    pt = (pt + kWaves - 1) / kWaves * kWaves;
   }
-  int64_t pb = (max_blocks + 3) / 4;
-  if (pb < kMinPartBlocks) pb = kMinPartBlocks;
-  if (pb > kMaxPartBlocks) pb = kMaxPartBlocks;
-  pb = (pb + kWaves - 1) / kWaves * kWaves;
-  return pb >= max_blocks ? max_blocks : (int32_t)pb;
+  return pt >= mt ? (int32_t)mt : (int32_t)pt;
+}
+
+int32_t num_parts_of(int32_t max_blocks, int32_t block_size, int32_t part_tiles) {
+  const int64_t mt = max_tiles_of(max_blocks, block_size);
+  return odd_up((int32_t)((mt + part_tiles - 1) / part_tiles));
 }
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
@@ -97,9 +115,9 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t requested) {
   if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-      block_size != kBlockSize || requested < 0 || requested % kBlockSize)
+      !valid_block_size(block_size) || !valid_partition(requested, block_size))
     return PKV_EINVAL;
-  return choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, requested) * kBlockSize;
+  return choose_part_tiles(max_blocks_per_seq, block_size, requested) * kTile;
 }
 
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
@@ -107,12 +125,11 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                        int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_blocks_per_seq <= 0 || block_size != kBlockSize || partition_size < 0 ||
-      partition_size % kBlockSize)
+      max_blocks_per_seq <= 0 || !valid_block_size(block_size) ||
+      !valid_partition(partition_size, block_size))
     return 0;
-  const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
-                                        partition_size);
-  const int32_t parts = odd_up((max_blocks_per_seq + pb - 1) / pb);
+  const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
+  const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
   return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
 }
 
@@ -133,15 +150,15 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
       max_blocks_per_seq <= 0 || partition_size < 0)
     return PKV_EINVAL;
   if (num_heads % num_kv_heads) return PKV_EINVAL;
-  if (block_size != kBlockSize) return PKV_ENOTSUP;
+  if (!valid_block_size(block_size)) return PKV_ENOTSUP;
   if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
   if (num_heads / num_kv_heads > kMaxGroup) return PKV_ENOTSUP;
   // token counts stay in int32
-  if (max_blocks_per_seq > (1 << 26)) return PKV_ENOTSUP;
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return PKV_ENOTSUP;
   if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
   if (out_dtype != PKV_F32 && out_dtype != PKV_F16) return PKV_EINVAL;
   if (q_dtype != (cache_dtype == PKV_F32 ? PKV_F32 : PKV_F16)) return PKV_ENOTSUP;
-  if (partition_size % kBlockSize) return PKV_EINVAL;
+  if (!valid_partition(partition_size, block_size)) return PKV_EINVAL;
   if (!(scale == scale)) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PKV_EINVAL;
@@ -153,9 +170,8 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   if (is_quant(cache_dtype) && (!aligned(k_scale, 8) || !aligned(v_scale, 8)))
     return PKV_EINVAL;
 
-  const int32_t pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq,
-                                        partition_size);
-  const int32_t parts = odd_up((max_blocks_per_seq + pb - 1) / pb);
+  const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
+  const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
   if ((int64_t)num_seqs * num_heads > INT32_MAX || (int64_t)num_seqs * num_kv_heads > INT32_MAX ||
       decode_grid(num_seqs * num_kv_heads, parts) > INT32_MAX)
     return PKV_ENOTSUP;
@@ -184,7 +200,8 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   p.num_heads = num_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_heads / num_kv_heads;
-  p.part_blocks = pb;
+  p.block_size = block_size;
+  p.part_tiles = pt;
   p.num_parts = parts;
   p.num_units = num_seqs * num_kv_heads;
   p.qk_scale = scale * 1.4426950408889634f;
@@ -256,9 +273,8 @@ int paged_kv_write(const void *key, const void *value, int32_t src_dtype, int64_
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || key_stride < 0 ||
       value_stride < 0)
     return PKV_EINVAL;
-  if (num_kv_heads > 65535 || (int64_t)num_blocks * kBlockSize > INT64_MAX / 2)
-    return PKV_ENOTSUP;
-  if (block_size != kBlockSize) return PKV_ENOTSUP;
+  if (num_kv_heads > 65535) return PKV_ENOTSUP;
+  if (!valid_block_size(block_size)) return PKV_ENOTSUP;
   if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
   if (src_dtype != PKV_F32 && src_dtype != PKV_F16) return PKV_EINVAL;
   if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
@@ -289,6 +305,7 @@ int paged_kv_write(const void *key, const void *value, int32_t src_dtype, int64_
   p.num_tokens = num_tokens;
   p.num_blocks = num_blocks;
   p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
   return status_of(launch_write(p, src_dtype, cache_dtype, head_dim,
                                 static_cast<hipStream_t>(stream)));
 }
@@ -298,7 +315,7 @@ int paged_copy_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale
                       int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, void *stream) {
   if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_EINVAL;
-  if (block_size != kBlockSize) return PKV_ENOTSUP;
+  if (!valid_block_size(block_size)) return PKV_ENOTSUP;
   if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
   if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
   if (num_pairs == 0) return PKV_OK;
@@ -316,8 +333,8 @@ int paged_copy_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale
   p.pairs = block_pairs;
   p.num_pairs = num_pairs;
   p.num_blocks = num_blocks;
-  p.block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(cache_dtype);
-  p.scale_elems = is_quant(cache_dtype) ? (int64_t)num_kv_heads * kBlockSize : 0;
+  p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(cache_dtype);
+  p.scale_elems = is_quant(cache_dtype) ? (int64_t)num_kv_heads * block_size : 0;
   return status_of(launch_copy(p, static_cast<hipStream_t>(stream)));
 }
 

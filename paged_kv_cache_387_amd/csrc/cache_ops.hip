@@ -20,21 +20,21 @@ namespace {
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-template <int SRC, int KV, int D>
+template <int SRC, int KV, int D, int BS>
 __global__ __launch_bounds__(64) void write_kernel(WriteParams p) {
-  constexpr int TILE = kBlockSize * D * ebytes<KV>();
+  constexpr int TILE = BS * D * ebytes<KV>();
   const int i = blockIdx.x;
   const int kvh = blockIdx.y;
   const int64_t slot = p.slots[i];
-  if (slot < 0 || slot >= (int64_t)p.num_blocks * kBlockSize) return;
-  const int64_t blk = slot / kBlockSize;
-  const int t = (int)(slot % kBlockSize);
+  if (slot < 0 || slot >= (int64_t)p.num_blocks * BS) return;
+  const int64_t blk = slot / BS;
+  const int t = (int)(slot % BS);
   const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * TILE;
   const size_t esz = SRC == PKV_F32 ? 4 : 2;
   const uint8_t *k_row = static_cast<const uint8_t *>(p.key) + ((size_t)i * p.key_stride + (size_t)kvh * D) * esz;
   const uint8_t *v_row = static_cast<const uint8_t *>(p.value) + ((size_t)i * p.value_stride + (size_t)kvh * D) * esz;
-  const size_t sidx = ((size_t)blk * p.num_kv_heads + kvh) * kBlockSize + t;
-  write_token_wave<SRC, KV, D>(k_row, v_row, p.k_cache + tile, p.v_cache + tile,
+  const size_t sidx = ((size_t)blk * p.num_kv_heads + kvh) * BS + t;
+  write_token_wave<SRC, KV, D, BS>(k_row, v_row, p.k_cache + tile, p.v_cache + tile,
                                p.k_scale ? p.k_scale + sidx : nullptr,
                                p.v_scale ? p.v_scale + sidx : nullptr, t, threadIdx.x);
 }
@@ -60,14 +60,21 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
   }
 }
 
+template <int SRC, int KV, int D>
+hipError_t launch_write_bs(const WriteParams &p, hipStream_t stream) {
+  dim3 grid(p.num_tokens, p.num_kv_heads);
+  switch (p.block_size) {
+    case 8: hipLaunchKernelGGL((write_kernel<SRC, KV, D, 8>), grid, dim3(64), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((write_kernel<SRC, KV, D, 32>), grid, dim3(64), 0, stream, p); break;
+    default: hipLaunchKernelGGL((write_kernel<SRC, KV, D, 16>), grid, dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 template <int SRC, int KV>
 hipError_t launch_write_d(const WriteParams &p, int head_dim, hipStream_t stream) {
-  dim3 grid(p.num_tokens, p.num_kv_heads);
-  if (head_dim == 64)
-    hipLaunchKernelGGL((write_kernel<SRC, KV, 64>), grid, dim3(64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((write_kernel<SRC, KV, 128>), grid, dim3(64), 0, stream, p);
-  return hipGetLastError();
+  return head_dim == 64 ? launch_write_bs<SRC, KV, 64>(p, stream)
+                        : launch_write_bs<SRC, KV, 128>(p, stream);
 }
 
 template <int SRC>

@@ -148,17 +148,24 @@ template <> struct Prefetch<PKV_I8> { static constexpr int NB = PKV_PREFETCH_Q8;
 template <> struct Prefetch<PKV_E4M3> { static constexpr int NB = PKV_PREFETCH_Q8; };
 
 // SRC < 0: decode only.  SRC = PKV_F16 / PKV_F32: fused decode step, the new
-// token's K/V (of that type) is written first (see DecodeParams).
-template <int KV, int D, int OUT, int SRC>
+// token's K/V (of that type) is written first (see DecodeParams).  BS = block
+// size (8, 16 or 32 tokens).  The kernel works on 16-token tiles (the MFMA
+// row count): a 32-token block is two tiles stored one after the other, a
+// 16-token tile spans two 8-token blocks.
+template <int KV, int D, int OUT, int SRC, int BS>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) {
   constexpr int EB = Kv<KV>::EB;
   constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
-  constexpr int TILE = kBlockSize * D * EB;   // bytes of one (block, kv head) tile
+  constexpr int SLICE = BS * D * EB;          // bytes of one (block, kv head) slice
+  constexpr int TPB = BS >= kTile ? BS / kTile : 1;   // tiles per block
+  constexpr bool SPLIT = BS < kTile;          // a tile spans two blocks
+  constexpr int TB = SPLIT ? BS : kTile;      // tokens of a tile within one block
   constexpr int NL = D * EB / 64;             // 16-byte loads per lane per K (and V) tile
   constexpr int NACC = D / 16;                // 16x16 output tiles
   constexpr int E = 4 / EB;                   // head_dim elements per V word
   constexpr int LDS_ROW = D + 4;
   constexpr int NB = Prefetch<KV>::NB;
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
 
   __shared__ float lds_o[kWaves][kMaxGroup][LDS_ROW];
   __shared__ float lds_m[kWaves][kMaxGroup];
@@ -187,19 +194,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   const int G = p.group;
   const int H = p.num_heads;
 
-  const int first = part * p.part_blocks;
-  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks + first + w;
+  const int first = part * p.part_tiles;      // first tile of the partition
+  const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks;
+
+  // Table entries of this wave's tiles first + w + j * kWaves, 64 at a time,
+  // one per lane (readlane picks entry j): the tile's block (the first of its
+  // two blocks when SPLIT; tvb holds the second).  Entries are clamped to
+  // `lim` blocks.
+  auto load_tv = [&](int c0, int lim, int *tvb) {
+    const int tile = first + w + (c0 + lane) * kWaves;
+    int e = SPLIT ? 2 * tile : tile / TPB;
+    e = e < lim ? e : lim - 1;
+    if constexpr (SPLIT) {
+      const int e2 = 2 * tile + 1 < lim ? 2 * tile + 1 : e;
+      *tvb = trow[e2];
+    }
+    return trow[e];
+  };
 
   // Loads that do not depend on the sequence length go first, so that they
   // overlap with the read of seq_lens: the table entries of the wave's first
-  // 64 blocks (one per lane; lanes past the row's end re-read its last entry)
-  // and the q fragment (B operand of the q.K MFMAs, column r = head kvh*G+r;
-  // columns r >= G repeat head kvh*G and their results are never stored).
-  int tv_next;
-  {
-    const int col = first + w + lane * kWaves;
-    tv_next = trow[(col < p.max_blocks ? col : p.max_blocks - 1) - first - w];
-  }
+  // 64 tiles (clamped to the row) and the q fragment (B operand of the q.K
+  // MFMAs, column r = head kvh*G+r; columns r >= G repeat head kvh*G and
+  // their results are never stored).
+  int tvb_next = 0;
+  int tv_next = load_tv(0, p.max_blocks, &tvb_next);
   const size_t qrow = ((size_t)s * H + kvh * G + (r < G ? r : 0)) * D;
   float qf32[NL][4];
   h8 qf16[NL][QUANT ? 2 : 1];
@@ -237,74 +256,83 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   }
 
   int L = p.seq_lens[s];
-  L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
-  const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int nparts_s = (nblk + p.part_blocks - 1) / p.part_blocks;
-  if (first >= nblk) {
+  L = L < 0 ? 0 : (L > p.max_blocks * BS ? p.max_blocks * BS : L);
+  const int nblk = (L + BS - 1) / BS;                 // blocks in use
+  const int ntile = (L + kTile - 1) / kTile;          // tiles in use
+  const int nparts_s = (ntile + p.part_tiles - 1) / p.part_tiles;
+  if (first >= ntile) {
     if (part == 0) {  // empty sequence: zero output rows
       for (int e = threadIdx.x; e < G * D; e += 64 * kWaves)
         store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
     }
     return;
   }
-  const int last = min(first + p.part_blocks, nblk);
+  const int last = min(first + p.part_tiles, ntile);
 
-  // Blocks of this wave: first + w + k * kWaves, k < nb_w, walked in chunks of
-  // 64 whose table entries are held one per lane (readlane picks entry j).
-  const int nb_part = last - first;
-  const int nb_w = nb_part > w ? (nb_part - w + kWaves - 1) / kWaves : 0;
-  auto load_tv = [&](int c0) {
-    const int nc = min(64, nb_w - c0);
-    const int tj = lane < nc ? lane : nc - 1;
-    return trow[(size_t)(c0 + tj) * kWaves];
-  };
+  // Tiles of this wave: first + w + k * kWaves, k < nt_w.
+  const int nt_part = last - first;
+  const int nt_w = nt_part > w ? (nt_part - w + kWaves - 1) / kWaves : 0;
 
   // ---- fused step: copy-on-write of the tail block, then the new token ----
-  // Only the wave that consumes the tail block touches it: it copies the
-  // (block, kv head) slice from cow_src[s] if asked, writes the new token at
-  // position L - 1, and waits for its stores before it issues the load of the
-  // tail tile, so that load sees them.  When the tail tile is not among the
-  // wave's first NB loads, the write runs after those are issued and overlaps
-  // with them.  Other sequences may read the copy source concurrently;
-  // nothing else writes these bytes.
+  // The partition that holds a sequence's tail block first copies that
+  // block's (kv head) slice from cow_src[s] when asked -- all threads of the
+  // workgroup, then a barrier, since with 32-token blocks another wave reads
+  // the other tile of the block.  The wave that consumes the tail tile then
+  // writes the new token at position L - 1 and waits for its stores before it
+  // issues the load of that tile, so the load sees them; when the tail tile is
+  // not among the wave's first NB loads, the write overlaps with those loads.
+  // Other sequences may read the copy source concurrently; nothing else
+  // writes these bytes.
+  const int tail_blk = nblk - 1;
+  size_t tail_slice = 0, tail_sc = 0;
+  bool tail_ok = false;
+  if constexpr (SRC >= 0) {
+    const int tail_tile = ntile - 1;
+    if (tail_tile >= first && tail_tile < last) {
+      const int phys = trow[tail_blk];
+      tail_ok = (unsigned)phys < (unsigned)p.num_blocks;
+      tail_slice = ((size_t)(tail_ok ? phys : 0) * p.num_kv_heads + kvh) * SLICE;
+      tail_sc = ((size_t)(tail_ok ? phys : 0) * p.num_kv_heads + kvh) * BS;
+      const int src = p.cow_src ? p.cow_src[s] : -1;
+      if (tail_ok && (unsigned)src < (unsigned)p.num_blocks && src != phys) {
+        const size_t sslice = ((size_t)src * p.num_kv_heads + kvh) * SLICE;
+        for (int o = threadIdx.x * 16; o < SLICE; o += 64 * kWaves * 16) {
+          *reinterpret_cast<u4 *>(p.k_cache_w + tail_slice + o) =
+              *reinterpret_cast<const u4 *>(p.k_cache_w + sslice + o);
+          *reinterpret_cast<u4 *>(p.v_cache_w + tail_slice + o) =
+              *reinterpret_cast<const u4 *>(p.v_cache_w + sslice + o);
+        }
+        if constexpr (QUANT) {
+          const size_t ssc = ((size_t)src * p.num_kv_heads + kvh) * BS;
+          if (threadIdx.x < BS) {
+            p.k_scale_w[tail_sc + threadIdx.x] = p.k_scale_w[ssc + threadIdx.x];
+            p.v_scale_w[tail_sc + threadIdx.x] = p.v_scale_w[ssc + threadIdx.x];
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the copy lands before anyone reads the block
+        __syncthreads();
+      }
+    }
+  }
   bool step_pending = false;
   auto step_write = [&]() {
     if constexpr (SRC >= 0) {
-      const int tail = nblk - 1;
-      const int phys = p.block_tables[(size_t)s * p.max_blocks + tail];
-      if ((unsigned)phys >= (unsigned)p.num_blocks) return;
-      const size_t tile = ((size_t)phys * p.num_kv_heads + kvh) * TILE;
-      const size_t sc = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize;
-      const int src = p.cow_src ? p.cow_src[s] : -1;
-      if ((unsigned)src < (unsigned)p.num_blocks && src != phys) {
-        const size_t stile = ((size_t)src * p.num_kv_heads + kvh) * TILE;
-        copy_bytes_wave(p.k_cache_w + tile, p.k_cache_w + stile, TILE, lane);
-        copy_bytes_wave(p.v_cache_w + tile, p.v_cache_w + stile, TILE, lane);
-        if constexpr (QUANT) {
-          const size_t ssc = ((size_t)src * p.num_kv_heads + kvh) * kBlockSize;
-          if (lane < kBlockSize) {
-            p.k_scale_w[sc + lane] = p.k_scale_w[ssc + lane];
-            p.v_scale_w[sc + lane] = p.v_scale_w[ssc + lane];
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // the copy lands before the token overwrites its slot
-      }
-      const int t = (L - 1) % kBlockSize;
+      const int t = (L - 1) % BS;
       constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
       const size_t row = ((size_t)s * p.num_kv_heads + kvh) * D * esz;
-      write_token_wave<SRC, KV, D>(static_cast<const uint8_t *>(p.key_new) + row,
-                                   static_cast<const uint8_t *>(p.value_new) + row,
-                                   p.k_cache_w + tile, p.v_cache_w + tile,
-                                   QUANT ? p.k_scale_w + sc + t : nullptr,
-                                   QUANT ? p.v_scale_w + sc + t : nullptr, t, lane);
+      write_token_wave<SRC, KV, D, BS>(static_cast<const uint8_t *>(p.key_new) + row,
+                                       static_cast<const uint8_t *>(p.value_new) + row,
+                                       p.k_cache_w + tail_slice, p.v_cache_w + tail_slice,
+                                       QUANT ? p.k_scale_w + tail_sc + t : nullptr,
+                                       QUANT ? p.v_scale_w + tail_sc + t : nullptr, t, lane);
       __builtin_amdgcn_s_waitcnt(0);     // stores complete before the tail tile is loaded
     }
   };
   if constexpr (SRC >= 0) {
-    const int tail = nblk - 1;
-    if (tail >= first && tail < last && w == (tail - first) % kWaves) {
-      // the tail is this wave's last block, entry nb_w - 1 of its walk
-      if (nb_w - 1 < Prefetch<KV>::NB)
+    const int tail_tile = ntile - 1;
+    if (tail_ok && w == (tail_tile - first) % kWaves) {
+      // the tail tile is this wave's last, entry nt_w - 1 of its walk
+      if (nt_w - 1 < Prefetch<KV>::NB)
         step_write();
       else
         step_pending = true;
@@ -319,8 +347,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
   f4 accp = f4{0.f, 0.f, 0.f, 0.f};   // int8: sum_t P'_t of column r (every row)
 
-  const size_t kv_head_off = (size_t)kvh * TILE;
-  const size_t block_stride = (size_t)p.num_kv_heads * TILE;
+  const size_t kv_head_off = (size_t)kvh * SLICE;
+  const size_t block_stride = (size_t)p.num_kv_heads * SLICE;
 
   struct Tile {
     u4 k[NL];
@@ -329,27 +357,48 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     bool ok;
   };
 
-  // Start the loads of a block whose table entry is lane j of tv.
-  auto issue = [&](int tv, int j, Tile &t) {
-    int phys = __builtin_amdgcn_readlane(tv, j);
-    t.ok = (unsigned)phys < (unsigned)p.num_blocks;
-    phys = t.ok ? phys : 0;
-    const uint8_t *kb = p.k_cache + (size_t)phys * block_stride + kv_head_off;
-    const uint8_t *vb = p.v_cache + (size_t)phys * block_stride + kv_head_off;
+  // Start the loads of tile `tile` (absolute), whose table entries are lane j
+  // of tv (and tvb).  Lane (r, g) reads token r of the tile for K and tokens
+  // 4g..4g+3 for V and the scales; with SPLIT, tokens 0-7 come from the first
+  // block and 8-15 from the second.
+  auto issue = [&](int tv, int tvb, int j, int tile, Tile &t) {
+    int pa = __builtin_amdgcn_readlane(tv, j);
+    // with SPLIT, a second block past the sequence's end (its tokens are all
+    // masked) is read from the first block instead
+    int pb = SPLIT && 2 * tile + 1 < nblk ? __builtin_amdgcn_readlane(tvb, j) : pa;
+    t.ok = (unsigned)pa < (unsigned)p.num_blocks && (unsigned)pb < (unsigned)p.num_blocks;
+    pa = t.ok ? pa : 0;
+    pb = t.ok ? pb : 0;
+    // Slices are runs of TB-token tiles (TB = 8 when SPLIT, else 16; a
+    // 32-token block holds two): this tile's bytes start at tile_off.
+    const int tq = SPLIT ? 0 : tile % TPB;               // tile within its block
+    const size_t tile_off = (size_t)tq * (TB * D * EB);
+    const int pk = SPLIT && r >= 8 ? pb : pa;            // block of this lane's K token
+    const int pv = SPLIT && g >= 2 ? pb : pa;            // block of this lane's V tokens
+    const int tk = SPLIT ? (r & 7) : r;                  // K token within its tile
+    const int tv0 = SPLIT ? 4 * (g & 1) : 4 * g;         // first V token within its tile
+    const uint8_t *kb = p.k_cache + (size_t)pk * block_stride + kv_head_off + tile_off;
+    const uint8_t *vb = p.v_cache + (size_t)pv * block_stride + kv_head_off + tile_off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) t.k[i] = load16_stream(kb + (size_t)(64 * i + lane) * 16);
+    for (int i = 0; i < NL; ++i)
+      t.k[i] = load16_stream(kb + (size_t)((4 * i + g) * TB + tk) * 16);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) t.v[i] = load16_stream(vb + (size_t)(16 * i + r) * 64 + 16 * g);
+    for (int i = 0; i < NL; ++i) {
+      if constexpr (EB == 1)
+        t.v[i] = load16_stream(vb + (size_t)((16 * i + r) * (TB / 4) + tv0 / 4) * 16);
+      else
+        t.v[i] = load16_stream(vb + (size_t)((16 * i + r) * TB + tv0) * 4);
+    }
     if constexpr (QUANT) {
-      const size_t so = ((size_t)phys * p.num_kv_heads + kvh) * kBlockSize + 4 * g;
+      const size_t so = ((size_t)pv * p.num_kv_heads + kvh) * BS + tq * kTile + tv0;
       t.ks = *reinterpret_cast<const u2 *>(p.k_scale + so);
       t.vs = *reinterpret_cast<const u2 *>(p.v_scale + so);
     }
   };
 
-  // Fold block blk (its tile already loaded) into the running state.
-  auto consume = [&](int blk, Tile &t) {
-    // q.K for the block: S^T[token 4g+v][head r] in sc[v]
+  // Fold tile `tile` (its data already loaded) into the running state.
+  auto consume = [&](int tile, Tile &t) {
+    // q.K for the tile: S^T[token 4g+v][head r] in sc[v]
     f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -368,8 +417,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qf16[i][QUANT ? 1 : 0], sc, 0, 0, 0);
       }
     }
-    if (!t.ok) return;  // table entry outside the pool: block skipped
-    const int tok0 = blk * kBlockSize + 4 * g;
+    if (!t.ok) return;  // table entry outside the pool: tile skipped
+    const int tok0 = tile * kTile + 4 * g;
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -383,10 +432,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int i = 0; i < NL; ++i) vw[i] = t.v[i];
     u2 vs = t.vs;
-    // Only a sequence's last block can be partial (uniform per wave).  Its
+    // Only a sequence's last tile can be partial (uniform per wave).  Its
     // unwritten slots may hold anything, NaN included: their scores become
     // -inf and their V words (and V scales) zero.
-    if (__builtin_expect((blk + 1) * kBlockSize > L, 0)) {
+    if (__builtin_expect((tile + 1) * kTile > L, 0)) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const bool valid = tok0 + v < L;
@@ -404,8 +453,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
         for (int i = 0; i < NL; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) vw[i][e] &= keep;
-      }
-      if constexpr (QUANT) {
         const uint32_t keep0 = (tok0 + 0 < L ? 0xFFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
         const uint32_t keep1 = (tok0 + 2 < L ? 0xFFFFu : 0u) | (tok0 + 3 < L ? 0xFFFF0000u : 0u);
         vs = u2{vs[0] & keep0, vs[1] & keep1};
@@ -416,7 +463,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     bm = fmaxf(bm, xor32(bm));
     const float mn = fmaxf(m, bm);
     // Rescale only when some column's running max rose (m = -inf before the
-    // first block, so the first block always rescales: alpha = 0).
+    // first tile, so the first tile always rescales: alpha = 0).
     if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
       const float alpha = exp2f(m - mn);
       l *= alpha;
@@ -471,19 +518,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     }
   };
 
-  // ---- block loop: a ring of NB tiles, each refilled right after use ----
-  // The wave's blocks are walked in chunks of up to 64 (one table entry per
+  // ---- tile loop: a ring of NB tiles, each refilled right after use ----
+  // The wave's tiles are walked in chunks of up to 64 (one table entry per
   // lane).  Within a chunk the steady-state rounds issue every load
   // unconditionally, so the compiler's wait counts stay exact and NB - 1
   // tiles remain in flight while one is consumed; only the last round of a
   // chunk guards its loads.
-  for (int c0 = 0; c0 < nb_w; c0 += 64) {
-    const int nc = min(64, nb_w - c0);
-    const int tv = tv_next;
-    const int blk0 = first + w + c0 * kWaves;   // block of chunk entry 0
+  for (int c0 = 0; c0 < nt_w; c0 += 64) {
+    const int nc = min(64, nt_w - c0);
+    const int tv = tv_next, tvb = tvb_next;
+    const int t0 = first + w + c0 * kWaves;   // tile of chunk entry 0
     Tile ring[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) issue(tv, j < nc ? j : nc - 1, ring[j]);
+    for (int j = 0; j < NB; ++j) {
+      const int jj = j < nc ? j : nc - 1;
+      issue(tv, tvb, jj, t0 + jj * kWaves, ring[j]);
+    }
     if (step_pending) {   // overlaps with the loads just issued
       step_write();
       step_pending = false;
@@ -492,21 +542,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     for (; k0 + 2 * NB <= nc; k0 += NB) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        consume(blk0 + (k0 + j) * kWaves, ring[j]);
-        issue(tv, k0 + j + NB, ring[j]);
+        consume(t0 + (k0 + j) * kWaves, ring[j]);
+        issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kWaves, ring[j]);
       }
     }
     // last round: the ring holds entries k0 .. k0+NB-1 (those < nc), at most
     // NB - 1 further entries remain to be loaded
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (k0 + j < nc) consume(blk0 + (k0 + j) * kWaves, ring[j]);
-      if (k0 + j + NB < nc) issue(tv, k0 + j + NB, ring[j]);
+      if (k0 + j < nc) consume(t0 + (k0 + j) * kWaves, ring[j]);
+      if (k0 + j + NB < nc) issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kWaves, ring[j]);
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      if (k0 + NB + j < nc) consume(blk0 + (k0 + NB + j) * kWaves, ring[j]);
-    if (c0 + 64 < nb_w) tv_next = load_tv(c0 + 64);
+      if (k0 + NB + j < nc) consume(t0 + (k0 + NB + j) * kWaves, ring[j]);
+    if (c0 + 64 < nt_w) tv_next = load_tv(c0 + 64, p.max_blocks, &tvb_next);
   }
 
   // ---- combine the waves through LDS ----
@@ -575,9 +625,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const int row = blockIdx.x;              // s * H + h
   const int s = row / p.num_heads;
   int L = p.seq_lens[s];
-  L = L < 0 ? 0 : (L > p.max_blocks * kBlockSize ? p.max_blocks * kBlockSize : L);
-  const int nblk = (L + kBlockSize - 1) / kBlockSize;
-  const int np = (nblk + p.part_blocks - 1) / p.part_blocks;
+  L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
+  const int ntile = (L + kTile - 1) / kTile;
+  const int np = (ntile + p.part_tiles - 1) / p.part_tiles;
   if (np <= 1) return;   // written directly by the decode kernel
   const int t = threadIdx.x;
   const size_t base = (size_t)row * p.num_parts;
@@ -615,11 +665,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   }
 }
 
-template <int KV, int D, int OUT, int SRC>
+template <int KV, int D, int OUT, int SRC, int BS>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = decode_grid(p.num_units, p.num_parts);
-  hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC>), dim3((unsigned)grid), dim3(64 * kWaves),
-                     0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS>), dim3((unsigned)grid),
+                     dim3(64 * kWaves), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.num_parts <= 1) return err;
   hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_seqs * p.num_heads),
@@ -627,10 +677,19 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int KV, int D, int OUT, int SRC>
+hipError_t launch_bs(const DecodeParams &p, hipStream_t stream) {
+  switch (p.block_size) {
+    case 8: return launch_typed<KV, D, OUT, SRC, 8>(p, stream);
+    case 32: return launch_typed<KV, D, OUT, SRC, 32>(p, stream);
+    default: return launch_typed<KV, D, OUT, SRC, 16>(p, stream);
+  }
+}
+
 template <int KV, int D, int SRC>
 hipError_t launch_out(const DecodeParams &p, int out_dtype, hipStream_t stream) {
-  return out_dtype == PKV_F32 ? launch_typed<KV, D, PKV_F32, SRC>(p, stream)
-                              : launch_typed<KV, D, PKV_F16, SRC>(p, stream);
+  return out_dtype == PKV_F32 ? launch_bs<KV, D, PKV_F32, SRC>(p, stream)
+                              : launch_bs<KV, D, PKV_F16, SRC>(p, stream);
 }
 
 template <int KV, int SRC>

@@ -43,27 +43,37 @@ __device__ __forceinline__ float wave_max_all(float x) {
   return x;
 }
 
-// Byte offsets inside a (block, kv head) tile (pool layout of pkv.h).  For
-// V, 2- and 4-byte elements use 4-byte columns, token-minor; 1-byte elements
-// use 16-byte groups of 4 elements x 4 tokens, so that each 4-byte word holds
-// one element of 4 consecutive tokens.
+// Byte offsets of element byte j of token t inside a (block, kv head) slice
+// of BS tokens (pool layout of pkv.h).  A slice is a run of tiles of
+// TB = min(BS, 16) tokens (two for BS = 32).  Inside a tile, K uses 16-byte
+// columns, token-minor; V of 2- and 4-byte elements 4-byte columns,
+// token-minor; V of 1-byte elements 16-byte groups of 4 elements x 4
+// tokens, so that each 4-byte word holds one element of 4 consecutive tokens.
+template <int BS> constexpr int tile_rows() { return BS < 16 ? BS : 16; }
+
+template <int BS, int D, int EB>
 __device__ __forceinline__ size_t k_byte(int t, int j) {
-  return (size_t)((j >> 4) * kBlockSize + t) * 16 + (j & 15);
+  constexpr int TB = tile_rows<BS>();
+  const int u = t % TB;
+  return (size_t)(t / TB) * (TB * D * EB) + (size_t)((j >> 4) * TB + u) * 16 + (j & 15);
 }
-template <int EB>
+template <int BS, int D, int EB>
 __device__ __forceinline__ size_t v_byte(int t, int j) {
+  constexpr int TB = tile_rows<BS>();
+  const int u = t % TB;
+  const size_t tile = (size_t)(t / TB) * (TB * D * EB);
   if constexpr (EB == 1)
-    return (size_t)((j >> 2) * (kBlockSize / 4) + (t >> 2)) * 16 + (j & 3) * 4 + (t & 3);
+    return tile + (size_t)((j >> 2) * (TB / 4) + (u >> 2)) * 16 + (j & 3) * 4 + (u & 3);
   else
-    return (size_t)((j >> 2) * kBlockSize + t) * 4 + (j & 3);
+    return tile + (size_t)((j >> 2) * TB + u) * 4 + (j & 3);
 }
 
-// One wavefront writes token slot t of the K and V tiles of one (block, kv
-// head): src rows k_row / v_row hold D elements of SRC type; the scale
+// One wavefront writes token slot t of the K and V slices of one (block, kv
+// head) of BS tokens: src rows k_row / v_row hold D elements of SRC type; the scale
 // pointers address the slot's fp16 scale (quantized caches only).  Lane l
 // owns elements l*D/64 .. (l+1)*D/64 - 1.  The source loads are issued before
 // anything else so they overlap.
-template <int SRC, int KV, int D>
+template <int SRC, int KV, int D, int BS>
 __device__ __forceinline__ void write_token_wave(const void *k_row, const void *v_row,
                                                  uint8_t *k_tile, uint8_t *v_tile,
                                                  uint16_t *k_scale, uint16_t *v_scale, int t,
@@ -91,7 +101,7 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int j = (lane * PER + k) * EB;
-        const size_t off = which ? v_byte<EB>(t, j) : k_byte(t, j);
+        const size_t off = which ? v_byte<BS, D, EB>(t, j) : k_byte<BS, D, EB>(t, j);
         if constexpr (KV == PKV_F32)
           *reinterpret_cast<float *>(tile + off) = x[k];
         else
@@ -116,7 +126,7 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
           else
             code = e4m3_encode_sat(y);
         }
-        tile[which ? v_byte<1>(t, j) : k_byte(t, j)] = (uint8_t)code;
+        tile[which ? v_byte<BS, D, 1>(t, j) : k_byte<BS, D, 1>(t, j)] = (uint8_t)code;
       }
       if (lane == 0) *(which ? v_scale : k_scale) = __builtin_bit_cast(uint16_t, s16);
     }

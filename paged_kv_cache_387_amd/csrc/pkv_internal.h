@@ -10,7 +10,7 @@
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;   // tokens per physical block
+constexpr int kTile = 16;        // tokens per decode tile (the MFMA row count)
 #ifndef PKV_WAVES
 #define PKV_WAVES 4
 #endif
@@ -39,8 +39,9 @@ struct DecodeParams {
   int num_heads;
   int num_kv_heads;
   int group;        // num_heads / num_kv_heads
-  int part_blocks;  // blocks per partition
-  int num_parts;    // partitions in the grid (ceil(max_blocks / part_blocks))
+  int block_size;   // tokens per physical block: 8, 16 or 32
+  int part_tiles;   // 16-token tiles per partition (whole blocks)
+  int num_parts;    // partitions in the grid (>= ceil(max tokens / 16 / part_tiles))
   int num_units;    // num_seqs * num_kv_heads
   float qk_scale;   // scale * log2(e): scores are kept in base 2
   // Fused decode step only: the new token of each sequence (row s of
@@ -84,6 +85,7 @@ struct WriteParams {
   int num_tokens;
   int num_blocks;
   int num_kv_heads;
+  int block_size;
 };
 
 struct CopyParams {

@@ -227,6 +227,22 @@ def custom(name: str, lens, H: int, Hkv: int, D: int, cache_dtype: str = "f16",
                    partition_size=partition_size)
 
 
+def with_block_size(w: Workload, block_size: int) -> Workload:
+    """The same workload (same token script, same values) on blocks of
+    `block_size` tokens: the pool keeps its token capacity and gets a free
+    order of its own; table rows hold the same number of tokens."""
+    import copy
+    w2 = copy.copy(w)
+    tokens = w.max_blocks_per_seq * w.block_size
+    w2.block_size = block_size
+    w2.max_blocks_per_seq = -(-tokens // block_size)
+    w2.num_blocks = -(-w.num_blocks * w.block_size // block_size)
+    w2.free_order = permutation(stream_key(w.seed, "free_order", block_size), w2.num_blocks)
+    w2.name = f"{w.name}_bs{block_size}"
+    w2.memo = None
+    return w2
+
+
 def with_decode_step(w: Workload) -> Workload:
     """The same workload followed by one decode step: every decode sequence
     appends one token (position = its current length) and writes it."""
@@ -245,7 +261,8 @@ def with_decode_step(w: Workload) -> Workload:
     w2.ops = list(w.ops) + [("step",)] + [("append", s) for s in w.decode_seqs] + \
         [("write", s, lens.get(s, 0), 1) for s in w.decode_seqs]
     w2.max_blocks_per_seq = max(w.max_blocks_per_seq,
-                                max(-(-(lens.get(s, 0) + 1) // 16) for s in w.decode_seqs))
+                                max(-(-(lens.get(s, 0) + 1) // w.block_size)
+                                    for s in w.decode_seqs))
     w2.name = w.name + "_step"
     w2.memo = None
     return w2

@@ -52,6 +52,15 @@ def test_partition_and_workspace_sizes():
         p = pkv.partition_size(S, Hkv, mb)
         assert p % 16 == 0 and (p // 16 == mb or (p // 16) % 4 == 0)
     assert pkv.lib().paged_attention_partition_size(1, 1, 4, 16, 24) == pkv.EINVAL
+    # other block sizes: partitions are whole 16-token tiles and whole blocks
+    assert pkv.partition_size(8, 8, 4096, requested=512, block_size=8) == 512
+    assert pkv.partition_size(8, 8, 1024, requested=512, block_size=32) == 512
+    assert pkv.lib().paged_attention_partition_size(8, 8, 1024, 32, 48) == pkv.EINVAL
+    assert pkv.lib().paged_attention_partition_size(8, 8, 1024, 12, 0) == pkv.EINVAL
+    # the automatic choice depends on the table's width in tokens, not in blocks
+    for bs in (8, 16, 32):
+        mb = 32768 // bs
+        assert pkv.partition_size(8, 8, mb, block_size=bs) == 4096
 
 
 def _decode_status(**kw):
@@ -73,7 +82,9 @@ def _decode_status(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), pkv.ENOTSUP),
-    (dict(block_size=32), pkv.ENOTSUP),
+    (dict(block_size=12), pkv.ENOTSUP),                      # block sizes: 8, 16, 32
+    (dict(block_size=64), pkv.ENOTSUP),
+    (dict(block_size=32, partition_size=48), pkv.EINVAL),     # not whole 32-token blocks
     (dict(num_heads=9), pkv.EINVAL),
     (dict(num_heads=64, num_kv_heads=2), pkv.ENOTSUP),       # group of 32 > 16
     (dict(q_dtype=pkv.F32), pkv.ENOTSUP),
@@ -96,11 +107,11 @@ def test_write_and_copy_argument_validation():
     L = pkv.lib()
     P = ctypes.c_void_p
     b = P(1 << 20)
-    # head_dim 96 unsupported; block size 8 unsupported; bad src dtype; stride < row
+    # head_dim 96 unsupported; block size 12 unsupported; bad src dtype; stride < row
     assert L.paged_kv_write(b, b, pkv.F16, 0, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 96,
                             16, None) == pkv.ENOTSUP
     assert L.paged_kv_write(b, b, pkv.F16, 0, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 64,
-                            8, None) == pkv.ENOTSUP
+                            12, None) == pkv.ENOTSUP
     assert L.paged_kv_write(b, b, pkv.I8, 0, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 64,
                             16, None) == pkv.EINVAL
     assert L.paged_kv_write(b, b, pkv.F16, 64, 0, b, 4, b, b, None, None, pkv.F16, 8, 2, 64,

@@ -58,13 +58,13 @@ ops = st.lists(st.tuples(st.sampled_from(["alloc", "append", "append", "fork", "
 
 
 @settings(max_examples=300, deadline=None)
-@given(ops, st.randoms(use_true_random=False))
-def test_random_ops_match_model(seq, rnd):
+@given(ops, st.randoms(use_true_random=False), st.sampled_from([8, 16, 32]))
+def test_random_ops_match_model(seq, rnd, bs):
     n = 20
     order = list(range(n))
     rnd.shuffle(order)
-    lib = pkv.BlockAllocator(n, 16, order)
-    model = BlockManagerModel(n, 16, order)
+    lib = pkv.BlockAllocator(n, bs, order)
+    model = BlockManagerModel(n, bs, order)
     for kind, a, b, k in seq:
         _apply(lib, model, kind, a, b, k)
         model.check_invariants()
@@ -90,8 +90,9 @@ def test_slots_and_errors():
     assert e.value.status == pkv.EINVAL
     with pytest.raises(pkv.PkvError):
         pkv.BlockAllocator(4, 16, [0, 1, 1, 2])
-    with pytest.raises(pkv.PkvError):
-        pkv.BlockAllocator(4, 8)
+    for bad in (4, 12, 64):   # block sizes other than 8, 16, 32
+        with pytest.raises(pkv.PkvError):
+            pkv.BlockAllocator(4, bad)
 
 
 def test_batched_append_matches_single_appends():
@@ -114,11 +115,14 @@ def test_batched_append_matches_single_appends():
     lambda: workloads.c5_shared_prefix(),
     lambda: workloads.c5_shared_prefix(cow_pairs=True),
     lambda: workloads.c3_long_context(),
+    lambda: workloads.with_block_size(workloads.c2_qwen3_32b_layer(), 8),
+    lambda: workloads.with_block_size(workloads.c5_shared_prefix(cow_pairs=True), 32),
+    lambda: workloads.with_block_size(workloads.c5_shared_prefix(cow_pairs=True), 8),
 ])
 def test_workload_scripts_give_identical_tables(make):
     w = make()
-    lib = pkv.BlockAllocator(w.num_blocks, 16, w.free_order)
-    model = BlockManagerModel(w.num_blocks, 16, w.free_order)
+    lib = pkv.BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+    model = BlockManagerModel(w.num_blocks, w.block_size, w.free_order)
     pairs_l, pairs_m = [], []
     for op in w.ops:
         if op[0] == "allocate":

@@ -1,0 +1,132 @@
+"""GPU parity for block sizes 8 and 32 (16 is covered everywhere else):
+cache writes and copies bit-exact against the oracle's pools, decodes and
+fused decode steps (with copy-on-write) within tolerance, on ragged small
+workloads over several partition sizes and on two full-size configurations."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from oracle.replay import oracle_output, replay as oracle_replay  # noqa: E402
+from synth import workloads  # noqa: E402
+
+from gpu_helpers import check_close, check_pools_equal, say  # noqa: E402
+
+BS = [8, 32]
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_387_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+@pytest.mark.parametrize("bs", BS)
+@pytest.mark.parametrize("src,cache_dt,D,Hkv", [("f32", "f32", 64, 2), ("f16", "f16", 128, 8),
+                                                ("f16", "i8", 128, 8), ("f16", "e4m3", 64, 2)])
+def test_write_and_copy_bit_exact(pkv, bs, src, cache_dt, D, Hkv):
+    say(f"write+copy bs={bs} src={src} cache={cache_dt} D={D} Hkv={Hkv}")
+    rng = np.random.default_rng(hash((bs, src, cache_dt, D)) % 2**32)
+    nb = 9
+    T = nb * bs - 7
+    slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int64)
+    slots[2] = -1
+    dt = np.float32 if src == "f32" else np.float16
+    key = (rng.standard_normal((T, Hkv, D)) * rng.choice([0.01, 1, 30], (T, Hkv, 1))).astype(dt)
+    val = (rng.standard_normal((T, Hkv, D)) * rng.choice([0.01, 1, 30], (T, Hkv, 1))).astype(dt)
+    pairs = np.array([[2, 7], [0, 8], [5, 5], [4, -1]], np.int32)
+    pools = oracle.Pools(nb, Hkv, D, cache_dt, block_size=bs)
+    oracle.write(pools, key.astype(np.float32), val.astype(np.float32), slots)
+    oracle.copy_blocks(pools, pairs)
+    cache = pkv.PagedKVCache(nb, Hkv, D, cache_dt, block_size=bs, fill_byte=0xFF)
+    pkv.paged_kv_write(torch.from_numpy(key).cuda(), torch.from_numpy(val).cuda(),
+                       torch.from_numpy(slots).cuda(), cache)
+    pkv.paged_copy_blocks(cache, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    check_pools_equal(cache, pools, f"bs={bs} {src}->{cache_dt}")
+
+
+def _ragged(cache_dt, bs, D=128, H=16, Hkv=2, lens=(1, 7, 8, 9, 15, 16, 17, 31, 33, 100, 257)):
+    w = workloads.custom(f"bs{bs}_{cache_dt}_{D}", list(lens), H, Hkv, D, cache_dt, seed=11,
+                         out_dtype="f32" if cache_dt == "f32" else "f16")
+    return workloads.with_block_size(w, bs)
+
+
+DECODE = [(dt, D, H, Hkv) for dt, D, H, Hkv in
+          [("f16", 128, 16, 2), ("f32", 64, 8, 2), ("i8", 128, 16, 2), ("e4m3", 64, 8, 2)]]
+
+
+@pytest.mark.parametrize("bs", BS)
+@pytest.mark.parametrize("dt,D,H,Hkv", DECODE)
+def test_decode_small(pkv, bs, dt, D, H, Hkv):
+    from paged_kv_cache_387_amd import driver
+    w = _ragged(dt, bs, D, H, Hkv)
+    w.memo = {}
+    say(f"decode {w.name}: S={w.num_seqs} H={H}/{Hkv} D={D} {dt} bs={bs}")
+    ro = oracle_replay(w)
+    rg = driver.replay(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(rg.tables_host, ro.block_tables)
+    check_pools_equal(rg.cache, ro.pools, w.name)
+    ref = oracle_output(ro, w)
+    for part in [0, 32, 64, 1 << 20]:
+        out = driver.decode(rg, w, partition_size=part)
+        torch.cuda.synchronize()
+        check_close(out, ref, dt, f"{w.name} partition={part}")
+
+
+STEP = {
+    "ragged_f16": lambda bs: workloads.with_decode_step(_ragged("f16", bs)),
+    "ragged_i8": lambda bs: workloads.with_decode_step(_ragged("i8", bs)),
+    "c5_cow_f16": lambda bs: workloads.with_block_size(
+        workloads.c5_shared_prefix(num_seqs=8, prefix=96, suffix_lo=1, suffix_hi=47,
+                                   cow_pairs=True, H=16, Hkv=2, D=128, num_blocks=96), bs),
+}
+
+
+@pytest.mark.parametrize("bs", BS)
+@pytest.mark.parametrize("name", list(STEP))
+def test_fused_step(pkv, bs, name):
+    from paged_kv_cache_387_amd import driver
+    w = STEP[name](bs)
+    w.memo = {}
+    ro = oracle_replay(w)
+    say(f"fused step {w.name} bs={bs}: copies {len(ro.step_pairs)}")
+    for part in [0, 32, 64]:
+        rg = driver.replay(w, stop_at_step=True)
+        out, slots, pairs, tables, lens = driver.fused_step(rg, w, partition_size=part)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots, ro.step_slots)
+        assert np.array_equal(pairs, ro.step_pairs)
+        assert np.array_equal(tables, ro.block_tables)
+        check_pools_equal(rg.cache, ro.pools, f"{w.name} partition={part} pools")
+        check_close(out, oracle_output(ro, w), w.cache_dtype, f"{w.name} partition={part}")
+    if name.startswith("c5_cow"):
+        assert len(ro.step_pairs) > 0
+
+
+@pytest.mark.parametrize("bs,make", [
+    (8, lambda: workloads.c2_qwen3_32b_layer()),
+    (32, lambda: workloads.c2_qwen3_32b_layer()),
+    (32, lambda: workloads.c4_quantized("i8")),
+])
+def test_full_size(pkv, bs, make):
+    from paged_kv_cache_387_amd import driver
+    w = workloads.with_block_size(make(), bs)
+    w.memo = {}
+    say(f"full size {w.name}: S={w.num_seqs} pool={w.num_blocks} bs={bs}")
+    ro = oracle_replay(w)
+    rg = driver.replay(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(rg.tables_host, ro.block_tables)
+    check_pools_equal(rg.cache, ro.pools, w.name)
+    w.memo = None
+    ref = oracle_output(ro, w)
+    out = driver.decode(rg, w, partition_size=0)
+    torch.cuda.synchronize()
+    check_close(out, ref, w.cache_dtype, w.name)

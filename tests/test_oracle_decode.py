@@ -248,8 +248,9 @@ def test_layout_offsets_golden(golden_dir):
     cases = json.load(open(os.path.join(golden_dir, "layout_offsets.json")))["cases"]
     for c in cases:
         Hkv, D, dt = c["Hkv"], c["D"], c["dtype"]
-        nb = c["slot"] // BS + 2
-        pools = oracle.Pools(nb, Hkv, D, dt, sentinel=None)   # all zero
+        bs = c.get("block_size", BS)
+        nb = c["slot"] // bs + 2
+        pools = oracle.Pools(nb, Hkv, D, dt, block_size=bs, sentinel=None)   # all zero
         K = np.zeros((1, Hkv, D), np.float32)
         V = np.zeros((1, Hkv, D), np.float32)
         # values whose every byte is nonzero in f32 and f16 (1.2345678: 0x3F9E0651 / 0x3CF0)
