@@ -195,6 +195,12 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write
     f_scale = nbytes / 1024.0 / copy_value(copy_fetch_csv)
     w_scale = nbytes / 1024.0 / copy_value(copy_write_csv)
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    def is_plain_decode(name):
+        # decode_kernel<KV, D, OUT, SRC, BS>: SRC = -1 is paged_attention_decode, any
+        # other value the fused step (which also writes the new token)
+        args = name.split("decode_kernel<", 1)[1].split(">", 1)[0].split(",")
+        return int(args[3]) == -1
+
     lines, total = [], 0.0
     for name in sorted(fetch):
         if "decode_kernel" not in name and "merge_kernel" not in name:
@@ -202,9 +208,12 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write
         fk = sum(fetch[name]) / len(fetch[name])
         wk = sum(write.get(name, [0.0])) / max(1, len(write.get(name, [])))
         b = (fk * f_scale + wk * w_scale) * 1024.0
-        total += b
+        counted = "merge_kernel" in name or is_plain_decode(name)
+        if counted:
+            total += b
         lines.append(f"  {name}\n    dispatches {len(fetch[name])}  FETCH_SIZE {fk:.1f} KiB  "
-                     f"WRITE_SIZE {wk:.1f} KiB  -> {b / 1e6:.3f} MB per dispatch (scaled)")
+                     f"WRITE_SIZE {wk:.1f} KiB  -> {b / 1e6:.3f} MB per dispatch (scaled)"
+                     + ("" if counted else "  [fused step: not part of the decode call]"))
     out = [f"# HBM traffic per paged_attention_decode call, workload {workload}",
            "# commands (run from the repository root on the GPU host):"]
     out += [f"#   {c}" for c in commands]
@@ -213,6 +222,46 @@ def summarize_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write
             f"write x{w_scale:.4f}", "kernels:"] + lines
     out.append(f"traffic_bytes_per_launch {int(round(total))} source={decode_source_hash()}")
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+    return 0
+
+
+def summarize_trace(workload, trace_csv, stats_csv, commands):
+    """Write profiles/decode_<workload>_kernel_trace.txt from the rocprofv3
+    --kernel-trace --stats CSVs of a bench run: the kernel statistics and the
+    library's kernels per launch shape (rows with at least 5 launches)."""
+    import csv
+    import collections
+    import re
+
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        if "pkv::" not in name:
+            continue
+        short = re.sub(r"^void ", "", name).replace("pkv::(anonymous namespace)::", "")
+        short = short.split("(pkv::")[0]
+        agg[(short, r["Grid_Size_X"], r["Grid_Size_Y"])].append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = [f"# rocprofv3 kernel trace summary, workload {workload} (one fused decode step per "
+           f"launch of decode_kernel with step on; merge_kernel when split)",
+           "# commands (run from the repository root on the GPU host):"]
+    out += [f"#   {c}" for c in commands]
+    out.append(f"# source={decode_source_hash()}  (hash of the decode sources)")
+    out.append("# run_kernel_stats.csv (durations in ns; the bench setup's bulk cache writes and "
+               "host copies are included):")
+    out += [line.rstrip("\n") for line in open(stats_csv)]
+    out.append("# per (kernel, grid) from run_kernel_trace.csv, rows with >= 5 launches (grid in "
+               "threads):")
+    out.append(f"{'kernel':44s} {'grid_x':>9s} {'grid_y':>6s} {'calls':>6s} {'avg_us':>9s} "
+               f"{'min_us':>9s} {'max_us':>9s}")
+    for k, v in sorted(agg.items(), key=lambda kv: -len(kv[1])):
+        if len(v) >= 5:
+            out.append(f"{k[0]:44s} {k[1]:>9s} {k[2]:>6s} {len(v):6d} {sum(v) / len(v) / 1e3:9.2f} "
+                       f"{min(v) / 1e3:9.2f} {max(v) / 1e3:9.2f}")
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_kernel_trace.txt")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     open(path, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -244,11 +293,16 @@ def main():
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<workload>.txt from rocprofv3 counter CSVs "
                          "(no GPU needed)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
+                    help="write profiles/decode_<workload>_kernel_trace.txt from rocprofv3 "
+                         "kernel-trace CSVs (no GPU needed)")
     ap.add_argument("--command", action="append", default=[],
-                    help="with --summarize-traffic: command line that produced a CSV")
+                    help="with --summarize-*: command line that produced a CSV")
     args = ap.parse_args()
     if args.summarize_traffic:
         return summarize_traffic(args.workload, *args.summarize_traffic, args.command)
+    if args.summarize_trace:
+        return summarize_trace(args.workload, *args.summarize_trace, args.command)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
               f"multi-GPU path.", file=sys.stderr)
