@@ -69,6 +69,17 @@ def kv_bytes(lens, w) -> int:
     return b
 
 
+def kv_bytes_shared(sh, w) -> int:
+    """Algorithmic bytes of one shared-prefix decode call: each group's prefix
+    once, every suffix, q and out of every sequence, both tables."""
+    pieces = np.concatenate([np.asarray(sh["suffix_lens"], np.int64),
+                             np.asarray(sh["group_prefix_lens"], np.int64)])
+    b = kv_read_bytes(pieces, w)
+    b += len(sh["suffix_lens"]) * w.num_heads * w.head_dim * (EB[w.q_dtype] + EB[w.out_dtype])
+    b += 4 * int(np.sum((pieces + w.block_size - 1) // w.block_size)) + 4 * len(pieces)
+    return b
+
+
 def kv_read_bytes(lens, w) -> int:
     tok = int(np.asarray(lens, np.int64).sum())
     b = tok * w.num_kv_heads * 2 * w.head_dim * EB[w.cache_dtype]
@@ -280,6 +291,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="tokens per physical block (the pool keeps its token capacity)")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--shared", action="store_true",
+                    help="decode through paged_attention_decode_shared: sequences that "
+                         "share prefix blocks read them once per group")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as copy + write + decode launches instead of the fused "
                          "paged_decode_step")
@@ -375,22 +389,44 @@ def main():
         t0 = time.perf_counter()
         slots, pairs, src = alloc.append_slots(b["seqs"], with_src=True)
         tables, lens = alloc.export_tables(b["seqs"], maxb)
+        sh = alloc.export_shared(b["seqs"], maxb, maxb) if args.shared else None
         t_host += time.perf_counter() - t0
         steps.append(dict(b=i % R, slots=torch.from_numpy(slots).cuda(),
                           cow_src=torch.from_numpy(src.astype(np.int32)).cuda(),
                           pairs=torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
                           if len(pairs) else None, npairs=len(pairs),
                           tables=torch.from_numpy(tables).cuda(),
-                          lens=torch.from_numpy(lens).cuda(), lens_host=lens))
+                          lens=torch.from_numpy(lens).cuda(), lens_host=lens, sh=sh))
     host_alloc_us = t_host / total_steps * 1e6
     S, H, D, Hkv = w0.num_seqs, w0.num_heads, w0.head_dim, w0.num_kv_heads
     workspace = pkv.alloc_workspace(S, H, Hkv, D, maxb, part, block_size=bs)
+    if args.shared:
+        # suffix tables cut to the widest suffix of any step; device group arrays
+        msb = max(1, max(-(-int(st["sh"]["suffix_lens"].max()) // bs) for st in steps))
+        ws_need = 0
+        for st in steps:
+            sh = st["sh"]
+            st["grp"] = pkv.PrefixGroups(sh)
+            st["stables"] = torch.from_numpy(
+                np.ascontiguousarray(sh["suffix_tables"][:, :msb])).cuda()
+            st["slens"] = torch.from_numpy(sh["suffix_lens"]).cuda()
+            ws_need = max(ws_need, pkv.shared_workspace_bytes(S, H, Hkv, D, msb, st["grp"],
+                                                              part, bs))
+        workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device="cuda")
+        print(f"# shared: {steps[0]['sh']['num_groups']} group(s), prefix "
+              f"{steps[0]['sh']['group_prefix_lens'].tolist()}, suffix width {msb} blocks",
+              file=sys.stderr, flush=True)
     scale = float(np.float32(w0.scale))
     torch.cuda.synchronize()
 
     def run_step(st):
         b = batches[st["b"]]
-        if args.unfused:
+        if args.shared:
+            pkv.paged_attention_decode_shared(b["q"], cache, st["stables"], st["slens"], scale,
+                                              st["grp"], key=b["k"], value=b["v"],
+                                              cow_src=st["cow_src"], out=b["out"],
+                                              partition_size=part, workspace=workspace)
+        elif args.unfused:
             if st["pairs"] is not None:
                 pkv.paged_copy_blocks(cache, st["pairs"])
             pkv.paged_kv_write(b["k"], b["v"], st["slots"], cache)
@@ -439,6 +475,11 @@ def main():
 
     def run_decode(st):
         b = batches[st["b"]]
+        if args.shared:
+            pkv.paged_attention_decode_shared(b["q"], cache, st["stables"], st["slens"], scale,
+                                              st["grp"], out=b["out"], partition_size=part,
+                                              workspace=workspace)
+            return
         pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale, out=b["out"],
                                    partition_size=part, workspace=workspace)
 
@@ -453,7 +494,10 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     dec_ms = ev0.elapsed_time(ev1) / len(dec_steps)
-    dec_alg = np.mean([kv_bytes(st["lens_host"], w0) for st in dec_steps])
+    if args.shared:
+        dec_alg = np.mean([kv_bytes_shared(st["sh"], w0) for st in dec_steps])
+    else:
+        dec_alg = np.mean([kv_bytes(st["lens_host"], w0) for st in dec_steps])
     achieved = dec_alg / (dec_ms * 1e-3) / 1e9
 
     traffic = read_traffic(args.workload)
@@ -468,7 +512,7 @@ def main():
                    "mean_seq_len": round(mean_len, 1), "pool_blocks": num_blocks,
                    "rotating_batches": R, "partition_size": part,
                    "split_k": not single_pass, "graph": not args.no_graph,
-                   "fused_step": not args.unfused},
+                   "fused_step": not args.unfused, "shared_prefix": bool(args.shared)},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(S / (step_ms * 1e-3), 1),
         "tokens_per_s": round(S / (step_ms * 1e-3), 1),

@@ -100,7 +100,8 @@ typedef struct pkv_alloc pkv_alloc;
 
 /* Create an allocator over blocks 0 .. num_blocks-1.  free_order (host,
  * nullable) is a permutation of 0 .. num_blocks-1 giving the initial free-list
- * order (NULL: ascending).  block_size must be 16.  *out receives the handle. */
+ * order (NULL: ascending).  block_size is 8, 16 or 32 tokens.  *out receives
+ * the handle. */
 int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order,
                      pkv_alloc **out);
 void pkv_alloc_destroy(pkv_alloc *a);
@@ -113,7 +114,7 @@ int32_t pkv_alloc_free_list(const pkv_alloc *a, int32_t *out, int32_t cap);
 int32_t pkv_block_refcount(const pkv_alloc *a, int32_t block);
 
 /* Grow sequence seq_id (created if new) to num_tokens filled tokens, taking
- * ceil(num_tokens/16) - (blocks held) new blocks ("allocate(seq_id, num_tokens)"
+ * ceil(num_tokens/block_size) - (blocks held) new blocks ("allocate(seq_id, num_tokens)"
  * of [jsqmd, section 3.2]).  If the sequence's partly filled tail block is shared
  * and the call adds tokens to it, that block is first replaced by a private
  * copy: *cow_src / *cow_dst (host, nullable) receive the pair to copy with
@@ -123,7 +124,7 @@ int32_t pkv_block_refcount(const pkv_alloc *a, int32_t block);
 int pkv_seq_allocate(pkv_alloc *a, int64_t seq_id, int32_t num_tokens, int32_t *cow_src,
                      int32_t *cow_dst);
 /* Reserve the slot of the next token of an existing sequence (a new block
- * every 16th token [fairy, s06 decode-phase allocation]); *slot (host)
+ * every block_size-th token [fairy, s06 decode-phase allocation]); *slot (host)
  * receives it.  Copy-on-write as for pkv_seq_allocate. */
 int pkv_seq_append_slot(pkv_alloc *a, int64_t seq_id, int64_t *slot, int32_t *cow_src,
                         int32_t *cow_dst);
@@ -154,6 +155,35 @@ int pkv_seq_slots(const pkv_alloc *a, int64_t seq_id, int32_t start, int32_t cou
 int pkv_export_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
                       int32_t max_blocks_per_seq, int32_t *out_block_tables,
                       int32_t *out_seq_lens);
+/* Tables of n sequences split into shared prefixes and private suffixes, the
+ * input of paged_attention_decode_shared.  Sequences forked from one parent
+ * share the physical blocks of their common beginning [fairy, s05
+ * copy-on-write, s08 prefix sharing]; a group is every sequence (two or more
+ * of seq_ids) whose first table entry is the same physical block, numbered in
+ * order of its first member.  The group's prefix is the longest run of leading
+ * entries common to all members, cut to blocks every member has filled, to
+ * max_prefix_blocks and to a multiple of 16 tokens; a group whose prefix is
+ * shorter than max(16, min_prefix_tokens) tokens is not formed.  One level of
+ * sharing: sequences that share more than their group's common run still
+ * read the rest as suffix.  Host outputs:
+ *   suffix_tables [n][max_suffix_blocks] (padded with -1): each table without
+ *       its group's prefix entries; suffix_lens [n]: length minus prefix.
+ *   seq_group [n]: group of each sequence, -1 for none.
+ *   group_offsets [n/2 + 1 or more], group_members [n]: the members of group g
+ *       (indices into seq_ids, ascending) are group_members[group_offsets[g]
+ *       .. group_offsets[g+1]).
+ *   group_tables [n/2 or more][max_prefix_blocks] (padded with -1) and
+ *       group_prefix_lens [n/2 or more] (tokens): each group's prefix.
+ *   *num_groups, *max_group_size (0 without groups).
+ * PKV_ENOENT for an unknown id, PKV_EINVAL if a suffix is longer than
+ * max_suffix_blocks (nothing is written then). */
+int pkv_export_shared_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
+                             int32_t min_prefix_tokens, int32_t max_prefix_blocks,
+                             int32_t max_suffix_blocks, int32_t *suffix_tables,
+                             int32_t *suffix_lens, int32_t *seq_group, int32_t *group_offsets,
+                             int32_t *group_members, int32_t *group_tables,
+                             int32_t *group_prefix_lens, int32_t *num_groups,
+                             int32_t *max_group_size);
 
 /* ========================================================================
  * Device operations (gfx950 HIP kernels)
@@ -228,13 +258,13 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *            cache_dtype is F32, else F16; 16-byte aligned.
  *   k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks: the pools.
  *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; entry i is the
- *            physical block of tokens 16i .. 16i+15.  Entries past
- *            ceil(seq_len/16) are never read.
+ *            physical block of tokens i*block_size .. (i+1)*block_size - 1.
+ *            Entries past ceil(seq_len/block_size) are never read.
  *   seq_lens: device int32 [num_seqs], tokens already in the cache including
  *            the one just written; 0 gives a zero output row.
- *   head_dim 64 or 128; block_size 16; num_heads/num_kv_heads <= 16.
- *   partition_size: tokens per work unit along the sequence (multiple of
- *            block_size; 0 = library choice).  Longer sequences are split;
+ *   head_dim 64 or 128; block_size 8, 16 or 32; num_heads/num_kv_heads <= 16.
+ *   partition_size: tokens per work unit along the sequence (a multiple of
+ *            16 and of block_size; 0 = library choice).  Longer sequences are split;
  *            the partial results (max, sum, weighted V) are merged by a
  *            log-sum-exp reduction ("partial accumulate, then merge",
  *            paged_attention_v2 of [jsqmd, section 4.1]).
@@ -256,10 +286,11 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
 /* Fused decode step: for every sequence s with L = seq_lens[s] > 0,
  *   1. if cow_src (nullable, device int32 [num_seqs]) has cow_src[s] >= 0,
  *      copy block cow_src[s] into the sequence's tail block
- *      block_tables[s][(L-1)/16] (copy-on-write [fairy, s05]);
+ *      block_tables[s][(L-1)/block_size] (copy-on-write [fairy, s05]);
  *   2. write the sequence's new token -- row s of key / value, device
  *      [num_seqs][num_kv_heads][head_dim] of src_dtype -- at position L - 1,
- *      i.e. slot block_tables[s][(L-1)/16] * 16 + (L-1) % 16, quantizing as
+ *      i.e. slot block_tables[s][(L-1)/bs] * bs + (L-1) % bs (bs =
+ *      block_size), quantizing as
  *      paged_kv_write does ("append the new token's K/V" [fairy, s02]);
  *   3. compute out exactly as paged_attention_decode does, over all L tokens
  *      including the new one.
@@ -280,6 +311,66 @@ int paged_decode_step(void *out, int32_t out_dtype, const void *query, int32_t q
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* Groups of sequences that share the physical blocks of a prefix (as
+ * pkv_export_shared_tables produces them).  A host struct; the arrays are
+ * device int32 memory. */
+typedef struct pkv_prefix_groups {
+  int32_t num_groups;          /* 0: no sharing (plain decode) */
+  int32_t num_members;         /* entries of members */
+  int32_t max_group_size;      /* >= the member count of every group */
+  int32_t max_prefix_blocks;   /* row stride of tables */
+  const int32_t *offsets;      /* [num_groups + 1]: group g is members[offsets[g] .. offsets[g+1]) */
+  const int32_t *members;      /* [num_members]: sequence indices (rows of query / tables) */
+  const int32_t *tables;       /* [num_groups][max_prefix_blocks]: the prefix's physical blocks */
+  const int32_t *prefix_lens;  /* [num_groups]: prefix tokens, a multiple of 16 and of block_size */
+  const int32_t *seq_group;    /* [num_seqs]: group of each sequence, -1 for none */
+} pkv_prefix_groups;
+
+/* Workspace bytes of paged_attention_decode_shared (max_blocks_per_seq: the
+ * suffix tables' width).  0 for invalid arguments. */
+size_t paged_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              int32_t partition_size,
+                                              const pkv_prefix_groups *groups);
+
+/* Shared-prefix decode: the output of paged_attention_decode (or, with key /
+ * value, of paged_decode_step) for sequences whose tables are split into a
+ * shared prefix and a private suffix, reading each prefix block once per
+ * (group, kv head) instead of once per sequence.  Sequence s attends over its
+ * group's prefix (groups->tables[g], groups->prefix_lens[g] tokens, g =
+ * groups->seq_group[s]) followed by its suffix (block_tables[s],
+ * seq_lens[s] tokens): the token order of its full table.  Sharing of blocks
+ * between requests with reference counts is the page's [7yue, section 2;
+ * fairy, s05, s08]; that each sharer's softmax over prefix + suffix is the
+ * log-sum-exp merge of the softmaxes over the two pieces is the same identity
+ * as the split-K merge of paged_attention_v2 [jsqmd, section 4.1].
+ *   key, value, src_dtype, cow_src: as paged_decode_step, applied to the
+ *       suffix (the new token is position seq_lens[s] - 1 of the suffix);
+ *       both NULL for decode only.
+ *   block_tables, max_blocks_per_seq, seq_lens: the suffixes.
+ *   groups: host struct (see above); num_groups = 0 runs the plain path.
+ *       Contract: each member's full table is the group's prefix followed by
+ *       its suffix table, and every sequence is a member of its seq_group.
+ *       The prefix kernels read the blocks of groups->tables only.
+ *   workspace: >= paged_attention_shared_workspace_bytes(...) bytes, 256-byte
+ *       aligned.
+ * Other arguments, arithmetic and errors as paged_attention_decode.  Three
+ * launches: the (suffix) decode or step kernel, the prefix kernel (all of a
+ * group's query heads of one kv head against each prefix tile, on MFMA), and
+ * the merge. */
+int paged_attention_decode_shared(void *out, int32_t out_dtype, const void *query,
+                                  int32_t q_dtype, const void *key, const void *value,
+                                  int32_t src_dtype, const int32_t *cow_src, void *k_cache,
+                                  void *v_cache, void *k_scale, void *v_scale,
+                                  int32_t cache_dtype, int32_t num_blocks,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  float scale, const pkv_prefix_groups *groups,
+                                  int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* ========================================================================
  * Bandwidth diagnostics (measurement helpers, not part of the method)

@@ -123,6 +123,66 @@ class BlockManagerModel:
             lens.append(self.lens[s])
         return "ok", rows, lens
 
+    def export_shared(self, seqs, min_prefix_tokens: int, max_prefix_blocks: int,
+                      max_suffix_blocks: int):
+        """Tables split into shared prefixes and private suffixes.
+
+        Sequences forked from one parent share the physical blocks of their
+        common beginning (s05 copy-on-write and s08 of "KVcache-learning").  A
+        group is every sequence (two or more) whose first table entry is the
+        same physical block, taken in the order of its first member; its prefix
+        is the longest run of leading entries all members have in common,
+        limited to blocks every member has filled, to max_prefix_blocks and to
+        whole 16-token tiles.  Groups whose prefix is shorter than
+        max(16, min_prefix_tokens) tokens are not formed.  Returns status and a
+        dict of the host arrays the C call fills.
+        """
+        for s in seqs:
+            if s not in self.tables:
+                return "enoent", None
+        bs = self.block_size
+        firsts = {}
+        for i, s in enumerate(seqs):
+            if self.tables[s]:
+                firsts.setdefault(self.tables[s][0], []).append(i)
+        groups = []
+        for members in sorted(firsts.values(), key=lambda mem: mem[0]):
+            if len(members) < 2:
+                continue
+            tabs = [self.tables[seqs[i]] for i in members]
+            limit = min([max_prefix_blocks] + [self.lens[seqs[i]] // bs for i in members])
+            k = 0
+            while k < limit and all(t[k] == tabs[0][k] for t in tabs):
+                k += 1
+            while (k * bs) % 16:
+                k -= 1
+            if k * bs >= max(16, min_prefix_tokens):
+                groups.append((members, k))
+        n = len(seqs)
+        seq_group, pre = [-1] * n, [0] * n
+        for gi, (members, k) in enumerate(groups):
+            for i in members:
+                seq_group[i], pre[i] = gi, k
+        suffix_tables, suffix_lens = [], []
+        for i, s in enumerate(seqs):
+            rest = self.tables[s][pre[i]:]
+            if len(rest) > max_suffix_blocks:
+                return "einval", None
+            suffix_tables.append(rest + [-1] * (max_suffix_blocks - len(rest)))
+            suffix_lens.append(self.lens[s] - pre[i] * bs)
+        offsets, members_flat, group_tables, prefix_lens = [0], [], [], []
+        for members, k in groups:
+            members_flat += members
+            offsets.append(len(members_flat))
+            head = self.tables[seqs[members[0]]][:k]
+            group_tables.append(head + [-1] * (max_prefix_blocks - k))
+            prefix_lens.append(k * bs)
+        return "ok", dict(suffix_tables=suffix_tables, suffix_lens=suffix_lens,
+                          seq_group=seq_group, group_offsets=offsets,
+                          group_members=members_flat, group_tables=group_tables,
+                          group_prefix_lens=prefix_lens, num_groups=len(groups),
+                          max_group_size=max([len(m) for m, _ in groups], default=0))
+
     # invariants ---------------------------------------------------------------
     def check_invariants(self):
         counts = [0] * self.num_blocks

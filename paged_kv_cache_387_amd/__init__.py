@@ -29,10 +29,21 @@ EXPORTS = [
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_num_free", "pkv_alloc_free_list",
     "pkv_block_refcount", "pkv_seq_allocate", "pkv_seq_append_slot", "pkv_seq_append_slots",
     "pkv_seq_fork", "pkv_seq_free", "pkv_seq_len", "pkv_seq_slots", "pkv_export_tables",
+    "pkv_export_shared_tables",
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_decode_step",
+    "paged_attention_shared_workspace_bytes", "paged_attention_decode_shared",
     "pkv_stream_read", "pkv_stream_copy",
 ]
+
+
+class PrefixGroupsC(ctypes.Structure):
+    """struct pkv_prefix_groups of pkv.h (host struct of device pointers)."""
+    _fields_ = [("num_groups", ctypes.c_int32), ("num_members", ctypes.c_int32),
+                ("max_group_size", ctypes.c_int32), ("max_prefix_blocks", ctypes.c_int32),
+                ("offsets", ctypes.c_void_p), ("members", ctypes.c_void_p),
+                ("tables", ctypes.c_void_p), ("prefix_lens", ctypes.c_void_p),
+                ("seq_group", ctypes.c_void_p)]
 
 
 class PkvError(RuntimeError):
@@ -69,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "pkv_seq_len": ([P, i64, P], ctypes.c_int),
             "pkv_seq_slots": ([P, i64, i32, i32, P], ctypes.c_int),
             "pkv_export_tables": ([P, P, i32, i32, P, P], ctypes.c_int),
+            "pkv_export_shared_tables": ([P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P],
+                                         ctypes.c_int),
             "paged_kv_write": ([P, P, i32, i64, i64, P, i32, P, P, P, P, i32, i32, i32, i32,
                                 i32, P], ctypes.c_int),
             "paged_copy_blocks": ([P, P, P, P, i32, i32, P, i32, i32, i32, i32, P],
@@ -80,6 +93,11 @@ def lib() -> ctypes.CDLL:
             "paged_decode_step": ([P, i32, P, i32, P, P, i32, P, P, P, P, P, i32, i32, P, i32,
                                    P, i32, i32, i32, i32, i32, f32, i32, P, sz, P],
                                   ctypes.c_int),
+            "paged_attention_shared_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32, P],
+                                                       sz),
+            "paged_attention_decode_shared": ([P, i32, P, i32, P, P, i32, P, P, P, P, P, i32,
+                                               i32, P, i32, P, i32, i32, i32, i32, i32, f32, P,
+                                               i32, P, sz, P], ctypes.c_int),
             "pkv_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
             "pkv_stream_copy": ([P, P, sz, i32, P], ctypes.c_int),
         }
@@ -197,6 +215,33 @@ class BlockAllocator:
         _check(lib().pkv_export_tables(self._h, _np_ptr(ids), n, max_blocks, _np_ptr(tables),
                                        _np_ptr(lens)), "pkv_export_tables")
         return tables[:n], lens[:n]
+
+    def export_shared(self, seqs, max_prefix_blocks: int, max_suffix_blocks: int,
+                      min_prefix_tokens: int = 0) -> dict:
+        """Tables split into shared prefixes and private suffixes (host numpy
+        arrays, trimmed to their used lengths): suffix_tables, suffix_lens,
+        seq_group, group_offsets, group_members, group_tables,
+        group_prefix_lens, num_groups, max_group_size, max_prefix_blocks."""
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = len(ids)
+        m = max(n, 1)
+        st = np.empty((m, max_suffix_blocks), np.int32)
+        sl = np.empty(m, np.int32)
+        sg = np.empty(m, np.int32)
+        go = np.empty(m + 1, np.int32)
+        gm = np.empty(m, np.int32)
+        gt = np.empty((m, max_prefix_blocks), np.int32)
+        gp = np.empty(m, np.int32)
+        ng, mg = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pkv_export_shared_tables(
+            self._h, _np_ptr(ids), n, min_prefix_tokens, max_prefix_blocks, max_suffix_blocks,
+            _np_ptr(st), _np_ptr(sl), _np_ptr(sg), _np_ptr(go), _np_ptr(gm), _np_ptr(gt),
+            _np_ptr(gp), ctypes.byref(ng), ctypes.byref(mg)), "pkv_export_shared_tables")
+        g = ng.value
+        return dict(suffix_tables=st[:n], suffix_lens=sl[:n], seq_group=sg[:n],
+                    group_offsets=go[:g + 1], group_members=gm[:go[g]],
+                    group_tables=gt[:g], group_prefix_lens=gp[:g], num_groups=g,
+                    max_group_size=mg.value, max_prefix_blocks=max_prefix_blocks)
 
 
 # ---------------------------------------------------------------------------
@@ -428,6 +473,104 @@ def paged_decode_step(query, key, value, cache: PagedKVCache, block_tables, seq_
         _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
         cache.block_size, float(scale), partition_size, ws_ptr, ws_len, _stream_ptr(stream)),
         "paged_decode_step")
+    return out
+
+
+class PrefixGroups:
+    """Device copy of the group arrays of BlockAllocator.export_shared and the
+    pkv_prefix_groups struct that points at them."""
+
+    def __init__(self, shared: dict, device="cuda"):
+        torch = _torch()
+
+        def up(a):
+            a = np.ascontiguousarray(a, dtype=np.int32).reshape(-1)
+            return torch.from_numpy(a if a.size else np.zeros(1, np.int32)).to(device)
+
+        self.num_groups = int(shared["num_groups"])
+        self.max_group_size = max(int(shared["max_group_size"]), 1)
+        self.max_prefix_blocks = int(shared["max_prefix_blocks"])
+        self.num_members = int(len(shared["group_members"]))
+        self.offsets = up(shared["group_offsets"])
+        self.members = up(shared["group_members"])
+        self.tables = up(shared["group_tables"])
+        self.prefix_lens = up(shared["group_prefix_lens"])
+        self.seq_group = up(shared["seq_group"])
+        self.num_seqs = int(len(shared["seq_group"]))
+        if self.num_groups > 0:
+            need = self.num_groups * self.max_prefix_blocks
+            if self.tables.numel() < need or self.offsets.numel() < self.num_groups + 1:
+                raise ValueError("group arrays are shorter than num_groups needs")
+        self.c = PrefixGroupsC(self.num_groups, self.num_members, self.max_group_size,
+                               self.max_prefix_blocks, self.offsets.data_ptr(),
+                               self.members.data_ptr(), self.tables.data_ptr(),
+                               self.prefix_lens.data_ptr(), self.seq_group.data_ptr())
+
+
+def shared_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, groups: PrefixGroups,
+                           partition_size: int = 0, block_size: int = BLOCK_SIZE) -> int:
+    return lib().paged_attention_shared_workspace_bytes(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+        partition_size, ctypes.byref(groups.c))
+
+
+def paged_attention_decode_shared(query, cache: PagedKVCache, block_tables, seq_lens,
+                                  scale: float, groups: PrefixGroups, key=None, value=None,
+                                  cow_src=None, out=None, out_dtype=None,
+                                  partition_size: int = 0, workspace=None, stream=None):
+    """Decode (or, with key / value, the fused decode step) of sequences whose
+    tables are split into a shared prefix (groups) and a private suffix
+    (block_tables / seq_lens): each prefix block is read once per (group, kv
+    head) for all the group's queries."""
+    torch = _torch()
+    S, H, D = query.shape
+    q_dt = {torch.float32: F32, torch.float16: F16}.get(query.dtype)
+    if q_dt is None:
+        raise ValueError("query must be float32 or float16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if groups.num_groups > 0 and groups.num_seqs != S:
+        raise ValueError("groups describe a different number of sequences")
+    maxb = block_tables.shape[1]
+    if out is None:
+        odt = out_dtype if out_dtype is not None else query.dtype
+        out = torch.empty((S, H, D), dtype=odt, device=query.device)
+    o_dt = {torch.float32: F32, torch.float16: F16}.get(out.dtype)
+    if o_dt is None or tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be float32/float16 [num_seqs, num_heads, head_dim]")
+    if D != cache.head_dim or H % cache.num_kv_heads:
+        raise ValueError("query shape does not match the cache")
+    kp = vp = cp = None
+    src = F16
+    if key is not None or value is not None:
+        src = {torch.float32: F32, torch.float16: F16}.get(key.dtype)
+        if src is None or value is None or value.dtype != key.dtype:
+            raise ValueError("key/value must both be float32 or float16")
+        if tuple(key.shape) != (S, cache.num_kv_heads, D) or value.shape != key.shape:
+            raise ValueError(f"key/value must be [{S}, {cache.num_kv_heads}, {D}]")
+        row = S * cache.num_kv_heads * D
+        kp, vp = _dev(key, "key", numel=row), _dev(value, "value", numel=row)
+        cp = None if cow_src is None else _dev(cow_src, "cow_src", torch.int32, S)
+    need = shared_workspace_bytes(S, H, cache.num_kv_heads, D, maxb, groups, partition_size,
+                                  cache.block_size)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr, ws_len = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", numel=need)
+        ws_len = workspace.numel() * workspace.element_size()
+    nbytes = cache_bytes(cache.num_blocks, cache.num_kv_heads, D, cache.cache_dtype,
+                         cache.block_size)
+    ks, vs = cache._scales()
+    _check(lib().paged_attention_decode_shared(
+        _dev(out, "out"), o_dt, _dev(query, "query"), q_dt, kp, vp, src, cp,
+        _dev(cache.k, "k_cache", numel=nbytes), _dev(cache.v, "v_cache", numel=nbytes), ks, vs,
+        cache.cache_dtype, cache.num_blocks,
+        _dev(block_tables, "block_tables", torch.int32, S * maxb), maxb,
+        _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
+        cache.block_size, float(scale), ctypes.byref(groups.c), partition_size, ws_ptr, ws_len,
+        _stream_ptr(stream)), "paged_attention_decode_shared")
     return out
 
 

@@ -281,4 +281,97 @@ int pkv_export_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
   return PKV_OK;
 }
 
+int pkv_export_shared_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
+                             int32_t min_prefix_tokens, int32_t max_prefix_blocks,
+                             int32_t max_suffix_blocks, int32_t *suffix_tables,
+                             int32_t *suffix_lens, int32_t *seq_group, int32_t *group_offsets,
+                             int32_t *group_members, int32_t *group_tables,
+                             int32_t *group_prefix_lens, int32_t *num_groups,
+                             int32_t *max_group_size) {
+  if (!a || n < 0 || min_prefix_tokens < 0 || max_prefix_blocks <= 0 || max_suffix_blocks <= 0 ||
+      !num_groups || !max_group_size || !group_offsets)
+    return PKV_EINVAL;
+  if (n > 0 && (!seq_ids || !suffix_tables || !suffix_lens || !seq_group || !group_members ||
+                !group_tables || !group_prefix_lens))
+    return PKV_EINVAL;
+  std::vector<const pkv_seq *> sq(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_ENOENT;
+    sq[i] = &it->second;
+  }
+  const int32_t bs = a->block_size;
+  // a prefix is whole 16-token tiles: an even number of 8-token blocks
+  const int32_t step = bs < 16 ? 16 / bs : 1;
+  const int64_t min_tokens = min_prefix_tokens > 16 ? min_prefix_tokens : 16;
+
+  // candidate groups: sequences whose first block is the same physical block,
+  // numbered in order of their first member
+  std::unordered_map<int32_t, int32_t> by_first;
+  std::vector<std::vector<int32_t>> cand;
+  for (int32_t i = 0; i < n; ++i) {
+    if (sq[i]->blocks.empty()) continue;
+    auto ins = by_first.emplace(sq[i]->blocks[0], (int32_t)cand.size());
+    if (ins.second) cand.emplace_back();
+    cand[ins.first->second].push_back(i);
+  }
+  std::vector<int32_t> grp_of(n, -1), pre_blocks(n, 0);
+  std::vector<int32_t> kept, kept_blocks;
+  for (size_t c = 0; c < cand.size(); ++c) {
+    const std::vector<int32_t> &mem = cand[c];
+    if (mem.size() < 2) continue;
+    // longest common run of leading entries, limited to blocks every member
+    // has filled
+    int64_t k = max_prefix_blocks;
+    for (int32_t i : mem) {
+      const int64_t filled = sq[i]->len / bs;
+      if (filled < k) k = filled;
+    }
+    const std::vector<int32_t> &t0 = sq[mem[0]]->blocks;
+    int64_t common = 0;
+    while (common < k) {
+      bool same = true;
+      for (int32_t i : mem)
+        if (sq[i]->blocks[common] != t0[common]) { same = false; break; }
+      if (!same) break;
+      ++common;
+    }
+    common -= common % step;
+    if (common * bs < min_tokens) continue;
+    for (int32_t i : mem) {
+      grp_of[i] = (int32_t)kept.size();
+      pre_blocks[i] = (int32_t)common;
+    }
+    kept.push_back((int32_t)c);
+    kept_blocks.push_back((int32_t)common);
+  }
+  for (int32_t i = 0; i < n; ++i)
+    if ((int64_t)sq[i]->blocks.size() - pre_blocks[i] > max_suffix_blocks) return PKV_EINVAL;
+
+  // outputs
+  for (int32_t i = 0; i < n; ++i) {
+    const std::vector<int32_t> &t = sq[i]->blocks;
+    int32_t *row = suffix_tables + (size_t)i * max_suffix_blocks;
+    const int32_t ns = (int32_t)t.size() - pre_blocks[i];
+    for (int32_t j = 0; j < max_suffix_blocks; ++j) row[j] = j < ns ? t[pre_blocks[i] + j] : -1;
+    suffix_lens[i] = sq[i]->len - pre_blocks[i] * bs;
+    seq_group[i] = grp_of[i];
+  }
+  int32_t pos = 0, biggest = 0;
+  for (size_t g = 0; g < kept.size(); ++g) {
+    const std::vector<int32_t> &mem = cand[kept[g]];
+    group_offsets[g] = pos;
+    for (int32_t i : mem) group_members[pos++] = i;
+    if ((int32_t)mem.size() > biggest) biggest = (int32_t)mem.size();
+    const std::vector<int32_t> &t0 = sq[mem[0]]->blocks;
+    int32_t *row = group_tables + g * (size_t)max_prefix_blocks;
+    for (int32_t j = 0; j < max_prefix_blocks; ++j) row[j] = j < kept_blocks[g] ? t0[j] : -1;
+    group_prefix_lens[g] = kept_blocks[g] * bs;
+  }
+  group_offsets[kept.size()] = pos;
+  *num_groups = (int32_t)kept.size();
+  *max_group_size = biggest;
+  return PKV_OK;
+}
+
 }  // extern "C"

@@ -81,15 +81,55 @@ struct WorkspaceLayout {
   size_t o_off, lse_off, total;
 };
 
+// A row of partials per (sequence, head): num_parts suffix (or whole-sequence)
+// partitions, then `extra` shared-prefix partitions.
 WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                 int32_t num_parts) {
+                                 int32_t num_parts, int32_t extra = 0) {
   WorkspaceLayout w{0, 0, 0};
-  if (num_parts <= 1) return w;
-  const size_t rows = (size_t)num_seqs * num_heads * num_parts;
+  if (num_parts <= 1 && extra == 0) return w;
+  const size_t rows = (size_t)num_seqs * num_heads * (num_parts + extra);
   w.o_off = 0;
   w.lse_off = round256(rows * head_dim * sizeof(float));
   w.total = w.lse_off + rows * sizeof(float);
   return w;
+}
+
+// Shared-prefix partitioning: enough (group, kv head, column block,
+// partition) workgroups to give every compute unit one (each holds 64 query
+// columns in 4 waves, one wave per SIMD), with partitions of at least 16
+// tiles and a multiple of the wave count.
+constexpr int64_t kPrefixTargetWgs = 256;
+constexpr int64_t kPrefixMinTiles = 16;
+constexpr int kPrefixNominalCols = 64;
+
+struct PrefixPlan {
+  int32_t pp_tiles = 0, num_pparts = 0;
+};
+
+bool valid_groups(const pkv_prefix_groups *gr, int32_t block_size) {
+  if (!gr || gr->num_groups < 0) return false;
+  if (gr->num_groups == 0) return true;
+  return gr->num_members >= 0 && gr->max_group_size >= 1 && gr->max_prefix_blocks >= 1 &&
+         (int64_t)gr->max_prefix_blocks * block_size <= (1 << 30);
+}
+
+PrefixPlan plan_prefix(const pkv_prefix_groups *gr, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t block_size) {
+  PrefixPlan pl;
+  if (!gr || gr->num_groups <= 0) return pl;
+  const int64_t tiles = (int64_t)gr->max_prefix_blocks * block_size / kTile;
+  if (tiles <= 0) return pl;
+  const int64_t cols = (int64_t)gr->max_group_size * (num_heads / num_kv_heads);
+  const int64_t per_part =
+      (int64_t)gr->num_groups * num_kv_heads * ((cols + kPrefixNominalCols - 1) / kPrefixNominalCols);
+  int64_t parts = (kPrefixTargetWgs + per_part - 1) / per_part;
+  const int64_t max_parts = (tiles + kPrefixMinTiles - 1) / kPrefixMinTiles;
+  parts = parts < 1 ? 1 : (parts > max_parts ? max_parts : parts);
+  int64_t pt = (tiles + parts - 1) / parts;
+  pt = (pt + kWaves - 1) / kWaves * kWaves;
+  pl.pp_tiles = (int32_t)pt;
+  pl.num_pparts = (int32_t)((tiles + pt - 1) / pt);
+  return pl;
 }
 
 }  // namespace
@@ -133,6 +173,21 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
   return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
 }
 
+size_t paged_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              int32_t partition_size,
+                                              const pkv_prefix_groups *groups) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_heads % num_kv_heads || max_blocks_per_seq <= 0 || !valid_block_size(block_size) ||
+      !valid_partition(partition_size, block_size) || !valid_groups(groups, block_size))
+    return 0;
+  const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
+  const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
+  const PrefixPlan pl = plan_prefix(groups, num_heads, num_kv_heads, block_size);
+  return workspace_layout(num_seqs, num_heads, head_dim, parts, pl.num_pparts).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -145,7 +200,8 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
                    int32_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
                    const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                   int32_t partition_size, void *workspace, size_t workspace_bytes) {
+                   int32_t partition_size, void *workspace, size_t workspace_bytes,
+                   int32_t extra_parts = 0) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || partition_size < 0)
     return PKV_EINVAL;
@@ -175,7 +231,7 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   if ((int64_t)num_seqs * num_heads > INT32_MAX || (int64_t)num_seqs * num_kv_heads > INT32_MAX ||
       decode_grid(num_seqs * num_kv_heads, parts) > INT32_MAX)
     return PKV_ENOTSUP;
-  const WorkspaceLayout wl = workspace_layout(num_seqs, num_heads, head_dim, parts);
+  const WorkspaceLayout wl = workspace_layout(num_seqs, num_heads, head_dim, parts, extra_parts);
   const size_t need = wl.total;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PKV_EINVAL;
@@ -203,6 +259,8 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   p.block_size = block_size;
   p.part_tiles = pt;
   p.num_parts = parts;
+  p.ws_stride = parts + extra_parts;
+  p.ws_pre = parts;
   p.num_units = num_seqs * num_kv_heads;
   p.qk_scale = scale * 1.4426950408889634f;
   *pp = p;
@@ -263,6 +321,108 @@ int paged_decode_step(void *out, int32_t out_dtype, const void *query, int32_t q
   p.v_scale_w = static_cast<uint16_t *>(v_scale);
   return status_of(launch_decode_step(p, cache_dtype, src_dtype, out_dtype, head_dim,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int paged_attention_decode_shared(void *out, int32_t out_dtype, const void *query,
+                                  int32_t q_dtype, const void *key, const void *value,
+                                  int32_t src_dtype, const int32_t *cow_src, void *k_cache,
+                                  void *v_cache, void *k_scale, void *v_scale,
+                                  int32_t cache_dtype, int32_t num_blocks,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  float scale, const pkv_prefix_groups *groups,
+                                  int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  if (!groups || groups->num_groups < 0) return PKV_EINVAL;
+  if (!valid_block_size(block_size)) return PKV_ENOTSUP;
+  if (!valid_groups(groups, block_size)) return PKV_EINVAL;
+  const pkv_prefix_groups &gr = *groups;
+  if (gr.num_groups > 0 &&
+      (!gr.offsets || !gr.members || !gr.tables || !gr.prefix_lens || !gr.seq_group ||
+       !aligned(gr.offsets, 4) || !aligned(gr.members, 4) || !aligned(gr.tables, 4) ||
+       !aligned(gr.prefix_lens, 4) || !aligned(gr.seq_group, 4)))
+    return PKV_EINVAL;
+  if (num_heads > 0 && num_kv_heads > 0 && num_heads % num_kv_heads) return PKV_EINVAL;
+  const bool step = key != nullptr || value != nullptr;
+  PrefixPlan pl;
+  if (num_heads > 0 && num_kv_heads > 0)
+    pl = plan_prefix(groups, num_heads, num_kv_heads, block_size);
+  DecodeParams p{};
+  int st = prepare_decode(&p, out, out_dtype, query, q_dtype, k_cache, v_cache, k_scale, v_scale,
+                          cache_dtype, num_blocks, block_tables, max_blocks_per_seq, seq_lens,
+                          num_seqs, num_heads, num_kv_heads, head_dim, block_size, scale,
+                          partition_size, workspace, workspace_bytes, pl.num_pparts);
+  if (st != PKV_OK) return st;
+  if (step && src_dtype != (cache_dtype == PKV_F32 ? PKV_F32 : PKV_F16)) return PKV_ENOTSUP;
+  if (num_seqs == 0) return PKV_OK;
+  if (step) {
+    if (!key || !value) return PKV_EINVAL;
+    if (!aligned(key, elem_bytes(src_dtype)) || !aligned(value, elem_bytes(src_dtype)) ||
+        !aligned(cow_src, 4))
+      return PKV_EINVAL;
+  }
+  PrefixParams pp{};
+  if (gr.num_groups > 0 && pl.num_pparts > 0) {
+    const int64_t units = (int64_t)gr.num_groups * num_kv_heads;
+    const int chunks = prefix_chunks(cache_dtype);
+    const int64_t cols = (int64_t)gr.max_group_size * (num_heads / num_kv_heads);
+    const int64_t col_blocks = (cols + 16 * chunks - 1) / (16 * chunks);
+    if (units > INT32_MAX || col_blocks > INT32_MAX ||
+        (int64_t)unit_groups((int)units) * kXcds * col_blocks * pl.num_pparts > INT32_MAX)
+      return PKV_ENOTSUP;
+    p.seq_group = gr.seq_group;
+    p.group_prefix_lens = gr.prefix_lens;
+    p.num_groups = gr.num_groups;
+    p.max_prefix_blocks = gr.max_prefix_blocks;
+    p.pp_tiles = pl.pp_tiles;
+    pp.q = query;
+    pp.k_cache = p.k_cache;
+    pp.v_cache = p.v_cache;
+    pp.k_scale = p.k_scale;
+    pp.v_scale = p.v_scale;
+    pp.offsets = gr.offsets;
+    pp.members = gr.members;
+    pp.tables = gr.tables;
+    pp.prefix_lens = gr.prefix_lens;
+    pp.ws_o = p.ws_o;
+    pp.ws_lse = p.ws_lse;
+    pp.num_blocks = num_blocks;
+    pp.num_seqs = num_seqs;
+    pp.num_heads = num_heads;
+    pp.num_kv_heads = num_kv_heads;
+    pp.group = p.group;
+    pp.num_groups = gr.num_groups;
+    pp.num_members = gr.num_members;
+    pp.max_prefix_blocks = gr.max_prefix_blocks;
+    pp.num_units = (int)units;
+    pp.col_blocks = (int)col_blocks;
+    pp.pp_tiles = pl.pp_tiles;
+    pp.num_pparts = pl.num_pparts;
+    pp.ws_stride = p.ws_stride;
+    pp.ws_pre = p.ws_pre;
+    pp.qk_scale = p.qk_scale;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (step) {
+    p.key_new = key;
+    p.value_new = value;
+    p.cow_src = cow_src;
+    p.k_cache_w = static_cast<uint8_t *>(k_cache);
+    p.v_cache_w = static_cast<uint8_t *>(v_cache);
+    p.k_scale_w = static_cast<uint16_t *>(k_scale);
+    p.v_scale_w = static_cast<uint16_t *>(v_scale);
+    err = launch_decode_step(p, cache_dtype, src_dtype, out_dtype, head_dim, s);
+  } else {
+    err = launch_decode(p, cache_dtype, out_dtype, head_dim, s);
+  }
+  if (err != hipSuccess || p.seq_group == nullptr) return status_of(err);
+  // The prefix pass reads only prefix blocks, which the step neither copies
+  // into nor writes; the merge then combines suffix and prefix partials.
+  err = launch_prefix(pp, cache_dtype, head_dim, block_size, s);
+  if (err != hipSuccess) return status_of(err);
+  return status_of(launch_merge(p, out_dtype, head_dim, s));
 }
 
 int paged_kv_write(const void *key, const void *value, int32_t src_dtype, int64_t key_stride,

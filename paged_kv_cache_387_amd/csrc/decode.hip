@@ -39,98 +39,10 @@
 // conversion) and use the fp16 MFMAs, the K scale multiplies the scores and
 // the V scale is folded into P (P' = p * s_v * 64 in fp16; the factor 64 keeps
 // P' out of fp16's subnormal range and is divided out at the end).
-#include <cmath>
-
-#include "kv_write.h"
+#include "attn_common.h"
 
 namespace pkv {
 namespace {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-
-constexpr float kPvBoost = 64.0f;   // fold factor for quantized V scales
-
-template <int KV> struct Kv;
-template <> struct Kv<PKV_F32> { static constexpr int EB = 4; };
-template <> struct Kv<PKV_F16> { static constexpr int EB = 2; };
-template <> struct Kv<PKV_I8> { static constexpr int EB = 1; };
-template <> struct Kv<PKV_E4M3> { static constexpr int EB = 1; };
-
-__device__ __forceinline__ u4 load16(const uint8_t *p) {
-  return *reinterpret_cast<const u4 *>(p);
-}
-// K/V tiles are read once per step: non-temporal loads keep them from
-// displacing reusable lines (tables, q, shared blocks) and stream faster.
-__device__ __forceinline__ u4 load16_stream(const uint8_t *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u4 *>(p));
-}
-
-__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
-// Element bit-casts go through a by-value scalar: __builtin_bit_cast applied
-// directly to a subscripted ext_vector element (vec[j]) compiled to element 0
-// with this compiler.
-__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
-__device__ __forceinline__ uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
-
-// int8 codes to fp16, biased: a byte u = c + 128 (the code with its sign bit
-// flipped) under the exponent byte 0x64 is the fp16 value 1024 + u = c + 1152,
-// exact; one v_perm takes two such bytes and the 0x64 bytes from a constant
-// register.  The bias is taken out of the dot products instead of the codes:
-// q.(c + 1152) = q.c + 1152 * sum(q) per head, and sum_t P'_t (c_t + 1152) =
-// P'.c + 1152 * sum_t P'_t, with sum_t P'_t from one more MFMA on a ones
-// operand (it sums exactly the fp16 weights the P.V MFMA multiplies).
-constexpr uint32_t kExp64 = 0x64646464u;
-constexpr float kI8Bias = 1152.0f;
-__device__ __forceinline__ h2 i8_pair(uint32_t flipped, uint32_t sel) {
-  return as_h2(__builtin_amdgcn_perm(kExp64, flipped, sel));
-}
-// perm selectors: bytes 0,1 (resp. 2,3) of src1 under 0x64 from src0
-constexpr uint32_t kSelLo = 0x04010400u;
-constexpr uint32_t kSelHi = 0x04030402u;
-
-// E4M3 codes to exact fp16 with the gfx950 conversion (scale 1.0): two codes
-// (the low or high half of a word) per instruction.
-__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, bool hi) {
-  return as_u32(hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
-                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-}
-
-// 4 codes of one word (in order) -> h4, exact.
-template <int KV>
-__device__ __forceinline__ h4 codes4_to_h4(uint32_t w) {
-  if constexpr (KV == PKV_I8) {
-    const uint32_t f = w ^ 0x80808080u;
-    return __builtin_bit_cast(h4, u2{as_u32(i8_pair(f, kSelLo)), as_u32(i8_pair(f, kSelHi))});
-  } else {
-    return __builtin_bit_cast(h4, u2{e4m3_pair(w, false), e4m3_pair(w, true)});
-  }
-}
-
-// 16 codes (one K column) -> two h8 (codes 0-7, 8-15), exact.
-template <int KV>
-__device__ __forceinline__ void codes16_to_h8(u4 w, h8 &lo, h8 &hi) {
-  const h4 a = codes4_to_h4<KV>(w[0]), b = codes4_to_h4<KV>(w[1]);
-  const h4 c = codes4_to_h4<KV>(w[2]), d = codes4_to_h4<KV>(w[3]);
-  lo = h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  hi = h8{c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
-}
-
-template <int OUT>
-__device__ __forceinline__ void store_out(void *out, size_t idx, float v) {
-  if constexpr (OUT == PKV_F32)
-    reinterpret_cast<float *>(out)[idx] = v;
-  else
-    reinterpret_cast<_Float16 *>(out)[idx] = (_Float16)v;
-}
-
-__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
 // Tiles of K/V (and scales) one wavefront keeps in flight: the ring of
 // prefetched blocks is NB deep.  Registers per tile: 2 * NL * 4 (+4 scales).
 #ifndef PKV_PREFETCH_F32
@@ -260,8 +172,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   const int nblk = (L + BS - 1) / BS;                 // blocks in use
   const int ntile = (L + kTile - 1) / kTile;          // tiles in use
   const int nparts_s = (ntile + p.part_tiles - 1) / p.part_tiles;
+  const int npre = prefix_parts_of(p, s);   // shared-prefix partials (merged later)
   if (first >= ntile) {
-    if (part == 0) {  // empty sequence: zero output rows
+    if (part == 0 && npre == 0) {  // empty sequence: zero output rows
       for (int e = threadIdx.x; e < G * D; e += 64 * kWaves)
         store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
     }
@@ -578,7 +491,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
 
-  const bool direct = nparts_s == 1;
+  const bool direct = nparts_s == 1 && npre == 0;
   for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) {
     const int hh = e / D, d = e % D;
     float M = lds_m[0][hh];
@@ -597,17 +510,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     if (direct) {
       store_out<OUT>(p.out, ((size_t)s * H + h) * D + d, o);
     } else {
-      const size_t row = ((size_t)s * H + h) * p.num_parts + part;
+      const size_t row = ((size_t)s * H + h) * p.ws_stride + part;
       p.ws_o[row * D + d] = o;
       if (d == 0) p.ws_lse[row] = M + log2f(den);
     }
   }
 }
 
-// Log-sum-exp merge of the partitions of sequences that used more than one:
-// one workgroup of kMergeThreads per (sequence, query head).  Thread t sums
-// partitions q = t / D, t / D + QG, ... of output element d = t % D; the loop
-// is unrolled so that its loads are in flight together.
+// Log-sum-exp merge of the partitions of sequences that used more than one
+// (and of a sequence's suffix partials with its shared-prefix partials): one
+// workgroup of kMergeThreads per (sequence, query head).  Thread t sums
+// partials q = t / D, t / D + QG, ... of output element d = t % D; the loop is
+// unrolled so that its loads are in flight together.
 constexpr int kMergeThreads = 256;
 
 __device__ __forceinline__ float wave_max64(float x) {
@@ -628,14 +542,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
   const int ntile = (L + kTile - 1) / kTile;
   const int np = (ntile + p.part_tiles - 1) / p.part_tiles;
-  if (np <= 1) return;   // written directly by the decode kernel
+  const int npre = prefix_parts_of(p, s);
+  if (np <= 1 && npre == 0) return;   // written directly by the decode kernel
+  // partial q: suffix partition q < np, else prefix partition q - np
+  const int nq = np + npre;
+  auto slot = [&](int q) { return q < np ? q : p.ws_pre + (q - np); };
   const int t = threadIdx.x;
-  const size_t base = (size_t)row * p.num_parts;
+  const size_t base = (size_t)row * p.ws_stride;
   const float *lse = p.ws_lse + base;
   const float *o = p.ws_o + base * D;
 
   float M = -INFINITY;
-  for (int q = t; q < np; q += kMergeThreads) M = fmaxf(M, lse[q]);
+  for (int q = t; q < nq; q += kMergeThreads) M = fmaxf(M, lse[slot(q)]);
   M = wave_max64(M);
   if ((t & 63) == 0) red[t >> 6] = M;
   __syncthreads();
@@ -646,9 +564,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const int qg = t / D, d = t % D;
   float num = 0.f, den = 0.f;
 #pragma unroll 8
-  for (int q = qg; q < np; q += QG) {
-    const float c = exp2f(lse[q] - M);
-    num += c * o[(size_t)q * D + d];
+  for (int q = qg; q < nq; q += QG) {
+    const int sq = slot(q);
+    const float c = exp2f(lse[sq] - M);
+    num += c * o[(size_t)sq * D + d];
     den += c;
   }
   part_num[qg][d] = num;
@@ -671,7 +590,8 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS>), dim3((unsigned)grid),
                      dim3(64 * kWaves), 0, stream, p);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.num_parts <= 1) return err;
+  // with shared prefixes the caller launches the merge after the prefix pass
+  if (err != hipSuccess || p.num_parts <= 1 || p.seq_group) return err;
   hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_seqs * p.num_heads),
                      dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
@@ -699,6 +619,22 @@ hipError_t launch_d(const DecodeParams &p, int out_dtype, int head_dim, hipStrea
 }
 
 }  // namespace
+
+hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream) {
+  const dim3 grid(p.num_seqs * p.num_heads), block(kMergeThreads);
+  if (head_dim == 64) {
+    if (out_dtype == PKV_F32)
+      hipLaunchKernelGGL((merge_kernel<64, PKV_F32>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<64, PKV_F16>), grid, block, 0, stream, p);
+  } else {
+    if (out_dtype == PKV_F32)
+      hipLaunchKernelGGL((merge_kernel<128, PKV_F32>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<128, PKV_F16>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, int head_dim,
                          hipStream_t stream) {

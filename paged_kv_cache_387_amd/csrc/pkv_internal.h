@@ -54,7 +54,65 @@ struct DecodeParams {
   uint8_t *v_cache_w;
   uint16_t *k_scale_w;
   uint16_t *v_scale_w;
+  // Shared prefixes only (seq_group null otherwise): block_tables /
+  // seq_lens then describe each sequence's suffix, and a sequence s with
+  // seq_group[s] = g in [0, num_groups) and a prefix of at least one tile also
+  // has the partials of its group's prefix in workspace slots ws_pre .. of its
+  // row; its suffix partials always go to the workspace and the merge writes
+  // `out`.
+  const int32_t *seq_group;
+  const int32_t *group_prefix_lens;
+  int num_groups;
+  int max_prefix_blocks;
+  int pp_tiles;     // tiles per prefix partition
+  int ws_stride;    // partial slots per (sequence, head) row of the workspace
+  int ws_pre;       // first slot of the prefix partials
 };
+
+// Shared-prefix pass: for each group of sequences whose block tables begin
+// with the same blocks, attention of all the group's queries over those
+// blocks, read once per (group, kv head).
+struct PrefixParams {
+  const void *q;
+  const uint8_t *k_cache;
+  const uint8_t *v_cache;
+  const uint16_t *k_scale;
+  const uint16_t *v_scale;
+  const int32_t *offsets;      // [num_groups + 1] CSR offsets into members
+  const int32_t *members;      // [num_members] sequence indices
+  const int32_t *tables;       // [num_groups][max_prefix_blocks]
+  const int32_t *prefix_lens;  // [num_groups] tokens
+  float *ws_o;
+  float *ws_lse;
+  int num_blocks;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;                   // query heads per kv head
+  int num_groups;
+  int num_members;
+  int max_prefix_blocks;
+  int num_units;               // num_groups * num_kv_heads
+  int col_blocks;              // workgroups across one group's query columns
+  int pp_tiles;                // tiles per prefix partition
+  int num_pparts;              // prefix partitions in the grid
+  int ws_stride;
+  int ws_pre;
+  float qk_scale;
+};
+
+// Prefix partials of sequence s (0: none).  Used identically by the decode
+// kernel (which then never writes `out` directly) and the merge.
+__device__ inline int prefix_parts_of(const DecodeParams &p, int s) {
+  if (p.seq_group == nullptr) return 0;
+  const int g = p.seq_group[s];
+  if ((unsigned)g >= (unsigned)p.num_groups) return 0;
+  int len = p.group_prefix_lens[g];
+  const int cap = p.max_prefix_blocks * p.block_size;
+  len = len < 0 ? 0 : (len > cap ? cap : len);
+  const int tiles = len / kTile;
+  return (tiles + p.pp_tiles - 1) / p.pp_tiles;
+}
 
 // Workgroups land on a die's compute units roughly round robin by id, and
 // the die and compute-unit counts are powers of two.  A count that strides
@@ -104,6 +162,15 @@ hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, 
                          hipStream_t stream);
 hipError_t launch_decode_step(const DecodeParams &p, int cache_dtype, int src_dtype,
                               int out_dtype, int head_dim, hipStream_t stream);
+// Columns (query vectors) one prefix workgroup handles: 16 per MFMA chunk.
+inline int prefix_chunks(int cache_dtype) { return cache_dtype == PKV_F32 ? 2 : 4; }
+inline int64_t prefix_grid(const PrefixParams &p) {
+  return (int64_t)unit_groups(p.num_units) * kXcds * p.col_blocks * p.num_pparts;
+}
+hipError_t launch_prefix(const PrefixParams &p, int cache_dtype, int head_dim, int block_size,
+                         hipStream_t stream);
+hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream);
+
 hipError_t launch_write(const WriteParams &p, int src_dtype, int cache_dtype, int head_dim,
                         hipStream_t stream);
 hipError_t launch_copy(const CopyParams &p, hipStream_t stream);

@@ -149,3 +149,35 @@ def fused_step(r: Replay, w, partition_size: int | None = None, out_dtype=None, 
                             cow_src=_to_dev(src.astype(np.int32)), out_dtype=odt,
                             partition_size=ps, stream=stream)
     return out, slots, pairs, tables, lens
+
+
+def shared(r: Replay, w, step: bool, partition_size: int | None = None, out_dtype=None,
+           min_prefix_tokens: int = 0, stream=None):
+    """Decode of workload `w` through paged_attention_decode_shared: the
+    allocator's tables are split into shared prefixes and suffixes
+    (export_shared).  With `step` (w replayed up to its ("step",) marker) the
+    allocator first appends one token per decode sequence and the call also
+    copies and writes, as fused_step.  Returns (out, slots, copy pairs, shared
+    export, full tables, lens)."""
+    import torch
+    from synth.workloads import step_rows
+    from . import PrefixGroups, paged_attention_decode_shared
+    seqs = list(w.decode_seqs)
+    slots = pairs = None
+    kw = {}
+    if step:
+        slots, pairs, src = r.alloc.append_slots(seqs, with_src=True)
+        k, v = step_rows(w)
+        kw = dict(key=_to_dev(k), value=_to_dev(v), cow_src=_to_dev(src.astype(np.int32)))
+    maxb = w.max_blocks_per_seq
+    sh = r.alloc.export_shared(seqs, maxb, maxb, min_prefix_tokens)
+    groups = PrefixGroups(sh)
+    odt = {"f32": torch.float32, "f16": torch.float16}[w.out_dtype] if out_dtype is None \
+        else out_dtype
+    ps = w.partition_size if partition_size is None else partition_size
+    out = paged_attention_decode_shared(
+        r.query, r.cache, _to_dev(sh["suffix_tables"]), _to_dev(sh["suffix_lens"]),
+        float(np.float32(w.scale)), groups, out_dtype=odt, partition_size=ps, stream=stream,
+        **kw)
+    tables, lens = r.alloc.export_tables(seqs, maxb)
+    return out, slots, pairs, sh, tables, lens

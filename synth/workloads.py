@@ -210,6 +210,60 @@ def c5_shared_prefix(num_seqs: int = 64, prefix: int = 8192, suffix_lo: int = 25
         content_owner=owner, description="shared-prefix copy-on-write decode step")
 
 
+def forked_groups(name: str, groups, singles=(), suffix_lo: int = 1, suffix_hi: int = 40,
+                  H: int = 16, Hkv: int = 2, D: int = 128, cache_dtype: str = "f16",
+                  keep_parents: bool = False, seed: int = 11) -> Workload:
+    """Several shared prefixes plus independent sequences.
+
+    For each (prefix, n_children) of `groups` a parent is allocated and written
+    (prefix tokens), forked to n_children children and, unless keep_parents,
+    freed; each child then gets a suffix of U[suffix_lo, suffix_hi] tokens of
+    its own (0 allowed).  Kept parents decode too (their length is the
+    prefix).  Each length of `singles` is an unrelated sequence.  The decode
+    batch lists all of them in a seeded shuffled order.
+    """
+    seed = _cfg_seed(950) + seed
+    ops, owner, decode, lens = [], {}, [], {}
+    nid = 1
+    for gi, (prefix, nchild) in enumerate(groups):
+        parent = nid
+        kids = list(range(nid + 1, nid + 1 + nchild))
+        nid += 1 + nchild
+        ops += [("allocate", parent, prefix), ("write", parent, 0, prefix)]
+        ops += [("fork", parent, c) for c in kids]
+        if keep_parents:
+            decode.append(parent)
+            lens[parent] = prefix
+        else:
+            ops.append(("free", parent))
+        suf = randint(stream_key(seed, "suffix", gi), 0, nchild, suffix_lo, suffix_hi)
+        for c, L in zip(kids, suf):
+            L = int(L)
+            if L:
+                ops += [("allocate", c, prefix + L), ("write", c, prefix, L)]
+            owner[c] = [(0, prefix, parent)]
+            lens[c] = prefix + L
+            decode.append(c)
+    for L in singles:
+        ops += [("allocate", nid, int(L)), ("write", nid, 0, int(L))]
+        decode.append(nid)
+        lens[nid] = int(L)
+        nid += 1
+    order = permutation(stream_key(seed, "decode_order"), len(decode))
+    decode = [decode[int(i)] for i in order]
+    need = sum(-(-L // 16) + 1 for L in lens.values())
+    num_blocks = need + 16
+    max_len = max(lens.values()) + 1
+    q_dtype = "f32" if cache_dtype == "f32" else "f16"
+    return Workload(
+        name=name, num_heads=H, num_kv_heads=Hkv, head_dim=D, q_dtype=q_dtype,
+        src_dtype=q_dtype, cache_dtype=cache_dtype,
+        out_dtype="f32" if cache_dtype == "f32" else "f16", scale=1.0 / math.sqrt(D),
+        num_blocks=num_blocks, free_order=permutation(stream_key(seed, "free_order"), num_blocks),
+        ops=ops, decode_seqs=decode, max_blocks_per_seq=-(-max_len // 16), seed=seed,
+        content_owner=owner, description="forked shared prefixes and independent sequences")
+
+
 def custom(name: str, lens, H: int, Hkv: int, D: int, cache_dtype: str = "f16",
            q_dtype: str | None = None, out_dtype: str = "f16", num_blocks: int | None = None,
            max_blocks: int | None = None, partition_size: int = 0, seed: int = 7,

@@ -123,3 +123,66 @@ def test_write_and_copy_argument_validation():
     assert L.paged_copy_blocks(b, b, None, None, pkv.I8, 8, b, 1, 2, 64, 16, None) == pkv.EINVAL
     assert L.paged_copy_blocks(b, b, None, None, pkv.F16, 8, b, 0, 2, 64, 16, None) == pkv.OK
     assert L.paged_copy_blocks(b, b, None, None, pkv.F16, 8, b, -1, 2, 64, 16, None) == pkv.EINVAL
+
+
+def _groups(**kw):
+    g = dict(num_groups=1, num_members=4, max_group_size=4, max_prefix_blocks=8,
+             offsets=1 << 20, members=1 << 20, tables=1 << 20, prefix_lens=1 << 20,
+             seq_group=1 << 20)
+    g.update(kw)
+    return pkv.PrefixGroupsC(**g)
+
+
+def _shared_status(groups, **kw):
+    args = dict(out=1 << 20, out_dtype=pkv.F16, query=1 << 20, q_dtype=pkv.F16,
+                k_cache=1 << 20, v_cache=1 << 20, cache_dtype=pkv.F16, num_blocks=64,
+                block_tables=1 << 20, max_blocks=8, seq_lens=1 << 20, num_seqs=4,
+                num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, workspace=None,
+                ws_bytes=0)
+    args.update(kw)
+    a, P = args, ctypes.c_void_p
+    return pkv.lib().paged_attention_decode_shared(
+        P(a["out"]), a["out_dtype"], P(a["query"]), a["q_dtype"], None, None, pkv.F16, None,
+        P(a["k_cache"]), P(a["v_cache"]), None, None, a["cache_dtype"], a["num_blocks"],
+        P(a["block_tables"]), a["max_blocks"], P(a["seq_lens"]), a["num_seqs"],
+        a["num_heads"], a["num_kv_heads"], a["head_dim"], a["block_size"], 0.1,
+        None if groups is None else ctypes.byref(groups), 0, P(a["workspace"]),
+        a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("groups,kw,status", [
+    (None, {}, pkv.EINVAL),                                   # groups struct required
+    ("neg", {}, pkv.EINVAL),                                  # num_groups < 0
+    ("size0", {}, pkv.EINVAL),                                # max_group_size 0
+    ("noprefix", {}, pkv.EINVAL),                             # max_prefix_blocks 0
+    ("nullmembers", {}, pkv.EINVAL),                          # a group array missing
+    ("misaligned", {}, pkv.EINVAL),
+    ("ok", dict(block_size=12), pkv.ENOTSUP),
+    ("ok", dict(num_heads=9), pkv.EINVAL),
+    ("ok", dict(workspace=None), pkv.EINVAL),                 # a workspace is needed
+    ("ok", dict(num_seqs=0), pkv.OK),
+    ("none", dict(num_seqs=0), pkv.OK),
+])
+def test_shared_argument_validation(groups, kw, status):
+    g = {"ok": _groups(), "neg": _groups(num_groups=-1), "size0": _groups(max_group_size=0),
+         "noprefix": _groups(max_prefix_blocks=0), "nullmembers": _groups(members=0),
+         "misaligned": _groups(tables=(1 << 20) + 2), "none": _groups(num_groups=0),
+         None: None}[groups]
+    assert _shared_status(g, **kw) == status
+
+
+def test_shared_workspace_sizes():
+    # 64 sequences sharing an 8192-token prefix, suffix tables 65 blocks wide:
+    # suffix partitions (64 tiles each: 2, padded to 3) then 4 prefix
+    # partitions of 128 tiles per (sequence, head) row
+    g = _groups(num_groups=1, num_members=64, max_group_size=64, max_prefix_blocks=512)
+    ws = pkv.lib().paged_attention_shared_workspace_bytes(64, 64, 8, 128, 65, 16, 0,
+                                                          ctypes.byref(g))
+    rows = 64 * 64 * (3 + 4)
+    assert ws == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    # no groups: the plain decode's workspace
+    g0 = _groups(num_groups=0)
+    for mb in (7, 2048):
+        assert pkv.lib().paged_attention_shared_workspace_bytes(
+            8, 64, 8, 128, mb, 16, 0, ctypes.byref(g0)) == pkv.workspace_bytes(8, 64, 8, 128, mb)
+    assert pkv.lib().paged_attention_shared_workspace_bytes(8, 64, 8, 128, 7, 16, 0, None) == 0
