@@ -241,7 +241,8 @@ class BlockAllocator:
         return dict(suffix_tables=st[:n], suffix_lens=sl[:n], seq_group=sg[:n],
                     group_offsets=go[:g + 1], group_members=gm[:go[g]],
                     group_tables=gt[:g], group_prefix_lens=gp[:g], num_groups=g,
-                    max_group_size=mg.value, max_prefix_blocks=max_prefix_blocks)
+                    max_group_size=mg.value, max_prefix_blocks=max_prefix_blocks,
+                    block_size=self.block_size)
 
 
 # ---------------------------------------------------------------------------
@@ -489,7 +490,18 @@ class PrefixGroups:
 
         self.num_groups = int(shared["num_groups"])
         self.max_group_size = max(int(shared["max_group_size"]), 1)
-        self.max_prefix_blocks = int(shared["max_prefix_blocks"])
+        # the prefix tables cut to the longest prefix (the prefix pass plans
+        # its partitions over this width)
+        plens = np.asarray(shared["group_prefix_lens"], np.int64)
+        width = int(shared["max_prefix_blocks"])
+        if self.num_groups > 0:
+            bs = int(shared.get("block_size", 0)) or None
+            longest = int(plens.max())
+            if bs:
+                width = max(1, min(width, -(-longest // bs)))
+            shared = dict(shared, group_tables=np.ascontiguousarray(
+                np.asarray(shared["group_tables"], np.int32)[:, :width]))
+        self.max_prefix_blocks = width
         self.num_members = int(len(shared["group_members"]))
         self.offsets = up(shared["group_offsets"])
         self.members = up(shared["group_members"])

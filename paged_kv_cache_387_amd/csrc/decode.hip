@@ -517,70 +517,117 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   }
 }
 
-// Log-sum-exp merge of the partitions of sequences that used more than one
-// (and of a sequence's suffix partials with its shared-prefix partials): one
-// workgroup of kMergeThreads per (sequence, query head).  Thread t sums
-// partials q = t / D, t / D + QG, ... of output element d = t % D; the loop is
-// unrolled so that its loads are in flight together.
+// Log-sum-exp merge of the partials of sequences that used more than one
+// partition (and of a sequence's suffix partials with its shared-prefix
+// partials).  A thread owns 4 output elements of one (sequence, head) row and
+// folds the partials q = qg, qg + QG, ... into a running (max, sum, weighted
+// sum) -- one pass, no separate maximum; the QG groups of a row are then
+// combined through LDS.  A workgroup of kMergeThreads holds 256 / (D/4 * QG)
+// rows.
 constexpr int kMergeThreads = 256;
 
-__device__ __forceinline__ float wave_max64(float x) {
+template <int D, int OUT, int QG>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
+  constexpr int TPH = D / 4;                       // threads per row and partial group
+  constexpr int RPW = kMergeThreads / (TPH * QG);  // rows per workgroup
+  static_assert(RPW >= 1, "partial groups");
+  __shared__ f4 red_o[QG > 1 ? kMergeThreads : 1];
+  __shared__ float red_m[QG > 1 ? kMergeThreads : 1];
+  __shared__ float red_z[QG > 1 ? kMergeThreads : 1];
+  const int t = threadIdx.x;
+  const int rl = t / (TPH * QG);
+  const int qg = (t / TPH) % QG;
+  const int dv = t % TPH;
+  const int row = blockIdx.x * RPW + rl;           // s * H + h
+  const bool live_row = row < p.num_seqs * p.num_heads;
+  int np = 0, npre = 0;
+  if (live_row) {
+    const int s = row / p.num_heads;
+    int L = p.seq_lens[s];
+    L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
+    const int ntile = (L + kTile - 1) / kTile;
+    np = (ntile + p.part_tiles - 1) / p.part_tiles;
+    npre = prefix_parts_of(p, s);
+  }
+  // rows with one partition and no prefix were written by the decode kernel
+  const bool merge = live_row && (np > 1 || npre > 0);
+  const int nq = np + npre;
+  float m = -INFINITY, z = 0.0f;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  if (merge) {
+    const size_t base = (size_t)row * p.ws_stride;
+    const float *lse = p.ws_lse + base;
+    const f4 *o = reinterpret_cast<const f4 *>(p.ws_o + base * D) + dv;
+#pragma unroll 4
+    for (int q = qg; q < nq; q += QG) {
+      const int sq = q < np ? q : p.ws_pre + (q - np);
+      const float lq = lse[sq];
+      const f4 oq = o[(size_t)sq * (D / 4)];
+      const float mn = fmaxf(m, lq);
+      const float a = exp2f(m - mn), b = exp2f(lq - mn);
+      acc = acc * a + oq * b;
+      z = z * a + b;
+      m = mn;
+    }
+  }
+  if constexpr (QG > 1) {
+    red_o[t] = acc;
+    red_m[t] = m;
+    red_z[t] = z;
+    __syncthreads();
+    if (qg != 0) return;
+    float M = m;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+    for (int i = 1; i < QG; ++i) M = fmaxf(M, red_m[t + i * TPH]);
+    acc = f4{0.f, 0.f, 0.f, 0.f};
+    z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      const float mi = red_m[t + i * TPH];
+      const float c = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+      acc += red_o[t + i * TPH] * c;
+      z += red_z[t + i * TPH] * c;
+    }
+  }
+  if (!merge) return;
+  const f4 r = acc * (1.0f / z);
+  const size_t oi = (size_t)row * D + 4 * dv;
+  if constexpr (OUT == PKV_F32) {
+    *reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.out) + oi) = r;
+  } else {
+    *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(p.out) + oi) =
+        h4{(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
+  }
+}
+
+// Partial groups per row for up to `nq` partials per row (at most 8 partials
+// per thread when the row has room for more groups).
+inline int merge_groups(int nq, int head_dim) {
+  const int max_groups = kMergeThreads / (head_dim / 4);
+  int g = 1;
+  while (g < max_groups && g * 8 < nq) g *= 2;
+  return g;
+}
+
+template <int D, int OUT, int QG>
+hipError_t launch_merge_g(const DecodeParams &p, hipStream_t stream) {
+  constexpr int RPW = kMergeThreads / (D / 4 * QG);
+  const int rows = p.num_seqs * p.num_heads;
+  hipLaunchKernelGGL((merge_kernel<D, OUT, QG>), dim3((rows + RPW - 1) / RPW),
+                     dim3(kMergeThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <int D, int OUT>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
-  constexpr int QG = kMergeThreads / D;   // partition groups
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float part_num[QG][D];
-  __shared__ float part_den[QG];
-  const int row = blockIdx.x;              // s * H + h
-  const int s = row / p.num_heads;
-  int L = p.seq_lens[s];
-  L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
-  const int ntile = (L + kTile - 1) / kTile;
-  const int np = (ntile + p.part_tiles - 1) / p.part_tiles;
-  const int npre = prefix_parts_of(p, s);
-  if (np <= 1 && npre == 0) return;   // written directly by the decode kernel
-  // partial q: suffix partition q < np, else prefix partition q - np
-  const int nq = np + npre;
-  auto slot = [&](int q) { return q < np ? q : p.ws_pre + (q - np); };
-  const int t = threadIdx.x;
-  const size_t base = (size_t)row * p.ws_stride;
-  const float *lse = p.ws_lse + base;
-  const float *o = p.ws_o + base * D;
-
-  float M = -INFINITY;
-  for (int q = t; q < nq; q += kMergeThreads) M = fmaxf(M, lse[slot(q)]);
-  M = wave_max64(M);
-  if ((t & 63) == 0) red[t >> 6] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
-
-  const int qg = t / D, d = t % D;
-  float num = 0.f, den = 0.f;
-#pragma unroll 8
-  for (int q = qg; q < nq; q += QG) {
-    const int sq = slot(q);
-    const float c = exp2f(lse[sq] - M);
-    num += c * o[(size_t)sq * D + d];
-    den += c;
-  }
-  part_num[qg][d] = num;
-  if (d == 0) part_den[qg] = den;
-  __syncthreads();
-  if (t < D) {
-    float n = 0.f, z = 0.f;
-#pragma unroll
-    for (int i = 0; i < QG; ++i) {
-      n += part_num[i][t];
-      z += part_den[i];
-    }
-    store_out<OUT>(p.out, (size_t)row * D + t, n / z);
+hipError_t launch_merge_d(const DecodeParams &p, hipStream_t stream) {
+  switch (merge_groups(p.ws_stride, D)) {
+    case 1: return launch_merge_g<D, OUT, 1>(p, stream);
+    case 2: return launch_merge_g<D, OUT, 2>(p, stream);
+    case 4: return launch_merge_g<D, OUT, 4>(p, stream);
+    case 8: return launch_merge_g<D, OUT, 8>(p, stream);
+    default:
+      if constexpr (D == 64) return launch_merge_g<D, OUT, 16>(p, stream);
+      else return launch_merge_g<D, OUT, 8>(p, stream);
   }
 }
 
@@ -592,9 +639,7 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   // with shared prefixes the caller launches the merge after the prefix pass
   if (err != hipSuccess || p.num_parts <= 1 || p.seq_group) return err;
-  hipLaunchKernelGGL((merge_kernel<D, OUT>), dim3(p.num_seqs * p.num_heads),
-                     dim3(kMergeThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_merge_d<D, OUT>(p, stream);
 }
 
 template <int KV, int D, int OUT, int SRC>
@@ -621,19 +666,11 @@ hipError_t launch_d(const DecodeParams &p, int out_dtype, int head_dim, hipStrea
 }  // namespace
 
 hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.num_seqs * p.num_heads), block(kMergeThreads);
-  if (head_dim == 64) {
-    if (out_dtype == PKV_F32)
-      hipLaunchKernelGGL((merge_kernel<64, PKV_F32>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((merge_kernel<64, PKV_F16>), grid, block, 0, stream, p);
-  } else {
-    if (out_dtype == PKV_F32)
-      hipLaunchKernelGGL((merge_kernel<128, PKV_F32>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((merge_kernel<128, PKV_F16>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  if (head_dim == 64)
+    return out_dtype == PKV_F32 ? launch_merge_d<64, PKV_F32>(p, stream)
+                                : launch_merge_d<64, PKV_F16>(p, stream);
+  return out_dtype == PKV_F32 ? launch_merge_d<128, PKV_F32>(p, stream)
+                              : launch_merge_d<128, PKV_F16>(p, stream);
 }
 
 hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, int head_dim,

@@ -30,6 +30,8 @@
 namespace pkv {
 namespace {
 
+typedef float f16v __attribute__((ext_vector_type(16)));
+
 // Wait until at most N vector-memory operations of the wave are outstanding
 // (loads complete in issue order), and keep the compiler from moving memory
 // accesses across the wait.  Loads straight into LDS are not tracked by the
@@ -69,12 +71,6 @@ __device__ __forceinline__ void lds_read_row(uint32_t addr, u4 *out) {
   }
 }
 
-// Tiles in flight per wave (LDS ring slots): 2*NL KiB each.
-template <int KV> struct PrefixRing { static constexpr int NR = 4; };
-template <> struct PrefixRing<PKV_F32> { static constexpr int NR = 2; };
-template <> struct PrefixRing<PKV_I8> { static constexpr int NR = 6; };
-template <> struct PrefixRing<PKV_E4M3> { static constexpr int NR = 6; };
-
 template <int KV, int D, int BS, int C>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) {
   constexpr int EB = Kv<KV>::EB;
@@ -86,7 +82,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
   constexpr int NL = D * EB / 64;
   constexpr int NACC = D / 16;
   constexpr int E = 4 / EB;
-  constexpr int NR = PrefixRing<KV>::NR;  // tiles in flight per wave
+  constexpr int NR = 2;                   // tiles in flight per wave (LDS ring slots)
   constexpr int LPT = 2 * NL + (QUANT ? 2 : 0);   // vector-memory loads per tile
   constexpr int CW = 16 * C;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
@@ -533,11 +529,566 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2- and 1-byte caches: 32x32 MFMA blocks.
+//
+// A wave takes 32-token steps (two 16-token tiles) of the partition, steps
+// w, w+4, ... (waves split the tokens; all four hold the workgroup's 64 query
+// columns as two blocks of 32).  Per step and column block:
+//   S^T[32 tokens][32 columns] = K q      D/16 MFMAs 32x32x16 (k = 16 dims)
+//   online softmax per column
+//   O^T[D][32] += V^T P^T                 2 x D/32 MFMAs (k = 16 tokens)
+// Layouts of v_mfma_f32_32x32x16_f16, lane l = 32h + n: A row l%32 and
+// B column l%32 hold k = 8h .. 8h+7; D holds column n, rows 8j + 4h + v
+// (j, v = 0..3) in element 4j + v.  Hence:
+//   q.K: lane (n, h) gives token n's K and column n's q for dims 16kk + 8h ..
+//        (1-byte K: columns of 16 codes are split over the MFMA pair 2c, 2c+1:
+//        lane h loads code column 2c + h, its low 8 codes go to MFMA 2c and the
+//        high 8 to 2c + 1, and q follows the same order);
+//   P.V: the scores of lane (n, h) are tokens 8j + 4h + v; MFMA kc (tokens
+//        16kc .. 16kc+15) takes elements 8kc .. 8kc+7 as its k slots, i.e.
+//        tokens 16kc + 4h + 0..3 and 16kc + 8 + 4h + 0..3 -- the V operand of
+//        lane (m, h) reads exactly those tokens: two 16-byte groups of V.
+//        2-byte V: group = 4 tokens x dims (2c, 2c+1), c = 32G + m: one MFMA
+//        for the even dims and one for the odd dims of each G.  1-byte V:
+//        group = 4 tokens x dims 4m .. 4m+3: one MFMA per dim offset e.
+// K, V (and quantized-cache scales) go straight into a per-wave LDS ring.
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p) {
+  constexpr int EB = Kv<KV>::EB;
+  constexpr bool QUANT = EB == 1;
+  static_assert(KV == PKV_F16 || QUANT, "2- and 1-byte caches");
+  constexpr int SLICE = BS * D * EB;
+  constexpr bool SPLIT = BS < kTile;
+  constexpr int TB = SPLIT ? BS : kTile;       // tokens of a stored tile
+  constexpr int TPS = BS >= 32 ? 1 : 32 / BS;  // table entries per 32-token step
+  constexpr int NKK = D / 16;                  // q.K MFMAs per block
+  constexpr int KLD = QUANT ? NKK / 2 : NKK;   // 16-byte K loads per lane and step
+  constexpr int NG = QUANT ? 1 : D / 64;       // 2-byte V: groups of 32 column pairs
+  constexpr int VLD = QUANT ? 4 : 4 * NG;      // 16-byte V loads per lane and step
+  constexpr int NT = QUANT ? 4 : 2 * NG;       // output tiles (32 rows) per column block
+  constexpr int NB2 = 2;                       // column blocks of 32 per wave
+  constexpr int CW = 32 * NB2;
+  constexpr int NR = QUANT ? 4 : 2;            // LDS ring depth (steps in flight)
+  constexpr int LPS = KLD + VLD + (QUANT ? 1 : 0);
+  static_assert((NR - 1) * LPS < 64, "wait count");
+
+  // The ring (per wave: NR slots of KLD + VLD rows of 64 lanes x 16 bytes);
+  // after the tile loop the same memory holds every wave's accumulators.
+  constexpr size_t kRingBytes = sizeof(u4) * kWaves * NR * (KLD + VLD) * 64;
+  constexpr size_t kAccBytes = sizeof(f16v) * kWaves * NB2 * NT * 64;
+  __shared__ u4 lds_raw[(kRingBytes > kAccBytes ? kRingBytes : kAccBytes) / sizeof(u4)];
+  u4(*lds_ring)[NR][KLD + VLD][64] = reinterpret_cast<u4(*)[NR][KLD + VLD][64]>(&lds_raw[0]);
+  f16v(*lds_acc)[NB2][NT][64] = reinterpret_cast<f16v(*)[NB2][NT][64]>(&lds_raw[0]);
+  __shared__ uint32_t lds_sc[kWaves][NR][64];   // quantized: K then V scales of the step
+  __shared__ float lds_m[kWaves][CW];
+  __shared__ float lds_l[kWaves][CW];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+
+  const int bid = blockIdx.x;
+  const int die_slot = bid / kXcds;
+  const int ugroups = unit_groups(p.num_units);
+  const int per_part = ugroups * p.col_blocks;
+  const int part = die_slot / per_part;
+  const int rem = die_slot - part * per_part;
+  const int cb = rem / ugroups;
+  const int u = (rem - cb * ugroups) * kXcds + bid % kXcds;
+  if (u >= p.num_units || part >= p.num_pparts) return;
+  const int grp = u / p.num_kv_heads;
+  const int kvh = u - grp * p.num_kv_heads;
+  const int G = p.group;
+  const int H = p.num_heads;
+
+  int off = p.offsets[grp];
+  int end = p.offsets[grp + 1];
+  off = off < 0 ? 0 : (off > p.num_members ? p.num_members : off);
+  end = end < off ? off : (end > p.num_members ? p.num_members : end);
+  const int ncols = (end - off) * G;
+  const int c0 = cb * CW;
+  if (c0 >= ncols) return;
+
+  int plen = p.prefix_lens[grp];
+  plen = plen < 0 ? 0 : (plen > p.max_prefix_blocks * BS ? p.max_prefix_blocks * BS : plen);
+  const int ntile = plen / kTile;
+  const int first = part * p.pp_tiles;        // even: pp_tiles is a multiple of 8
+  if (first >= ntile) return;
+  const int last = min(first + p.pp_tiles, ntile);
+  const int nsteps = (last - first + 1) / 2;  // the last may hold one tile
+  const int ns_w = nsteps > w ? (nsteps - w + kWaves - 1) / kWaves : 0;
+  const int32_t *trow = p.tables + (size_t)grp * p.max_prefix_blocks;
+  // The column blocks of one partition read the same tiles: each starts its
+  // walk at a different step, so that they do not request the same lines of
+  // the same L2 channels at the same time (walks of up to 64 steps).
+  const int rot = ns_w > 0 && ns_w <= 64 ? (cb * 5) % ns_w : 0;
+  auto walk = [&](int k) { return rot ? (k + rot < ns_w ? k + rot : k + rot - ns_w) : k; };
+
+  // Table entries of step c + lane of this wave (TPS per step), clamped.
+  auto load_tv = [&](int c, int *tv) {
+    const int step = w + walk(c + lane < ns_w ? c + lane : 0) * kWaves;
+    const int e0 = (first / 2 + step) * TPS;
+    const int lim = p.max_prefix_blocks;
+#pragma unroll
+    for (int e = 0; e < TPS; ++e) tv[e] = trow[e0 + e < lim ? e0 + e : lim - 1];
+  };
+  int tv_next[TPS];
+  load_tv(0, tv_next);
+
+  // Query columns: column c0 + 32*nb + n is head kvh*G + (c % G) of member c / G.
+  int col_seq[NB2], col_head[NB2];
+  bool col_ok[NB2];
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    const int c = c0 + 32 * nb + n;
+    col_ok[nb] = c < ncols;
+    const int cc = col_ok[nb] ? c : 0;
+    const int sq = p.members[off + cc / G];
+    col_ok[nb] = col_ok[nb] && (unsigned)sq < (unsigned)p.num_seqs;
+    col_seq[nb] = (unsigned)sq < (unsigned)p.num_seqs ? sq : 0;
+    col_head[nb] = kvh * G + cc % G;
+  }
+  // B operands: q dims of MFMA kk for lane half h (see the K order above)
+  h8 qf[NB2][NKK];
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    const _Float16 *qr = reinterpret_cast<const _Float16 *>(p.q) +
+                         ((size_t)col_seq[nb] * H + col_head[nb]) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int d0 = QUANT ? 16 * (2 * (kk / 2) + h) + 8 * (kk % 2) : 16 * kk + 8 * h;
+      qf[nb][kk] = __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qr + d0)));
+    }
+  }
+  float qbias[NB2];
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    qbias[nb] = 0.0f;
+    if constexpr (KV == PKV_I8) {
+      float qs = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs += (float)qf[nb][kk][e];
+      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(qs), __float_as_uint(qs),
+                                                      false, false);
+      qbias[nb] = kI8Bias * (__uint_as_float(a[0]) + __uint_as_float(a[1]));
+    }
+  }
+
+  float m[NB2], l[NB2];
+  f16v acc[NB2][NT];
+  float psum[NB2];   // int8: sum of the fp16 weights P' of this lane's rows
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    m[nb] = -INFINITY;
+    l[nb] = 0.0f;
+    psum[nb] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[nb][t] = f16v{};
+  }
+  constexpr float kTau = QUANT ? 2.0f : 8.0f;
+  bool fresh = true;
+
+  const size_t kv_head_off = (size_t)kvh * SLICE;
+  const size_t block_stride = (size_t)p.num_kv_heads * SLICE;
+
+  struct Slot {
+    bool ok;
+    bool half;   // the step holds one tile only
+  };
+
+  // Block (and tile within the block) of token tt (0..31) of a step whose
+  // table entries are e[0..TPS-1]; *row receives its row in the stored tile.
+  auto locate = [&](const int *e, int tt, int *row, size_t *tile_off) {
+    if constexpr (BS == 32) {
+      *row = tt & 15;
+      *tile_off = (size_t)(tt >> 4) * (TB * D * EB);
+      return e[0];
+    } else if constexpr (BS == 16) {
+      *row = tt & 15;
+      *tile_off = 0;
+      return e[tt >> 4];
+    } else {
+      *row = tt & 7;
+      *tile_off = 0;
+      return e[tt >> 3];
+    }
+  };
+
+  auto issue = [&](const int *tv, int j, int step_tile, int slot, Slot &sl) {
+    // entries of a missing second tile (past the prefix: padding) are
+    // replaced by the first, whose data is read in its place
+    sl.half = step_tile + 1 >= last;
+    constexpr int kHalf = TPS > 1 ? TPS / 2 : 1;
+    const int used = sl.half ? kHalf : TPS;
+    int e[TPS];
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) {
+      e[k] = __builtin_amdgcn_readlane(tv[k < used ? k : 0], j);
+      ok = ok && (unsigned)e[k] < (unsigned)p.num_blocks;
+    }
+    sl.ok = ok;
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) e[k] = ok ? e[k] : 0;
+    // a missing second tile is read from the first (its weights are zero)
+    const int tmask = sl.half ? 15 : 31;
+    // K: token n
+    {
+      int row;
+      size_t toff;
+      const int b = locate(e, n & tmask, &row, &toff);
+      const uint8_t *kb = p.k_cache + (size_t)b * block_stride + kv_head_off + toff;
+#pragma unroll
+      for (int k = 0; k < KLD; ++k)
+        load16_to_lds(kb + (size_t)(((2 * k + h) * TB + row) * 16), &lds_ring[w][slot][k][0]);
+    }
+    // V: tile kc, token quads 4h and 8 + 4h
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int qd = 0; qd < 2; ++qd) {
+        int row;
+        size_t toff;
+        const int tt = ((16 * kc) & tmask) + 8 * qd + 4 * h;
+        const int b = locate(e, tt, &row, &toff);
+        const uint8_t *vb = p.v_cache + (size_t)b * block_stride + kv_head_off + toff;
+        if constexpr (QUANT) {
+          const int grp4 = (D == 128) ? n : (n & 15);   // dims 4*grp4 .. +3
+          load16_to_lds(vb + (size_t)((grp4 * (TB / 4) + row / 4) * 16),
+                        &lds_ring[w][slot][KLD + 2 * kc + qd][0]);
+        } else {
+#pragma unroll
+          for (int gg = 0; gg < NG; ++gg)
+            load16_to_lds(vb + (size_t)(((32 * gg + n) * TB + row) * 4),
+                          &lds_ring[w][slot][KLD + (kc * NG + gg) * 2 + qd][0]);
+        }
+      }
+    }
+    if constexpr (QUANT) {
+      // lane: K (lanes 0-15 of each half) or V (16-31) scales of tokens 2i, 2i+1
+      const int i = n & 15;
+      int row;
+      size_t toff;
+      const int b = locate(e, (2 * i) & tmask, &row, &toff);
+      const int tile_in_block = (int)(toff / (TB * D * EB));
+      const uint16_t *sc = (n < 16 ? p.k_scale : p.v_scale) +
+                           ((size_t)b * p.num_kv_heads + kvh) * BS + tile_in_block * kTile + row;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)sc,
+                                       (__attribute__((address_space(3))) void *)&lds_sc[w][slot][0],
+                                       4, 0, 0);
+    }
+  };
+
+  auto consume = [&](int slot, const Slot &sl) {
+    if (!sl.ok) return;   // a table entry outside the pool: step skipped
+    const uint32_t base = (uint32_t)(size_t)(
+        (__attribute__((address_space(3))) const u4 *)&lds_ring[w][slot][0][lane]);
+    u4 raw[KLD + VLD];
+    lds_read_row<0, KLD + VLD, 1024>(base, raw);
+    u2 ksw[4], vsw[4];
+    if constexpr (QUANT) {
+      // scales of this lane's tokens 8j + 4h + 0..3: words 4j + 2h, +1
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t a = (uint32_t)(size_t)(
+            (__attribute__((address_space(3))) const uint32_t *)&lds_sc[w][slot][4 * jj + 2 * h]);
+        asm volatile("ds_read_b64 %0, %1" : "=v"(ksw[jj]) : "v"(a));
+        asm volatile("ds_read_b64 %0, %1 offset:64" : "=v"(vsw[jj]) : "v"(a));
+      }
+    }
+    lds_wait();
+#pragma unroll
+    for (int i = 0; i < KLD + VLD; ++i) after_wait(raw[i]);
+    float ksf[16], vsf[16];
+    if constexpr (QUANT) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        asm volatile("" : "+v"(ksw[jj]));
+        asm volatile("" : "+v"(vsw[jj]));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          ksf[4 * jj + v] = (float)as_h2(ksw[jj][v >> 1])[v & 1];
+          vsf[4 * jj + v] = (float)as_h2(vsw[jj][v >> 1])[v & 1] * kPvBoost;
+        }
+      }
+    }
+    // A operands
+    h8 ka[NKK];
+    if constexpr (QUANT) {
+#pragma unroll
+      for (int k = 0; k < KLD; ++k) codes16_to_h8<KV>(raw[k], ka[2 * k], ka[2 * k + 1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KLD; ++k) ka[k] = __builtin_bit_cast(h8, raw[k]);
+    }
+    h8 va[2][NT];   // [kc][output tile]
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      if constexpr (QUANT) {
+        const u4 a = raw[KLD + 2 * kc], b = raw[KLD + 2 * kc + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h4 lo = codes4_to_h4<KV>(a[e]), hi = codes4_to_h4<KV>(b[e]);
+          va[kc][e] = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      } else {
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const u4 a = raw[KLD + (kc * NG + gg) * 2], b = raw[KLD + (kc * NG + gg) * 2 + 1];
+          const u4 ev = u4{__builtin_amdgcn_perm(a[1], a[0], 0x05040100u),
+                           __builtin_amdgcn_perm(a[3], a[2], 0x05040100u),
+                           __builtin_amdgcn_perm(b[1], b[0], 0x05040100u),
+                           __builtin_amdgcn_perm(b[3], b[2], 0x05040100u)};
+          const u4 od = u4{__builtin_amdgcn_perm(a[1], a[0], 0x07060302u),
+                           __builtin_amdgcn_perm(a[3], a[2], 0x07060302u),
+                           __builtin_amdgcn_perm(b[1], b[0], 0x07060302u),
+                           __builtin_amdgcn_perm(b[3], b[2], 0x07060302u)};
+          va[kc][2 * gg] = __builtin_bit_cast(h8, ev);
+          va[kc][2 * gg + 1] = __builtin_bit_cast(h8, od);
+        }
+      }
+    }
+    // Scores.  Base-2 score x = k * s (fp16 cache: k = qk_scale for every
+    // token, so the block maximum is taken on the raw s and the scale is
+    // applied inside the exponent's fma; quantized caches: the per-token K
+    // scale makes x explicit).
+    float x[NB2][16], mn[NB2];
+    bool over = false;
+    const float ks = p.qk_scale;
+    // the column blocks' accumulation chains interleaved, so that consecutive
+    // MFMAs do not wait on each other
+    f16v scs[NB2];
+#pragma unroll
+    for (int nb = 0; nb < NB2; ++nb) scs[nb] = f16v{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB2; ++nb)
+        scs[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kk], qf[nb][kk], scs[nb], 0, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < NB2; ++nb) {
+      f16v &sc = scs[nb];
+      // rows 16..31 (elements 8..15) of a half step belong to the missing
+      // tile: left out of the maximum here, their weights zeroed below
+      const int nvalid = sl.half ? 8 : 16;
+      float bm;
+      if constexpr (QUANT) {
+        bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          x[nb][i] = (KV == PKV_I8 ? sc[i] - qbias[nb] : sc[i]) * ks * ksf[i];
+          if (i < nvalid) bm = fmaxf(bm, x[nb][i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[nb][i] = sc[i];
+        float e = sc[0];
+        if (ks >= 0.0f) {   // wave-uniform: the largest score, or the smallest
+#pragma unroll
+          for (int i = 1; i < 16; ++i)
+            if (i < nvalid) e = fmaxf(e, sc[i]);
+        } else {
+#pragma unroll
+          for (int i = 1; i < 16; ++i)
+            if (i < nvalid) e = fminf(e, sc[i]);
+        }
+        bm = e * ks;
+      }
+      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
+                                                      false, false);
+      bm = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      mn[nb] = fmaxf(m[nb], bm);
+      over = over || mn[nb] > m[nb] + kTau;
+    }
+    if (fresh) {
+#pragma unroll
+      for (int nb = 0; nb < NB2; ++nb) m[nb] = mn[nb];
+      fresh = false;
+    } else if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB2; ++nb) {
+        const float alpha = fast_exp2(m[nb] - mn[nb]);
+        l[nb] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[nb][t] *= alpha;
+        if constexpr (KV == PKV_I8) psum[nb] *= alpha;
+        m[nb] = mn[nb];
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB2; ++nb) {
+      float pr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pr[i] = QUANT ? fast_exp2(x[nb][i] - m[nb]) : fast_exp2(fmaf(x[nb][i], ks, -m[nb]));
+      if (sl.half) {
+#pragma unroll
+        for (int i = 8; i < 16; ++i) pr[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        l[nb] += pr[i];
+        if constexpr (QUANT) pr[i] *= vsf[i];
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const h8 pb = h8{(_Float16)pr[8 * kc], (_Float16)pr[8 * kc + 1], (_Float16)pr[8 * kc + 2],
+                         (_Float16)pr[8 * kc + 3], (_Float16)pr[8 * kc + 4],
+                         (_Float16)pr[8 * kc + 5], (_Float16)pr[8 * kc + 6],
+                         (_Float16)pr[8 * kc + 7]};
+        if constexpr (KV == PKV_I8) {   // the weights exactly as the MFMA sees them
+#pragma unroll
+          for (int i = 0; i < 8; ++i) psum[nb] += (float)pb[i];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[nb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[kc][t], pb, acc[nb][t], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int cc = 0; cc < ns_w; cc += 64) {
+    const int nc = min(64, ns_w - cc);
+    int tv[TPS];
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) tv[k] = tv_next[k];
+    auto step_tile = [&](int j) { return first + 2 * (w + walk(cc + j) * kWaves); };
+    Slot ring[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int jj = j < nc ? j : nc - 1;
+      issue(tv, jj, step_tile(jj), j, ring[j]);
+    }
+    int k0 = 0;
+    for (; k0 + 2 * NR <= nc; k0 += NR) {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        wait_vmcnt<(NR - 1) * LPS>();
+        consume(j, ring[j]);
+        asm volatile("" ::: "memory");
+        issue(tv, k0 + j + NR, step_tile(k0 + j + NR), j, ring[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      if (k0 + j < nc) {
+        wait_vmcnt<0>();
+        consume(j, ring[j]);
+      }
+      asm volatile("" ::: "memory");
+      if (k0 + j + NR < nc) issue(tv, k0 + j + NR, step_tile(k0 + j + NR), j, ring[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+      if (k0 + NR + j < nc) {
+        wait_vmcnt<0>();
+        consume(j, ring[j]);
+      }
+    wait_vmcnt<0>();
+    if (cc + 64 < ns_w) load_tv(cc + 64, tv_next);
+  }
+
+  // ---- combine the waves: maxima and sums, then the accumulators ----
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    if constexpr (KV == PKV_I8) {   // biased codes: subtract 1152 * (column's sum of P')
+      const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum[nb]),
+                                                       __float_as_uint(psum[nb]), false, false);
+      const float bias = kI8Bias * (__uint_as_float(ps[0]) + __uint_as_float(ps[1]));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[nb][t] -= bias;
+    }
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[nb]),
+                                                    __float_as_uint(l[nb]), false, false);
+    l[nb] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    if (h == 0) {
+      lds_m[w][32 * nb + n] = m[nb];
+      lds_l[w][32 * nb + n] = l[nb];
+    }
+  }
+  __syncthreads();
+  float Mx[NB2], den[NB2];
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    const int col = 32 * nb + n;
+    float M = lds_m[0][col];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, lds_m[ww][col]);
+    float z = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = lds_m[ww][col];
+      z += mw == -INFINITY ? 0.0f : exp2f(mw - M) * lds_l[ww][col];
+    }
+    Mx[nb] = M;
+    den[nb] = z;
+    const float f = m[nb] == -INFINITY ? 0.0f : exp2f(m[nb] - M);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[nb][t] *= f;
+  }
+  // every wave's scaled accumulators to LDS, then wave w reduces and writes
+  // the output rows 8w + 4h .. 8w + 4h + 3 of every tile (elements 4w .. 4w+3)
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) lds_acc[w][nb][t][lane] = acc[nb][t];
+  __syncthreads();
+  const int jj = w;          // row group of this wave
+  const int r0 = 8 * jj + 4 * h;
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb) {
+    if (!col_ok[nb]) continue;
+    const size_t row =
+        ((size_t)col_seq[nb] * H + col_head[nb]) * p.ws_stride + p.ws_pre + part;
+    float inv = 1.0f / den[nb];
+    if constexpr (QUANT) inv *= (1.0f / kPvBoost);
+    float *dst = p.ws_o + row * D;
+    f4 o[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f4 a = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float *src = reinterpret_cast<const float *>(&lds_acc[ww][nb][t][lane]) + 4 * jj;
+        a += *reinterpret_cast<const f4 *>(src);
+      }
+      o[t] = a * inv;
+    }
+    // element 4j + v of tile t is row 8j + 4h + v:
+    //   2-byte V, t = 2G + parity: dim 2(32G + row) + parity
+    //   1-byte V, t = e:           dim 4 row + e
+    if constexpr (QUANT) {
+      if (!(D == 64 && r0 >= 16)) {   // rows past the 16 dim groups of D = 64
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<f4 *>(dst + 4 * (r0 + v)) = f4{o[0][v], o[1][v], o[2][v], o[3][v]};
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        float *d0 = dst + 2 * (32 * gg + r0);
+        *reinterpret_cast<f4 *>(d0) =
+            f4{o[2 * gg][0], o[2 * gg + 1][0], o[2 * gg][1], o[2 * gg + 1][1]};
+        *reinterpret_cast<f4 *>(d0 + 4) =
+            f4{o[2 * gg][2], o[2 * gg + 1][2], o[2 * gg][3], o[2 * gg + 1][3]};
+      }
+    }
+    if (w == 0 && h == 0) p.ws_lse[row] = Mx[nb] + log2f(den[nb]);
+  }
+}
+
 template <int KV, int D, int BS>
 hipError_t launch_prefix_typed(const PrefixParams &p, hipStream_t stream) {
-  constexpr int C = KV == PKV_F32 ? 2 : 4;
-  hipLaunchKernelGGL((prefix_kernel<KV, D, BS, C>), dim3((unsigned)prefix_grid(p)),
-                     dim3(64 * kWaves), 0, stream, p);
+  if constexpr (KV == PKV_F32)
+    hipLaunchKernelGGL((prefix_kernel<KV, D, BS, 2>), dim3((unsigned)prefix_grid(p)),
+                       dim3(64 * kWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefix32_kernel<KV, D, BS>), dim3((unsigned)prefix_grid(p)),
+                       dim3(64 * kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
