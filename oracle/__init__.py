@@ -174,3 +174,32 @@ def decode(pools: Pools, q, block_tables, seq_lens, scale: float, num_threads: i
     if used < 0:
         raise ValueError("oracle decode: invalid shape")
     return out, used
+
+
+def prefill(pools: Pools, q, block_tables, seq_lens, q_offsets, scale: float,
+            num_threads: int = 0):
+    """fp64 attention of multi-token queries over the paged cache (prefill and
+    chunked prefill: the new tokens' K/V are in the cache already).  Sequence
+    s has the q_offsets[s+1] - q_offsets[s] query rows q_offsets[s] ..; they
+    are the last of its seq_lens[s] tokens, so query i sits at position
+    P = seq_lens[s] - q_len + i.  It attends over tokens 0 .. P: the cached
+    context and the new tokens up to itself (causal within the new tokens,
+    "KVcache-learning", s01 and s04; the paged layout does not change the
+    math, jsqmd.com section 9).  Each query row is therefore one decode row
+    over the first P + 1 tokens of its sequence's table.  q [T, H, D];
+    returns (out float64 [T, H, D], threads used)."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.asarray(seq_lens, np.int64)
+    offs = np.asarray(q_offsets, np.int64)
+    S = len(lens)
+    assert offs.shape == (S + 1,) and bt.shape[0] == S
+    T = int(offs[-1])
+    rows = np.empty((T, bt.shape[1]), np.int32)
+    rlen = np.empty(T, np.int32)
+    for s in range(S):
+        n = int(offs[s + 1] - offs[s])
+        assert 0 <= n <= lens[s]
+        for i in range(n):
+            rows[offs[s] + i] = bt[s]
+            rlen[offs[s] + i] = lens[s] - n + i + 1
+    return decode(pools, q, rows, rlen, scale, num_threads)

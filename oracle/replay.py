@@ -11,7 +11,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import Pools, copy_blocks, decode, write
+from . import Pools, copy_blocks, decode, prefill, write
 from .allocator_model import BlockManagerModel
 
 
@@ -86,4 +86,11 @@ def replay(w, sentinel=Pools.SENTINEL) -> OracleReplay:
 def oracle_output(r: OracleReplay, w, num_threads: int = 0):
     out, used = decode(r.pools, r.q, r.block_tables, r.seq_lens, np.float32(w.scale),
                        num_threads=num_threads)
+    return out
+
+
+def oracle_prefill_output(r: OracleReplay, w, num_threads: int = 0):
+    """Multi-token queries of workload w (w.q_lens set) over the replayed cache."""
+    out, used = prefill(r.pools, r.q, r.block_tables, r.seq_lens, w.q_offsets(),
+                        np.float32(w.scale), num_threads=num_threads)
     return out

@@ -58,6 +58,7 @@ class Workload:
     content_owner: dict = field(default_factory=dict)  # seq -> list of (pos_lo, pos_hi, owner)
     description: str = ""
     memo: dict | None = None          # set to {} to keep generated K/V rows for reuse
+    q_lens: list | None = None        # multi-token queries: query tokens per decode sequence
 
     @property
     def num_seqs(self) -> int:
@@ -70,9 +71,15 @@ class Workload:
     def query(self) -> np.ndarray:
         """q for the decode batch, [num_seqs, num_heads, head_dim]."""
         key = stream_key(self.seed, "q")
-        n = self.num_seqs * self.num_heads * self.head_dim
-        q = normal(key, 0, n).reshape(self.num_seqs, self.num_heads, self.head_dim)
+        rows = self.num_seqs if self.q_lens is None else int(sum(self.q_lens))
+        n = rows * self.num_heads * self.head_dim
+        q = normal(key, 0, n).reshape(rows, self.num_heads, self.head_dim)
         return q.astype(NP_DTYPE[self.q_dtype])
+
+    def q_offsets(self) -> np.ndarray:
+        """Multi-token queries: first query row of each decode sequence, and the total."""
+        assert self.q_lens is not None
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
 
     def kv_rows(self, which: str, owner: int, start: int, count: int) -> np.ndarray:
         """K ('k') or V ('v') values of positions [start, start+count) owned by `owner`,
@@ -262,6 +269,31 @@ def forked_groups(name: str, groups, singles=(), suffix_lo: int = 1, suffix_hi: 
         num_blocks=num_blocks, free_order=permutation(stream_key(seed, "free_order"), num_blocks),
         ops=ops, decode_seqs=decode, max_blocks_per_seq=-(-max_len // 16), seed=seed,
         content_owner=owner, description="forked shared prefixes and independent sequences")
+
+
+def chunked_prefill(name: str = "chunked_prefill", contexts=(1536,) * 8, chunks=(512,) * 8,
+                    H: int = 64, Hkv: int = 8, D: int = 128, cache_dtype: str = "f16",
+                    seed: int = 31) -> Workload:
+    """Multi-token queries over the paged cache: sequence i holds contexts[i]
+    cached tokens followed by a chunk of chunks[i] new tokens, all written to
+    the cache; the chunk's tokens are the queries (chunks[i] = contexts[i] +
+    chunks[i] is a whole prefill, chunks[i] = 1 a decode step)."""
+    seed = _cfg_seed(960) + seed
+    ops, decode, lens = [], [], []
+    for i, (c, n) in enumerate(zip(contexts, chunks)):
+        L = int(c) + int(n)
+        ops += [("allocate", i + 1, L), ("write", i + 1, 0, L)]
+        decode.append(i + 1)
+        lens.append(L)
+    num_blocks = sum(-(-L // 16) for L in lens) + 16
+    q_dtype = "f32" if cache_dtype == "f32" else "f16"
+    return Workload(
+        name=name, num_heads=H, num_kv_heads=Hkv, head_dim=D, q_dtype=q_dtype,
+        src_dtype=q_dtype, cache_dtype=cache_dtype,
+        out_dtype="f32" if cache_dtype == "f32" else "f16", scale=1.0 / math.sqrt(D),
+        num_blocks=num_blocks, free_order=permutation(stream_key(seed, "free_order"), num_blocks),
+        ops=ops, decode_seqs=decode, max_blocks_per_seq=-(-max(lens) // 16), seed=seed,
+        q_lens=[int(n) for n in chunks], description="chunked prefill over the paged cache")
 
 
 def custom(name: str, lens, H: int, Hkv: int, D: int, cache_dtype: str = "f16",
