@@ -54,6 +54,8 @@ def _workloads():
         "c5": (lambda r: W.c5_shared_prefix(), 2, 8192),
         "c5_cow": (lambda r: W.c5_shared_prefix(cow_pairs=True), 2, 8192),
         "c1": (lambda r: W.c1_tiny(), 1, None),
+        # multi-token queries: 8 x (1536 cached + 512 new tokens), bench_prefill
+        "prefill": (lambda r: W.chunked_prefill(), 1, None),
     }
 
 
@@ -256,8 +258,9 @@ def summarize_trace(workload, trace_csv, stats_csv, commands):
         short = short.split("(pkv::")[0]
         agg[(short, r["Grid_Size_X"], r["Grid_Size_Y"])].append(
             int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    out = [f"# rocprofv3 kernel trace summary, workload {workload} (one fused decode step per "
-           f"launch of decode_kernel with step on; merge_kernel when split)",
+    out = [f"# rocprofv3 kernel trace summary, workload {workload}: kernels of the library "
+           f"(decode_kernel<KV, D, OUT, SRC, BS>: SRC >= 0 is the fused step, -1 the plain "
+           f"decode; prefix32_kernel<KV, D, BS, MODE, OUT>: MODE 0 shared prefix, 1 prefill)",
            "# commands (run from the repository root on the GPU host):"]
     out += [f"#   {c}" for c in commands]
     out.append(f"# source={decode_source_hash()}  (hash of the decode sources)")
@@ -272,10 +275,127 @@ def summarize_trace(workload, trace_csv, stats_csv, commands):
         if len(v) >= 5:
             out.append(f"{k[0]:44s} {k[1]:>9s} {k[2]:>6s} {len(v):6d} {sum(v) / len(v) / 1e3:9.2f} "
                        f"{min(v) / 1e3:9.2f} {max(v) / 1e3:9.2f}")
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_kernel_trace.txt")
+    name = f"{workload}_kernel_trace.txt" if workload == "prefill" else \
+        f"decode_{workload}_kernel_trace.txt"
+    path = os.path.join(ROOT, "profiles", name)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     open(path, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
+    return 0
+
+
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+
+
+def prefill_flops(w) -> float:
+    """q.K and P.V flops of one multi-token-query call: query i of a chunk of
+    n at the end of L tokens sees L - n + i + 1 of them."""
+    tot = 0
+    lens = [op[2] for op in w.ops if op[0] == "allocate"]
+    for L, n in zip(lens, w.q_lens):
+        tot += sum(L - n + i + 1 for i in range(n))
+    return 4.0 * w.head_dim * w.num_heads * tot
+
+
+def bench_prefill(args, torch, pkv, driver) -> int:
+    """A chunked-prefill step: the chunk's K/V written into its slots
+    (paged_kv_write) and its queries' causal attention over the cache
+    (paged_attention_prefill), captured in a graph."""
+    from synth import workloads as W
+    w = W.chunked_prefill()
+    if args.block_size != 16:
+        w = W.with_block_size(w, args.block_size)
+    K, Wm = args.steps, args.warmup
+    part = 0 if args.partition < 0 else args.partition
+    r = driver.replay(w)
+    T = sum(w.q_lens)
+    offs = w.q_offsets()
+    # the chunk tokens' slots and values (rewritten by every step)
+    slots, ks, vs = [], [], []
+    for sidx, seq in enumerate(w.decode_seqs):
+        L = int(r.lens_host[sidx])
+        n = w.q_lens[sidx]
+        slots.append(r.alloc.slots(seq, L - n, n))
+        ks.append(w.kv_rows("k", seq, L - n, n))
+        vs.append(w.kv_rows("v", seq, L - n, n))
+    slot_t = torch.from_numpy(np.concatenate(slots)).cuda()
+    k_t = torch.from_numpy(np.concatenate(ks)).cuda()
+    v_t = torch.from_numpy(np.concatenate(vs)).cuda()
+    out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.float16, device="cuda")
+    off_t = torch.from_numpy(offs).cuda()
+    scale = float(np.float32(w.scale))
+    maxq = max(w.q_lens)
+    need = pkv.prefill_workspace_bytes(w.num_seqs, T, maxq, w.num_heads, w.num_kv_heads,
+                                       w.head_dim, w.max_blocks_per_seq, part, w.block_size)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+
+    def attn():
+        pkv.paged_attention_prefill(r.query, r.cache, r.block_tables, r.seq_lens, off_t, scale,
+                                    maxq, out=out, partition_size=part, workspace=ws)
+
+    def step():
+        pkv.paged_kv_write(k_t, v_t, slot_t, r.cache)
+        attn()
+
+    def timed(fn, n):
+        for _ in range(Wm):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    step_ms = timed(step, K)
+    attn_ms = timed(attn, K)
+    fl = prefill_flops(w)
+    achieved = fl / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": "paged prefill attention TFLOP/s (chunked prefill over the paged cache)",
+        "value": round(fl / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": Wm, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.cache_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "query_tokens": T,
+                   "context_plus_chunk": int(r.lens_host.max()), "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "kv_dtype": w.cache_dtype,
+                   "partition_size": part, "graph": True},
+        "tokens_per_s": round(T / (step_ms * 1e-3), 1),
+        "attention_ms": round(attn_ms, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": fl},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle.replay import replay as oracle_replay
+        ro = oracle_replay(w)
+        # sample: the last query rows of the first sequence (the longest views)
+        n = 8
+        L = int(ro.seq_lens[0])
+        rows = np.arange(offs[1] - n, offs[1])
+        lens = np.array([L - w.q_lens[0] + (rw - offs[0]) + 1 for rw in rows], np.int32)
+        tables = np.repeat(ro.block_tables[:1], n, axis=0)
+        t0, reps, used = time.perf_counter(), 0, 1
+        while time.perf_counter() - t0 < args.cpu_budget:
+            _, used = oracle.decode(ro.pools, ro.q[rows], tables, lens, np.float32(w.scale))
+            reps += 1
+        dt = time.perf_counter() - t0
+        fl_s = 4.0 * w.head_dim * w.num_heads * float(lens.sum()) * reps
+        result["cpu_baseline"] = {"value": round(fl_s / dt / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": int(used), "kind": "oracle",
+                                  "sample": f"{n} query rows of sequence 0 (views of {lens.min()}-"
+                                            f"{lens.max()} tokens), {reps} passes in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
     return 0
 
 
@@ -316,7 +436,8 @@ def main():
     if args.summarize_traffic:
         return summarize_traffic(args.workload, *args.summarize_traffic, args.command)
     if args.summarize_trace:
-        return summarize_trace(args.workload, *args.summarize_trace, args.command)
+        wl = args.workload + ("_shared" if args.shared else "")
+        return summarize_trace(wl, *args.summarize_trace, args.command)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
               f"multi-GPU path.", file=sys.stderr)
@@ -333,6 +454,8 @@ def main():
     torch.cuda.set_device(0)
     if args.pmc_copy:
         return pmc_copy()
+    if args.workload == "prefill":
+        return bench_prefill(args, torch, pkv, driver)
     factory, replicas, pool = _workloads()[args.workload]
     R = args.replicas or replicas
     bs = args.block_size

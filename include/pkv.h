@@ -372,6 +372,45 @@ int paged_attention_decode_shared(void *out, int32_t out_dtype, const void *quer
                                   int32_t partition_size, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* Multi-token queries over the paged cache (prefill and chunked prefill):
+ * sequence s has the query rows query_offsets[s] .. query_offsets[s+1] - 1
+ * (q_len of them); they are the last q_len of its seq_lens[s] tokens, whose
+ * K/V are already in the cache (paged_kv_write first).  Query i sits at
+ * position P = seq_lens[s] - q_len + i and attends over tokens 0 .. P -- the
+ * cached context and the new tokens up to itself [fairy, s01 attention, s04
+ * incremental generation; prefill then decode, 7yue, section 1]:
+ *   out[query_offsets[s] + i][h] = softmax_{t <= P}(scale * q . K_t) V_t
+ *   out:     device [num_query_tokens][num_heads][head_dim], F32 or F16.
+ *   query:   device [num_query_tokens][num_heads][head_dim], F16, 16-byte aligned.
+ *   query_offsets: device int32 [num_seqs + 1], non-decreasing, last =
+ *            num_query_tokens; q_len <= seq_lens[s] and <= max_query_len (host
+ *            bound that sizes the launch; rows of longer queries are not
+ *            written).
+ *   cache_dtype F16, I8 or E4M3 (the pass runs on fp16 MFMAs; F32 caches give
+ *   PKV_ENOTSUP); head_dim 64 or 128; block_size 8, 16 or 32.
+ *   partition_size: tokens per partition of the keys (a multiple of 32 and
+ *            of block_size; 0 = library choice: one pass per (sequence, kv
+ *            head, 64 query columns) unless that leaves compute units idle).
+ *            With several partitions the partial results go through the
+ *            workspace and a log-sum-exp merge.
+ *   workspace: >= paged_attention_prefill_workspace_bytes(...) bytes (0 with
+ *            one partition), 256-byte aligned.
+ * Arithmetic and errors as paged_attention_decode. */
+size_t paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens,
+                                               int32_t max_query_len, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_blocks_per_seq, int32_t block_size,
+                                               int32_t partition_size);
+int paged_attention_prefill(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                            const void *k_cache, const void *v_cache, const void *k_scale,
+                            const void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, const int32_t *query_offsets,
+                            int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, float scale, int32_t partition_size,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* ========================================================================
  * Bandwidth diagnostics (measurement helpers, not part of the method)
  *

@@ -33,6 +33,7 @@ EXPORTS = [
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_decode_step",
     "paged_attention_shared_workspace_bytes", "paged_attention_decode_shared",
+    "paged_attention_prefill_workspace_bytes", "paged_attention_prefill",
     "pkv_stream_read", "pkv_stream_copy",
 ]
 
@@ -98,6 +99,11 @@ def lib() -> ctypes.CDLL:
             "paged_attention_decode_shared": ([P, i32, P, i32, P, P, i32, P, P, P, P, P, i32,
                                                i32, P, i32, P, i32, i32, i32, i32, i32, f32, P,
                                                i32, P, sz, P], ctypes.c_int),
+            "paged_attention_prefill_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32,
+                                                         i32, i32], sz),
+            "paged_attention_prefill": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32, P, P, i32,
+                                         i32, i32, i32, i32, i32, i32, f32, i32, P, sz, P],
+                                        ctypes.c_int),
             "pkv_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
             "pkv_stream_copy": ([P, P, sz, i32, P], ctypes.c_int),
         }
@@ -583,6 +589,60 @@ def paged_attention_decode_shared(query, cache: PagedKVCache, block_tables, seq_
         _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
         cache.block_size, float(scale), ctypes.byref(groups.c), partition_size, ws_ptr, ws_len,
         _stream_ptr(stream)), "paged_attention_decode_shared")
+    return out
+
+
+def prefill_workspace_bytes(num_seqs: int, num_query_tokens: int, max_query_len: int,
+                            num_heads: int, num_kv_heads: int, head_dim: int,
+                            max_blocks_per_seq: int, partition_size: int = 0,
+                            block_size: int = BLOCK_SIZE) -> int:
+    return lib().paged_attention_prefill_workspace_bytes(
+        num_seqs, num_query_tokens, max_query_len, num_heads, num_kv_heads, head_dim,
+        max_blocks_per_seq, block_size, partition_size)
+
+
+def paged_attention_prefill(query, cache: PagedKVCache, block_tables, seq_lens, query_offsets,
+                            scale: float, max_query_len: int, out=None, out_dtype=None,
+                            partition_size: int = 0, workspace=None, stream=None):
+    """Multi-token queries (prefill / chunked prefill): query rows
+    query_offsets[s] .. query_offsets[s+1]-1 are the last tokens of sequence
+    s (already in the cache) and attend causally over its cached tokens."""
+    torch = _torch()
+    T, H, D = query.shape
+    if query.dtype != torch.float16:
+        raise ValueError("query must be float16")
+    S = block_tables.shape[0]
+    if block_tables.dim() != 2 or seq_lens.numel() < S or query_offsets.numel() < S + 1:
+        raise ValueError("block_tables [S, max_blocks], seq_lens [S], query_offsets [S+1]")
+    maxb = block_tables.shape[1]
+    if out is None:
+        odt = out_dtype if out_dtype is not None else torch.float16
+        out = torch.empty((T, H, D), dtype=odt, device=query.device)
+    o_dt = {torch.float32: F32, torch.float16: F16}.get(out.dtype)
+    if o_dt is None or tuple(out.shape) != (T, H, D):
+        raise ValueError("out must be float32/float16 [num_query_tokens, num_heads, head_dim]")
+    if D != cache.head_dim or H % cache.num_kv_heads:
+        raise ValueError("query shape does not match the cache")
+    need = prefill_workspace_bytes(S, T, max_query_len, H, cache.num_kv_heads, D, maxb,
+                                   partition_size, cache.block_size)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr, ws_len = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", numel=need)
+        ws_len = workspace.numel() * workspace.element_size()
+    nbytes = cache_bytes(cache.num_blocks, cache.num_kv_heads, D, cache.cache_dtype,
+                         cache.block_size)
+    ks, vs = cache._scales()
+    _check(lib().paged_attention_prefill(
+        _dev(out, "out"), o_dt, _dev(query, "query"), F16,
+        _dev(cache.k, "k_cache", numel=nbytes), _dev(cache.v, "v_cache", numel=nbytes), ks, vs,
+        cache.cache_dtype, cache.num_blocks,
+        _dev(block_tables, "block_tables", torch.int32, S * maxb), maxb,
+        _dev(seq_lens, "seq_lens", torch.int32, S),
+        _dev(query_offsets, "query_offsets", torch.int32, S + 1), S, T, int(max_query_len), H,
+        cache.num_kv_heads, D, cache.block_size, float(scale), partition_size, ws_ptr, ws_len,
+        _stream_ptr(stream)), "paged_attention_prefill")
     return out
 
 

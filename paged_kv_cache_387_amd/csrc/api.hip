@@ -1,5 +1,6 @@
 // C ABI of libpkv: argument validation and dispatch to the gfx950 kernels.
 // Every check runs on the host before anything is enqueued.
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -132,6 +133,46 @@ PrefixPlan plan_prefix(const pkv_prefix_groups *gr, int32_t num_heads, int32_t n
   return pl;
 }
 
+// Multi-token queries: partitions of the table's tokens.  One pass per
+// (sequence, kv head, 64-column block) when there are enough of them for the
+// compute units, else partitions of at least 32 tiles; explicit sizes must
+// be whole 32-token steps and whole blocks.
+constexpr int kPrefillCols = 64;
+
+struct PrefillPlan {
+  int64_t col_blocks = 0;
+  int32_t pp_tiles = 0, num_pparts = 0;
+};
+
+bool valid_prefill_partition(int32_t tokens, int32_t block_size) {
+  const int32_t unit = block_size > 32 ? block_size : 32;
+  return tokens >= 0 && tokens % unit == 0;
+}
+
+PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t max_query_len, int32_t max_blocks, int32_t block_size,
+                         int32_t requested) {
+  PrefillPlan pl;
+  const int64_t cols = (int64_t)max_query_len * (num_heads / num_kv_heads);
+  pl.col_blocks = (cols + kPrefillCols - 1) / kPrefillCols;
+  const int64_t tiles = max_tiles_of(max_blocks, block_size);
+  int64_t pt;
+  if (requested > 0) {
+    pt = requested / kTile;
+  } else {
+    const int64_t wgs = (int64_t)num_seqs * num_kv_heads * pl.col_blocks;
+    int64_t parts = (kPrefixTargetWgs + wgs - 1) / (wgs > 0 ? wgs : 1);
+    const int64_t max_parts = (tiles + 31) / 32;
+    parts = parts < 1 ? 1 : (parts > max_parts ? max_parts : parts);
+    pt = (tiles + parts - 1) / parts;
+    pt = (pt + 7) / 8 * 8;
+  }
+  if (pt >= tiles) pt = (tiles + 1) / 2 * 2;   // one partition (whole steps)
+  pl.pp_tiles = (int32_t)pt;
+  pl.num_pparts = (int32_t)((tiles + pt - 1) / pt);
+  return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,6 +212,22 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
   const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
   const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
   return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
+}
+
+size_t paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens,
+                                               int32_t max_query_len, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_blocks_per_seq, int32_t block_size,
+                                               int32_t partition_size) {
+  if (num_seqs <= 0 || num_query_tokens <= 0 || max_query_len <= 0 || num_heads <= 0 ||
+      num_kv_heads <= 0 || num_heads % num_kv_heads || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || !valid_block_size(block_size) ||
+      !valid_prefill_partition(partition_size, block_size))
+    return 0;
+  const PrefillPlan pl = plan_prefill(num_seqs, num_heads, num_kv_heads, max_query_len,
+                                      max_blocks_per_seq, block_size, partition_size);
+  if (pl.num_pparts <= 1) return 0;
+  return workspace_layout(num_query_tokens, num_heads, head_dim, pl.num_pparts).total;
 }
 
 size_t paged_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads,
@@ -423,6 +480,84 @@ int paged_attention_decode_shared(void *out, int32_t out_dtype, const void *quer
   err = launch_prefix(pp, cache_dtype, head_dim, block_size, s);
   if (err != hipSuccess) return status_of(err);
   return status_of(launch_merge(p, out_dtype, head_dim, s));
+}
+
+int paged_attention_prefill(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,
+                            const void *k_cache, const void *v_cache, const void *k_scale,
+                            const void *v_scale, int32_t cache_dtype, int32_t num_blocks,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, const int32_t *query_offsets,
+                            int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, float scale, int32_t partition_size,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0)
+    return PKV_EINVAL;
+  if (num_heads % num_kv_heads) return PKV_EINVAL;
+  if (!valid_block_size(block_size)) return PKV_ENOTSUP;
+  if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return PKV_ENOTSUP;
+  if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
+  if (cache_dtype == PKV_F32) return PKV_ENOTSUP;   // the pass runs on fp16 MFMAs
+  if (out_dtype != PKV_F32 && out_dtype != PKV_F16) return PKV_EINVAL;
+  if (q_dtype != PKV_F16) return PKV_ENOTSUP;
+  if (!valid_prefill_partition(partition_size, block_size)) return PKV_EINVAL;
+  if (!(scale == scale)) return PKV_EINVAL;
+  if (num_seqs == 0 || num_query_tokens == 0) return PKV_OK;
+  if (max_query_len <= 0) return PKV_EINVAL;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens || !query_offsets)
+    return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 4 * elem_bytes(out_dtype)) || !aligned(block_tables, 4) ||
+      !aligned(seq_lens, 4) || !aligned(query_offsets, 4))
+    return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!aligned(k_scale, 4) || !aligned(v_scale, 4))) return PKV_EINVAL;
+  const PrefillPlan pl = plan_prefill(num_seqs, num_heads, num_kv_heads, max_query_len,
+                                      max_blocks_per_seq, block_size, partition_size);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  if ((int64_t)num_query_tokens * num_heads > INT32_MAX || units > INT32_MAX ||
+      (int64_t)unit_groups((int)std::min<int64_t>(units, INT32_MAX)) * kXcds * pl.col_blocks *
+              pl.num_pparts > INT32_MAX)
+    return PKV_ENOTSUP;
+  WorkspaceLayout wl{0, 0, 0};
+  if (pl.num_pparts > 1) {
+    wl = workspace_layout(num_query_tokens, num_heads, head_dim, pl.num_pparts);
+    if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return PKV_EINVAL;
+  }
+  const int dev = check_device();
+  if (dev != PKV_OK) return dev;
+  PrefixParams pp{};
+  pp.q = query;
+  pp.k_cache = static_cast<const uint8_t *>(k_cache);
+  pp.v_cache = static_cast<const uint8_t *>(v_cache);
+  pp.k_scale = static_cast<const uint16_t *>(k_scale);
+  pp.v_scale = static_cast<const uint16_t *>(v_scale);
+  char *ws = static_cast<char *>(workspace);
+  pp.ws_o = wl.total ? reinterpret_cast<float *>(ws + wl.o_off) : nullptr;
+  pp.ws_lse = wl.total ? reinterpret_cast<float *>(ws + wl.lse_off) : nullptr;
+  pp.num_blocks = num_blocks;
+  pp.num_seqs = num_seqs;
+  pp.num_heads = num_heads;
+  pp.num_kv_heads = num_kv_heads;
+  pp.group = num_heads / num_kv_heads;
+  pp.num_units = (int)units;
+  pp.col_blocks = (int)pl.col_blocks;
+  pp.pp_tiles = pl.pp_tiles;
+  pp.num_pparts = pl.num_pparts;
+  pp.ws_stride = pl.num_pparts;
+  pp.ws_pre = 0;
+  pp.qk_scale = scale * 1.4426950408889634f;
+  pp.block_tables = block_tables;
+  pp.seq_lens = seq_lens;
+  pp.query_offsets = query_offsets;
+  pp.max_blocks = max_blocks_per_seq;
+  pp.num_query_tokens = num_query_tokens;
+  pp.block_size = block_size;
+  pp.out = out;
+  return status_of(launch_prefill(pp, cache_dtype, out_dtype, head_dim, block_size,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 int paged_kv_write(const void *key, const void *value, int32_t src_dtype, int64_t key_stride,

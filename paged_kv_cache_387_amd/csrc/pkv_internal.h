@@ -99,6 +99,16 @@ struct PrefixParams {
   int ws_stride;
   int ws_pre;
   float qk_scale;
+  // Multi-token queries (prefill mode of the same pass): unit = (sequence,
+  // kv head); sequence s has query rows query_offsets[s] .. query_offsets[s+1]
+  // - 1, the last of its seq_lens[s] tokens, each attending causally.
+  const int32_t *block_tables;   // [num_seqs][max_blocks]
+  const int32_t *seq_lens;
+  const int32_t *query_offsets;  // [num_seqs + 1]
+  int max_blocks;
+  int num_query_tokens;
+  int block_size;
+  void *out;                     // written directly when num_pparts == 1
 };
 
 // Prefix partials of sequence s (0: none).  Used identically by the decode
@@ -170,6 +180,9 @@ inline int64_t prefix_grid(const PrefixParams &p) {
 hipError_t launch_prefix(const PrefixParams &p, int cache_dtype, int head_dim, int block_size,
                          hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream);
+// Multi-token queries: the pass (and, with several partitions, the merge).
+hipError_t launch_prefill(const PrefixParams &p, int cache_dtype, int out_dtype, int head_dim,
+                          int block_size, hipStream_t stream);
 
 hipError_t launch_write(const WriteParams &p, int src_dtype, int cache_dtype, int head_dim,
                         hipStream_t stream);

@@ -553,7 +553,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
 //        for the even dims and one for the odd dims of each G.  1-byte V:
 //        group = 4 tokens x dims 4m .. 4m+3: one MFMA per dim offset e.
 // K, V (and quantized-cache scales) go straight into a per-wave LDS ring.
-template <int KV, int D, int BS>
+// MODE kModeShared: units are (group, kv head), columns the members' query
+// heads, the whole prefix visible, partials out.  MODE kModePrefill: units
+// are (sequence, kv head), columns its query tokens' heads with causal
+// limits; `out` (of type OUT) is written directly when there is one
+// partition, else partials.
+constexpr int kModeShared = 0;
+constexpr int kModePrefill = 1;
+
+template <int KV, int D, int BS, int MODE, int OUT>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p) {
   constexpr int EB = Kv<KV>::EB;
   constexpr bool QUANT = EB == 1;
@@ -598,28 +606,52 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
   const int cb = rem / ugroups;
   const int u = (rem - cb * ugroups) * kXcds + bid % kXcds;
   if (u >= p.num_units || part >= p.num_pparts) return;
-  const int grp = u / p.num_kv_heads;
+  const int grp = u / p.num_kv_heads;         // group, or sequence
   const int kvh = u - grp * p.num_kv_heads;
   const int G = p.group;
   const int H = p.num_heads;
+  constexpr bool PREFILL = MODE == kModePrefill;
 
-  int off = p.offsets[grp];
-  int end = p.offsets[grp + 1];
-  off = off < 0 ? 0 : (off > p.num_members ? p.num_members : off);
-  end = end < off ? off : (end > p.num_members ? p.num_members : end);
-  const int ncols = (end - off) * G;
+  // columns (and, prefill, the tokens of data and the causal limits)
+  int off, end, ltok;
+  const int32_t *trow;
+  int tlim;
+  if constexpr (PREFILL) {
+    off = p.query_offsets[grp];
+    end = p.query_offsets[grp + 1];
+    off = off < 0 ? 0 : (off > p.num_query_tokens ? p.num_query_tokens : off);
+    end = end < off ? off : (end > p.num_query_tokens ? p.num_query_tokens : end);
+    ltok = p.seq_lens[grp];
+    ltok = ltok < 0 ? 0 : (ltok > p.max_blocks * BS ? p.max_blocks * BS : ltok);
+    if (end - off > ltok) end = off + ltok;   // queries are the sequence's last tokens
+    trow = p.block_tables + (size_t)grp * p.max_blocks;
+    tlim = p.max_blocks;
+  } else {
+    off = p.offsets[grp];
+    end = p.offsets[grp + 1];
+    off = off < 0 ? 0 : (off > p.num_members ? p.num_members : off);
+    end = end < off ? off : (end > p.num_members ? p.num_members : end);
+    int plen = p.prefix_lens[grp];
+    plen = plen < 0 ? 0 : (plen > p.max_prefix_blocks * BS ? p.max_prefix_blocks * BS : plen);
+    ltok = plen / kTile * kTile;
+    trow = p.tables + (size_t)grp * p.max_prefix_blocks;
+    tlim = p.max_prefix_blocks;
+  }
+  const int nq = end - off;
+  const int ncols = nq * G;
   const int c0 = cb * CW;
   if (c0 >= ncols) return;
-
-  int plen = p.prefix_lens[grp];
-  plen = plen < 0 ? 0 : (plen > p.max_prefix_blocks * BS ? p.max_prefix_blocks * BS : plen);
-  const int ntile = plen / kTile;
+  // Prefill: query i (column c, i = c / G) sees tokens < ltok - nq + i + 1.
+  // The workgroup's columns span limits lim_lo .. lim_hi; tokens at or past
+  // lim_hi are never needed.
+  const int lim_lo = PREFILL ? ltok - nq + c0 / G + 1 : ltok;
+  const int lim_hi = PREFILL ? ltok - nq + min(nq - 1, (c0 + CW - 1) / G) + 1 : ltok;
+  const int ntile = (lim_hi + kTile - 1) / kTile;
   const int first = part * p.pp_tiles;        // even: pp_tiles is a multiple of 8
   if (first >= ntile) return;
   const int last = min(first + p.pp_tiles, ntile);
   const int nsteps = (last - first + 1) / 2;  // the last may hold one tile
   const int ns_w = nsteps > w ? (nsteps - w + kWaves - 1) / kWaves : 0;
-  const int32_t *trow = p.tables + (size_t)grp * p.max_prefix_blocks;
   // The column blocks of one partition read the same tiles: each starts its
   // walk at a different step, so that they do not request the same lines of
   // the same L2 channels at the same time (walks of up to 64 steps).
@@ -630,24 +662,31 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
   auto load_tv = [&](int c, int *tv) {
     const int step = w + walk(c + lane < ns_w ? c + lane : 0) * kWaves;
     const int e0 = (first / 2 + step) * TPS;
-    const int lim = p.max_prefix_blocks;
 #pragma unroll
-    for (int e = 0; e < TPS; ++e) tv[e] = trow[e0 + e < lim ? e0 + e : lim - 1];
+    for (int e = 0; e < TPS; ++e) tv[e] = trow[e0 + e < tlim ? e0 + e : tlim - 1];
   };
   int tv_next[TPS];
   load_tv(0, tv_next);
 
-  // Query columns: column c0 + 32*nb + n is head kvh*G + (c % G) of member c / G.
-  int col_seq[NB2], col_head[NB2];
+  // Query columns: column c0 + 32*nb + n is head kvh*G + (c % G) of member
+  // c / G (shared prefix), or of query row off + c / G (prefill); col_seq is
+  // the row of q (and of the output).  Columns past the end repeat column 0.
+  int col_seq[NB2], col_head[NB2], col_lim[NB2];
   bool col_ok[NB2];
 #pragma unroll
   for (int nb = 0; nb < NB2; ++nb) {
     const int c = c0 + 32 * nb + n;
     col_ok[nb] = c < ncols;
     const int cc = col_ok[nb] ? c : 0;
-    const int sq = p.members[off + cc / G];
-    col_ok[nb] = col_ok[nb] && (unsigned)sq < (unsigned)p.num_seqs;
-    col_seq[nb] = (unsigned)sq < (unsigned)p.num_seqs ? sq : 0;
+    if constexpr (PREFILL) {
+      col_seq[nb] = off + cc / G;
+      col_lim[nb] = ltok - nq + cc / G + 1;
+    } else {
+      const int sq = p.members[off + cc / G];
+      col_ok[nb] = col_ok[nb] && (unsigned)sq < (unsigned)p.num_seqs;
+      col_seq[nb] = (unsigned)sq < (unsigned)p.num_seqs ? sq : 0;
+      col_lim[nb] = ltok;
+    }
     col_head[nb] = kvh * G + cc % G;
   }
   // B operands: q dims of MFMA kk for lane half h (see the K order above)
@@ -698,6 +737,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
   struct Slot {
     bool ok;
     bool half;   // the step holds one tile only
+    int t0;      // first token of the step
   };
 
   // Block (and tile within the block) of token tt (0..31) of a step whose
@@ -719,11 +759,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
   };
 
   auto issue = [&](const int *tv, int j, int step_tile, int slot, Slot &sl) {
-    // entries of a missing second tile (past the prefix: padding) are
-    // replaced by the first, whose data is read in its place
+    // entries past the data (padding) are replaced by the step's first,
+    // whose data is read in their place; a missing second tile is read from
+    // the first
     sl.half = step_tile + 1 >= last;
-    constexpr int kHalf = TPS > 1 ? TPS / 2 : 1;
-    const int used = sl.half ? kHalf : TPS;
+    sl.t0 = step_tile * kTile;
+    const int left = ltok - sl.t0;   // tokens of data from the step's start
+    int used = BS >= 32 ? 1 : (left + BS - 1) / BS;
+    used = used < 1 ? 1 : (used > TPS ? TPS : used);
     int e[TPS];
     bool ok = true;
 #pragma unroll
@@ -852,13 +895,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
         }
       }
     }
+    // Prefill: steps that reach a causal limit or the end of the data mask
+    // per element (token t0 + 8j + 4h + v of element 4j + v): scores of
+    // tokens at or past the column's limit, and V (and its scales) of tokens
+    // past the data, which may be unwritten slots.
+    const bool edge = PREFILL && sl.t0 + 32 > lim_lo;
+    if (edge) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tok = sl.t0 + 16 * kc + (i < 4 ? 4 * h + i : 8 + 4 * h + (i - 4));
+          if (tok >= ltok) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) va[kc][t][i] = (_Float16)0.0f;
+          }
+        }
+      if constexpr (QUANT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (sl.t0 + 8 * (i / 4) + 4 * h + (i % 4) >= ltok) vsf[i] = 0.0f;
+      }
+    }
     // Scores.  Base-2 score x = k * s (fp16 cache: k = qk_scale for every
     // token, so the block maximum is taken on the raw s and the scale is
     // applied inside the exponent's fma; quantized caches: the per-token K
     // scale makes x explicit).
     float x[NB2][16], mn[NB2];
+    uint32_t dead[NB2];   // bit i: element i takes no part (masked token)
     bool over = false;
     const float ks = p.qk_scale;
+    const bool masked = edge || sl.half;   // wave-uniform
     // the column blocks' accumulation chains interleaved, so that consecutive
     // MFMAs do not wait on each other
     f16v scs[NB2];
@@ -872,29 +939,39 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
 #pragma unroll
     for (int nb = 0; nb < NB2; ++nb) {
       f16v &sc = scs[nb];
-      // rows 16..31 (elements 8..15) of a half step belong to the missing
-      // tile: left out of the maximum here, their weights zeroed below
-      const int nvalid = sl.half ? 8 : 16;
+      // masked elements: rows 16..31 (elements 8..15) of a half step belong
+      // to the missing tile; prefill edge steps mask tokens at or past the
+      // column's causal limit.  They are left out of the maximum, and their
+      // weights are zeroed below.
+      dead[nb] = sl.half ? 0xFF00u : 0u;
+      if (edge) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (sl.t0 + 8 * (i / 4) + 4 * h + (i % 4) >= col_lim[nb]) dead[nb] |= 1u << i;
+      }
       float bm;
       if constexpr (QUANT) {
         bm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           x[nb][i] = (KV == PKV_I8 ? sc[i] - qbias[nb] : sc[i]) * ks * ksf[i];
-          if (i < nvalid) bm = fmaxf(bm, x[nb][i]);
+          if (!masked || !((dead[nb] >> i) & 1u)) bm = fmaxf(bm, x[nb][i]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[nb][i] = sc[i];
-        float e = sc[0];
-        if (ks >= 0.0f) {   // wave-uniform: the largest score, or the smallest
+        // wave-uniform: the largest score, or the smallest (negative scale);
+        // with every element masked e stays infinite and bm is -inf (or NaN
+        // for a zero scale, which the maximum below ignores)
+        float e = ks >= 0.0f ? -INFINITY : INFINITY;
+        if (ks >= 0.0f) {
 #pragma unroll
-          for (int i = 1; i < 16; ++i)
-            if (i < nvalid) e = fmaxf(e, sc[i]);
+          for (int i = 0; i < 16; ++i)
+            if (!masked || !((dead[nb] >> i) & 1u)) e = fmaxf(e, sc[i]);
         } else {
 #pragma unroll
-          for (int i = 1; i < 16; ++i)
-            if (i < nvalid) e = fminf(e, sc[i]);
+          for (int i = 0; i < 16; ++i)
+            if (!masked || !((dead[nb] >> i) & 1u)) e = fminf(e, sc[i]);
         }
         bm = e * ks;
       }
@@ -925,9 +1002,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         pr[i] = QUANT ? fast_exp2(x[nb][i] - m[nb]) : fast_exp2(fmaf(x[nb][i], ks, -m[nb]));
-      if (sl.half) {
+      if (masked) {
 #pragma unroll
-        for (int i = 8; i < 16; ++i) pr[i] = 0.0f;
+        for (int i = 0; i < 16; ++i)
+          if ((dead[nb] >> i) & 1u) pr[i] = 0.0f;
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -1042,11 +1120,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
 #pragma unroll
   for (int nb = 0; nb < NB2; ++nb) {
     if (!col_ok[nb]) continue;
-    const size_t row =
-        ((size_t)col_seq[nb] * H + col_head[nb]) * p.ws_stride + p.ws_pre + part;
+    // prefill with a single partition writes the output row itself
+    const bool direct = PREFILL && p.num_pparts == 1;
+    const size_t orow = (size_t)col_seq[nb] * H + col_head[nb];
+    const size_t row = orow * p.ws_stride + p.ws_pre + part;
     float inv = 1.0f / den[nb];
     if constexpr (QUANT) inv *= (1.0f / kPvBoost);
-    float *dst = p.ws_o + row * D;
+    float *dst = direct ? nullptr : p.ws_o + row * D;
     f4 o[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -1061,23 +1141,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
     // element 4j + v of tile t is row 8j + 4h + v:
     //   2-byte V, t = 2G + parity: dim 2(32G + row) + parity
     //   1-byte V, t = e:           dim 4 row + e
+    // 4 consecutive output elements at element offset e0 of the row
+    auto put4 = [&](int e0, f4 v) {
+      if (direct) {
+        if constexpr (OUT == PKV_F32)
+          *reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.out) + orow * D + e0) = v;
+        else
+          *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(p.out) + orow * D + e0) =
+              h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      } else {
+        *reinterpret_cast<f4 *>(dst + e0) = v;
+      }
+    };
     if constexpr (QUANT) {
       if (!(D == 64 && r0 >= 16)) {   // rows past the 16 dim groups of D = 64
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          *reinterpret_cast<f4 *>(dst + 4 * (r0 + v)) = f4{o[0][v], o[1][v], o[2][v], o[3][v]};
+        for (int v = 0; v < 4; ++v) put4(4 * (r0 + v), f4{o[0][v], o[1][v], o[2][v], o[3][v]});
       }
     } else {
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        float *d0 = dst + 2 * (32 * gg + r0);
-        *reinterpret_cast<f4 *>(d0) =
-            f4{o[2 * gg][0], o[2 * gg + 1][0], o[2 * gg][1], o[2 * gg + 1][1]};
-        *reinterpret_cast<f4 *>(d0 + 4) =
-            f4{o[2 * gg][2], o[2 * gg + 1][2], o[2 * gg][3], o[2 * gg + 1][3]};
+        const int e0 = 2 * (32 * gg + r0);
+        put4(e0, f4{o[2 * gg][0], o[2 * gg + 1][0], o[2 * gg][1], o[2 * gg + 1][1]});
+        put4(e0 + 4, f4{o[2 * gg][2], o[2 * gg + 1][2], o[2 * gg][3], o[2 * gg + 1][3]});
       }
     }
-    if (w == 0 && h == 0) p.ws_lse[row] = Mx[nb] + log2f(den[nb]);
+    if (!direct && w == 0 && h == 0) p.ws_lse[row] = Mx[nb] + log2f(den[nb]);
   }
 }
 
@@ -1087,8 +1176,8 @@ hipError_t launch_prefix_typed(const PrefixParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((prefix_kernel<KV, D, BS, 2>), dim3((unsigned)prefix_grid(p)),
                        dim3(64 * kWaves), 0, stream, p);
   else
-    hipLaunchKernelGGL((prefix32_kernel<KV, D, BS>), dim3((unsigned)prefix_grid(p)),
-                       dim3(64 * kWaves), 0, stream, p);
+    hipLaunchKernelGGL((prefix32_kernel<KV, D, BS, kModeShared, PKV_F32>),
+                       dim3((unsigned)prefix_grid(p)), dim3(64 * kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1108,7 +1197,104 @@ hipError_t launch_prefix_d(const PrefixParams &p, int head_dim, int block_size,
                         : launch_prefix_bs<KV, 128>(p, block_size, stream);
 }
 
+// Merge of prefill partials (several partitions): a thread owns 4 elements of
+// one (query row, head) row; the row's sequence is found by bisection over
+// query_offsets, and its partitions are those that start below its causal
+// limit.  One pass over the partials with a running (max, sum, weighted sum).
+template <int D, int OUT>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefixParams p) {
+  constexpr int TPH = D / 4;
+  constexpr int RPW = 256 / TPH;
+  const int t = threadIdx.x;
+  const int rl = t / TPH, dv = t % TPH;
+  const int row = blockIdx.x * RPW + rl;
+  if (row >= p.num_query_tokens * p.num_heads) return;
+  const int qr = row / p.num_heads;
+  int lo = 0, hi = p.num_seqs;   // the last sequence whose first query row is <= qr
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.query_offsets[mid] <= qr) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  int off = p.query_offsets[s], end = p.query_offsets[s + 1];
+  off = off < 0 ? 0 : (off > p.num_query_tokens ? p.num_query_tokens : off);
+  end = end < off ? off : (end > p.num_query_tokens ? p.num_query_tokens : end);
+  int L = p.seq_lens[s];
+  L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
+  if (end - off > L) end = off + L;
+  const int i = qr - off;
+  if (i < 0 || i >= end - off) return;   // not a query row of s (the pass wrote nothing)
+  const int lim = L - (end - off) + i + 1;
+  const int np = ((lim + kTile - 1) / kTile + p.pp_tiles - 1) / p.pp_tiles;
+  const size_t base = (size_t)row * p.ws_stride;
+  const f4 *o = reinterpret_cast<const f4 *>(p.ws_o + base * D) + dv;
+  float m = -INFINITY, z = 0.0f;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int q = 0; q < np; ++q) {
+    const float lq = p.ws_lse[base + q];
+    const f4 oq = o[(size_t)q * (D / 4)];
+    const float mn = fmaxf(m, lq);
+    const float a = exp2f(m - mn), b = exp2f(lq - mn);
+    acc = acc * a + oq * b;
+    z = z * a + b;
+    m = mn;
+  }
+  const f4 r = acc * (1.0f / z);
+  const size_t oi = (size_t)row * D + 4 * dv;
+  if constexpr (OUT == PKV_F32)
+    *reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.out) + oi) = r;
+  else
+    *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(p.out) + oi) =
+        h4{(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
+}
+
+template <int KV, int D, int BS, int OUT>
+hipError_t launch_prefill_typed(const PrefixParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL((prefix32_kernel<KV, D, BS, kModePrefill, OUT>),
+                     dim3((unsigned)prefix_grid(p)), dim3(64 * kWaves), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.num_pparts <= 1) return err;
+  constexpr int RPW = 256 / (D / 4);
+  const int rows = p.num_query_tokens * p.num_heads;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, OUT>), dim3((rows + RPW - 1) / RPW), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int KV, int D, int OUT>
+hipError_t launch_prefill_bs(const PrefixParams &p, int block_size, hipStream_t stream) {
+  switch (block_size) {
+    case 8: return launch_prefill_typed<KV, D, 8, OUT>(p, stream);
+    case 32: return launch_prefill_typed<KV, D, 32, OUT>(p, stream);
+    default: return launch_prefill_typed<KV, D, 16, OUT>(p, stream);
+  }
+}
+
+template <int KV, int OUT>
+hipError_t launch_prefill_d(const PrefixParams &p, int head_dim, int block_size,
+                            hipStream_t stream) {
+  return head_dim == 64 ? launch_prefill_bs<KV, 64, OUT>(p, block_size, stream)
+                        : launch_prefill_bs<KV, 128, OUT>(p, block_size, stream);
+}
+
+template <int KV>
+hipError_t launch_prefill_o(const PrefixParams &p, int out_dtype, int head_dim, int block_size,
+                            hipStream_t stream) {
+  return out_dtype == PKV_F32 ? launch_prefill_d<KV, PKV_F32>(p, head_dim, block_size, stream)
+                              : launch_prefill_d<KV, PKV_F16>(p, head_dim, block_size, stream);
+}
+
 }  // namespace
+
+hipError_t launch_prefill(const PrefixParams &p, int cache_dtype, int out_dtype, int head_dim,
+                          int block_size, hipStream_t stream) {
+  switch (cache_dtype) {
+    case PKV_F16: return launch_prefill_o<PKV_F16>(p, out_dtype, head_dim, block_size, stream);
+    case PKV_I8: return launch_prefill_o<PKV_I8>(p, out_dtype, head_dim, block_size, stream);
+    default: return launch_prefill_o<PKV_E4M3>(p, out_dtype, head_dim, block_size, stream);
+  }
+}
 
 hipError_t launch_prefix(const PrefixParams &p, int cache_dtype, int head_dim, int block_size,
                          hipStream_t stream) {

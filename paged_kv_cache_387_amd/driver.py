@@ -181,3 +181,16 @@ def shared(r: Replay, w, step: bool, partition_size: int | None = None, out_dtyp
         **kw)
     tables, lens = r.alloc.export_tables(seqs, maxb)
     return out, slots, pairs, sh, tables, lens
+
+
+def prefill(r: Replay, w, partition_size: int = 0, out_dtype=None, stream=None):
+    """Multi-token queries of workload w (w.q_lens set; its script wrote every
+    token) through paged_attention_prefill over the replayed cache."""
+    import torch
+    from . import paged_attention_prefill
+    odt = {"f32": torch.float32, "f16": torch.float16}[w.out_dtype] if out_dtype is None \
+        else out_dtype
+    return paged_attention_prefill(r.query, r.cache, r.block_tables, r.seq_lens,
+                                   _to_dev(w.q_offsets()), float(np.float32(w.scale)),
+                                   max(w.q_lens), out_dtype=odt,
+                                   partition_size=partition_size, stream=stream)

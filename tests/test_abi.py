@@ -186,3 +186,54 @@ def test_shared_workspace_sizes():
         assert pkv.lib().paged_attention_shared_workspace_bytes(
             8, 64, 8, 128, mb, 16, 0, ctypes.byref(g0)) == pkv.workspace_bytes(8, 64, 8, 128, mb)
     assert pkv.lib().paged_attention_shared_workspace_bytes(8, 64, 8, 128, 7, 16, 0, None) == 0
+
+
+def _prefill_status(**kw):
+    a = dict(out=1 << 20, out_dtype=pkv.F16, query=1 << 20, q_dtype=pkv.F16, k_cache=1 << 20,
+             v_cache=1 << 20, k_scale=None, v_scale=None, cache_dtype=pkv.F16, num_blocks=64,
+             block_tables=1 << 20, max_blocks=8, seq_lens=1 << 20, query_offsets=1 << 20,
+             num_seqs=2, num_query_tokens=10, max_query_len=8, num_heads=8, num_kv_heads=2,
+             head_dim=128, block_size=16, scale=0.1, partition_size=0, workspace=None,
+             ws_bytes=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return pkv.lib().paged_attention_prefill(
+        P(a["out"]), a["out_dtype"], P(a["query"]), a["q_dtype"], P(a["k_cache"]),
+        P(a["v_cache"]), P(a["k_scale"]), P(a["v_scale"]), a["cache_dtype"], a["num_blocks"],
+        P(a["block_tables"]), a["max_blocks"], P(a["seq_lens"]), P(a["query_offsets"]),
+        a["num_seqs"], a["num_query_tokens"], a["max_query_len"], a["num_heads"],
+        a["num_kv_heads"], a["head_dim"], a["block_size"], a["scale"], a["partition_size"],
+        P(a["workspace"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cache_dtype=pkv.F32, q_dtype=pkv.F32), pkv.ENOTSUP),   # fp32 caches: not on this pass
+    (dict(q_dtype=pkv.F32), pkv.ENOTSUP),
+    (dict(head_dim=96), pkv.ENOTSUP),
+    (dict(block_size=12), pkv.ENOTSUP),
+    (dict(num_heads=9), pkv.EINVAL),
+    (dict(partition_size=16), pkv.EINVAL),                          # not whole 32-token steps
+    (dict(block_size=32, partition_size=48), pkv.EINVAL),           # not whole blocks
+    (dict(partition_size=32), pkv.EINVAL),                          # needs a workspace
+    (dict(max_query_len=0), pkv.EINVAL),
+    (dict(query_offsets=None), pkv.EINVAL),
+    (dict(cache_dtype=pkv.I8), pkv.EINVAL),                         # scales missing
+    (dict(scale=float("nan")), pkv.EINVAL),
+    (dict(num_query_tokens=0), pkv.OK),
+    (dict(num_seqs=0), pkv.OK),
+])
+def test_prefill_argument_validation(kw, status):
+    assert _prefill_status(**kw) == status
+
+
+def test_prefill_workspace_sizes():
+    L = pkv.lib()
+    # many query columns: one pass per (sequence, kv head, column block), no workspace
+    assert L.paged_attention_prefill_workspace_bytes(8, 4096, 512, 64, 8, 128, 128, 16, 0) == 0
+    # few columns over a long table: split into partitions of >= 32 tiles
+    ws = L.paged_attention_prefill_workspace_bytes(1, 4, 4, 8, 1, 128, 2048, 16, 0)
+    assert ws > 0
+    # explicit 512-token partitions over 4096 tokens: 8 per row
+    rows = 10 * 8 * 8
+    assert L.paged_attention_prefill_workspace_bytes(2, 10, 8, 8, 2, 128, 256, 16, 512) == \
+        (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
