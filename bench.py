@@ -56,6 +56,8 @@ def _workloads():
         "c1": (lambda r: W.c1_tiny(), 1, None),
         # multi-token queries: 8 x (1536 cached + 512 new tokens), bench_prefill
         "prefill": (lambda r: W.chunked_prefill(), 1, None),
+        # block swap to pinned host memory and back, bench_swap
+        "swap": (lambda r: W.c2_qwen3_32b_layer(), 1, None),
     }
 
 
@@ -399,6 +401,63 @@ def bench_prefill(args, torch, pkv, driver) -> int:
     return 0
 
 
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args, torch, pkv) -> int:
+    """Whole-block copies between the device pools and a pinned host pool
+    (paged_swap_blocks) for 4096 blocks of the C2 layer's shape (16 tokens x
+    8 kv heads x 128 x fp16: 64 KiB of K+V per block, 256 MiB), each
+    direction timed over a graph of repeated copies."""
+    nb = 4096
+    cache = pkv.PagedKVCache(nb, 8, 128, "f16", fill_byte=0x3C)
+    host = pkv.HostKVPool(nb, cache)
+    rng = np.random.default_rng(0)
+    dev_ids = rng.permutation(nb).astype(np.int32)
+    host_ids = np.arange(nb, dtype=np.int32)
+    out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], 1).copy()).cuda()
+    in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], 1).copy()).cuda()
+    nbytes = 2 * cache.k.numel()
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out_ms = timed(lambda: pkv.paged_swap_blocks(cache, host, out_pairs, to_host=True))
+    in_ms = timed(lambda: pkv.paged_swap_blocks(cache, host, in_pairs, to_host=False))
+    gbs_out = nbytes / (out_ms * 1e-3) / 1e9
+    gbs_in = nbytes / (in_ms * 1e-3) / 1e9
+    best = max(gbs_out, gbs_in)
+    result = {
+        "metric": "paged block swap GB/s (device <-> pinned host, whole blocks)",
+        "value": round((gbs_out + gbs_in) / 2, 2), "unit": "GB/s", "n_gpus": 1, "steps": 5,
+        "warmup": 2, "ms_per_step": round(out_ms + in_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "swap", "blocks": nb, "block_bytes_kv": nbytes // nb,
+                   "num_kv_heads": 8, "head_dim": 128, "block_size": 16},
+        "swap_out_gbs": round(gbs_out, 2), "swap_in_gbs": round(gbs_in, 2),
+        "roofline": {"bound": "host-link", "achieved": round(best, 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best / HOST_LINK_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +515,8 @@ def main():
         return pmc_copy()
     if args.workload == "prefill":
         return bench_prefill(args, torch, pkv, driver)
+    if args.workload == "swap":
+        return bench_swap(args, torch, pkv)
     factory, replicas, pool = _workloads()[args.workload]
     R = args.replicas or replicas
     bs = args.block_size

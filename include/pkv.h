@@ -155,6 +155,68 @@ int pkv_seq_slots(const pkv_alloc *a, int64_t seq_id, int32_t start, int32_t cou
 int pkv_export_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
                       int32_t max_blocks_per_seq, int32_t *out_block_tables,
                       int32_t *out_seq_lens);
+/* ---- swapping to a host block pool ("swap_out(blocks, cpu_blocks) /
+ * swap_in(blocks, gpu_blocks)" when device memory runs short [fairy, s06];
+ * swapped-out KV kept in CPU memory [yunthe, preemption / swap_space]) ----
+ * The allocator keeps a second pool of num_host_blocks host blocks with its
+ * own FIFO free list and reference counts.  A swapped-out sequence's table
+ * holds host blocks; it may only be freed or swapped back in (other calls on
+ * it return PKV_EINVAL).  Data moves with paged_swap_blocks. */
+/* Set the host pool size (free list 0 .. n-1); PKV_EINVAL while a sequence
+ * is swapped out. */
+int pkv_alloc_set_host_blocks(pkv_alloc *a, int32_t num_host_blocks);
+int32_t pkv_alloc_num_free_host(const pkv_alloc *a);
+int32_t pkv_alloc_free_list_host(const pkv_alloc *a, int32_t *out, int32_t cap);
+int32_t pkv_host_block_refcount(const pkv_alloc *a, int32_t block);
+/* *on_host (host) = 1 if the sequence is swapped out. */
+int pkv_seq_on_host(const pkv_alloc *a, int64_t seq_id, int32_t *on_host);
+/* Move n sequences (distinct, on the device) to the host pool, all or
+ * nothing.  Each distinct device block of their tables, in order of first
+ * appearance, gets one host block from the head of the host free list (so
+ * blocks the sequences share stay shared); pairs (host, [cap][2]) receives
+ * [device, host] rows -- copy them with paged_swap_blocks(to_host = 1) -- and
+ * *num_pairs their count.  The sequences' references to the device blocks are
+ * dropped (blocks other sequences still use stay).  PKV_ENOMEM if the host
+ * free list is too short, PKV_EINVAL if cap is. */
+int pkv_seq_swap_out(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int32_t *pairs,
+                     int32_t cap, int32_t *num_pairs);
+/* The reverse for n swapped-out sequences: each distinct host block gets a
+ * device block (prefix-cache blocks are evicted if the free list is short);
+ * pairs receives [host, device] rows (paged_swap_blocks(to_host = 0)); host
+ * blocks whose count drops to zero return to the host free-list tail. */
+int pkv_seq_swap_in(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int32_t *pairs,
+                    int32_t cap, int32_t *num_pairs);
+
+/* ---- automatic prefix caching [fairy, s08 APC: "each physical block is
+ * indexed by the hash of its content" and a request whose prompt starts with
+ * a cached block sequence reuses those blocks; jsqmd, section 4.2] ----
+ * Reading of the pages' per-block hash: a block's K/V depend on every token
+ * before it, so its key is the whole token prefix through that block -- a
+ * chained 64-bit hash, and a hit is verified exactly (the block's own tokens
+ * and its parent cached block).  Only full blocks are cached.  The cache holds
+ * one reference to each cached block; blocks that only the cache holds are
+ * evictable, least recently released first, and every allocating call evicts
+ * them (to the free-list tail) when the free list is too short. */
+/* Create seq_id (must be new) for a prompt of n tokens (host int32 token ids):
+ * the longest run of leading full blocks found in the cache is shared, the
+ * rest is taken from the free list.  *num_cached_tokens receives the shared
+ * tokens (a multiple of block_size), whose K/V need not be computed.
+ * PKV_ENOMEM (nothing changed) if the blocks cannot be found. */
+int pkv_seq_allocate_cached(pkv_alloc *a, int64_t seq_id, const int32_t *tokens, int32_t n,
+                            int32_t *num_cached_tokens);
+/* Register the full blocks of the first n tokens of seq_id (their K/V
+ * written; tokens = the sequence's token ids) in the cache, from the first
+ * block on; stops at a block whose prefix is cached as another block's or
+ * whose block is cached under another prefix. */
+int pkv_seq_cache_blocks(pkv_alloc *a, int64_t seq_id, const int32_t *tokens, int32_t n);
+/* Evict up to max_blocks cache-only blocks (least recently released first). */
+int pkv_prefix_cache_evict(pkv_alloc *a, int32_t max_blocks, int32_t *num_evicted);
+/* Number of cached blocks. */
+int32_t pkv_prefix_cache_size(const pkv_alloc *a);
+/* The evictable blocks, least recently released first (up to cap into out);
+ * returns their count. */
+int32_t pkv_prefix_cache_evictable(const pkv_alloc *a, int32_t *out, int32_t cap);
+
 /* Tables of n sequences split into shared prefixes and private suffixes, the
  * input of paged_attention_decode_shared.  Sequences forked from one parent
  * share the physical blocks of their common beginning [fairy, s05
@@ -229,6 +291,22 @@ int paged_copy_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale
                       int32_t cache_dtype, int32_t num_blocks, const int32_t *block_pairs,
                       int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, void *stream);
+
+/* Block swap between the device pools and host pools of the same layout
+ * (swap_out / swap_in [fairy, s06]): for each row of pairs (device int32
+ * [num_pairs][2]) copy the whole block -- K and V of every kv head and, for
+ * quantized caches, the scales -- from device block row[0] to host block
+ * row[1] (to_host = 1) or from host block row[0] to device block row[1]
+ * (to_host = 0).  host_k, host_v (and host_k_scale, host_v_scale) are host
+ * pools of num_host_blocks blocks in pinned memory that the device can
+ * address (hipHostMalloc / torch pin_memory); the copy runs as a kernel over
+ * the host link.  Rows with an index out of range are skipped; destinations
+ * must be distinct. */
+int paged_swap_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale,
+                      void *host_k, void *host_v, void *host_k_scale, void *host_v_scale,
+                      int32_t cache_dtype, int32_t num_blocks, int32_t num_host_blocks,
+                      const int32_t *block_pairs, int32_t num_pairs, int32_t to_host,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, void *stream);
 
 /* Partition size (tokens) paged_attention_decode uses for these shapes when
  * asked for `requested` (0 = the library's choice); a value >=

@@ -16,6 +16,17 @@ A plain Python model of the KV block manager, written from the pages:
 Reference counts (how many table entries point at a block) are this model's
 reading of "shared": a block returns to the free list when its count reaches
 zero.  Statuses are strings ("ok", "enomem", "enoent", "eexist", "einval").
+
+Swapping ("swap_out(blocks, cpu_blocks) / swap_in(blocks, gpu_blocks)" of the
+Block Manager, KVcache-learning s06; KV moved to CPU memory under
+preemption, yunthe.com): a host pool with its own FIFO free list; a set of
+sequences moves as a whole, blocks they share staying shared.
+
+Automatic prefix caching (KVcache-learning s08; jsqmd.com section 4.2): a full
+block is indexed by the token prefix through it (this model keys by the exact
+token tuple); the cache holds a reference; blocks only the cache holds are
+evicted least recently released first when an allocation finds the free list
+short.
 """
 from __future__ import annotations
 
@@ -32,6 +43,35 @@ class BlockManagerModel:
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
         self.ref = [0] * num_blocks
+        self.on_host: set[int] = set()
+        self.host_free: deque = deque()
+        self.host_ref: list[int] = []
+        self.cache: dict[tuple, int] = {}      # token prefix -> cached block
+        self.cached_as: dict[int, tuple] = {}  # cached block -> its prefix
+        self.lru: list[int] = []               # blocks only the cache holds, oldest first
+
+    # references ---------------------------------------------------------------
+    def _drop(self, b: int, k: int = 1):
+        self.ref[b] -= k
+        if self.ref[b] == 0:
+            self.free.append(b)
+        elif self.ref[b] == 1 and b in self.cached_as and b not in self.lru:
+            self.lru.append(b)
+
+    def _take(self, b: int):
+        self.ref[b] += 1
+        if b in self.lru:
+            self.lru.remove(b)
+
+    def _room(self, need: int) -> bool:
+        """Evict cache-only blocks (oldest release first) until `need` are free."""
+        if len(self.free) + len(self.lru) < need:
+            return False
+        while len(self.free) < need:
+            b = self.lru.pop(0)
+            del self.cache[self.cached_as.pop(b)]
+            self._drop(b)
+        return True
 
     def _blocks_for(self, n: int) -> int:
         return -(-n // self.block_size)
@@ -39,7 +79,7 @@ class BlockManagerModel:
     def allocate(self, seq: int, n_tokens: int):
         """Grow seq (created if new) to n_tokens filled tokens.
         Returns (status, cow_pair or None)."""
-        if n_tokens < 0:
+        if n_tokens < 0 or seq in self.on_host:
             return "einval", None
         table = self.tables.get(seq, [])
         cur = self.lens.get(seq, 0)
@@ -50,14 +90,14 @@ class BlockManagerModel:
         new_blocks = max(0, self._blocks_for(n_tokens) - len(table))
         # the partly filled tail block receives new tokens: copy it first if shared
         cow = cur % self.block_size != 0 and self.ref[table[-1]] > 1
-        if len(self.free) < new_blocks + (1 if cow else 0):
+        if not self._room(new_blocks + (1 if cow else 0)):
             return "enomem", None
         pair = None
         if cow:
             src = table[-1]
             dst = self.free.popleft()
             self.ref[dst] = 1
-            self.ref[src] -= 1
+            self._drop(src)
             table = table[:-1] + [dst]
             pair = (src, dst)
         for _ in range(new_blocks):
@@ -72,6 +112,8 @@ class BlockManagerModel:
         """Reserve the next token's slot.  Returns (status, slot, cow_pair or None)."""
         if seq not in self.tables:
             return "enoent", -1, None
+        if seq in self.on_host:
+            return "einval", -1, None
         pos = self.lens[seq]
         st, pair = self.allocate(seq, pos + 1)
         if st != "ok":
@@ -84,21 +126,151 @@ class BlockManagerModel:
             return "enoent"
         if child in self.tables:
             return "eexist"
+        if parent in self.on_host:
+            return "einval"
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         for b in self.tables[child]:
-            self.ref[b] += 1
+            self._take(b)
         return "ok"
 
     def release(self, seq: int) -> str:
         if seq not in self.tables:
             return "enoent"
-        for b in self.tables.pop(seq):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+        if seq in self.on_host:
+            for c in self.tables.pop(seq):
+                self.host_ref[c] -= 1
+                if self.host_ref[c] == 0:
+                    self.host_free.append(c)
+            self.on_host.discard(seq)
+        else:
+            for b in self.tables.pop(seq):
+                self._drop(b)
         del self.lens[seq]
         return "ok"
+
+    # swapping ----------------------------------------------------------------------
+    def set_host_blocks(self, n: int) -> str:
+        if self.on_host or n < 0:
+            return "einval"
+        self.host_free = deque(range(n))
+        self.host_ref = [0] * n
+        return "ok"
+
+    def _group(self, seqs, on_host: bool):
+        if len(set(seqs)) != len(seqs):
+            return "einval", None, None
+        for s in seqs:
+            if s not in self.tables:
+                return "enoent", None, None
+            if (s in self.on_host) != on_host:
+                return "einval", None, None
+        order, count = [], {}
+        for s in seqs:
+            for b in self.tables[s]:
+                if b not in count:
+                    order.append(b)
+                    count[b] = 0
+                count[b] += 1
+        return "ok", order, count
+
+    def swap_out(self, seqs):
+        """Move a set of device sequences to the host pool.  Returns (status,
+        [(device, host), ...])."""
+        st, order, count = self._group(seqs, False)
+        if st != "ok":
+            return st, None
+        if len(self.host_free) < len(order):
+            return "enomem", None
+        pairs = [(b, self.host_free.popleft()) for b in order]
+        where = dict(pairs)
+        for b, c in pairs:
+            self.host_ref[c] = count[b]
+        for b in order:
+            self._drop(b, count[b])
+        for s in seqs:
+            self.tables[s] = [where[b] for b in self.tables[s]]
+            self.on_host.add(s)
+        return "ok", pairs
+
+    def swap_in(self, seqs):
+        """Bring a set of swapped-out sequences back.  Returns (status,
+        [(host, device), ...])."""
+        st, order, count = self._group(seqs, True)
+        if st != "ok":
+            return st, None
+        if not self._room(len(order)):
+            return "enomem", None
+        pairs = [(c, self.free.popleft()) for c in order]
+        where = dict(pairs)
+        for c, b in pairs:
+            self.ref[b] = count[c]
+        for c in order:
+            self.host_ref[c] -= count[c]
+            if self.host_ref[c] == 0:
+                self.host_free.append(c)
+        for s in seqs:
+            self.tables[s] = [where[c] for c in self.tables[s]]
+            self.on_host.discard(s)
+        return "ok", pairs
+
+    # automatic prefix caching ------------------------------------------------------
+    def allocate_cached(self, seq: int, tokens):
+        """New sequence for a prompt: the longest run of leading full blocks
+        whose prefixes are cached is shared.  Returns (status, cached tokens)."""
+        if seq in self.tables:
+            return "eexist", 0
+        bs = self.block_size
+        tokens = [int(t) for t in tokens]
+        hits = []
+        while (len(hits) + 1) * bs <= len(tokens):
+            key = tuple(tokens[:(len(hits) + 1) * bs])
+            if key not in self.cache:
+                break
+            hits.append(self.cache[key])
+        need = self._blocks_for(len(tokens)) - len(hits)
+        if len(self.free) + len([b for b in self.lru if b not in hits]) < need:
+            return "enomem", 0
+        for b in hits:
+            self._take(b)
+        self._room(need)
+        table = list(hits)
+        for _ in range(need):
+            b = self.free.popleft()
+            self.ref[b] = 1
+            table.append(b)
+        self.tables[seq] = table
+        self.lens[seq] = len(tokens)
+        return "ok", len(hits) * bs
+
+    def cache_blocks(self, seq: int, tokens, n: int) -> str:
+        """Index the full blocks of the first n tokens of seq by their prefixes."""
+        if seq not in self.tables:
+            return "enoent"
+        if seq in self.on_host or n > self.lens[seq] or n < 0:
+            return "einval"
+        bs = self.block_size
+        tokens = [int(t) for t in tokens]
+        for i in range(n // bs):
+            key = tuple(tokens[:(i + 1) * bs])
+            if key in self.cache:
+                continue
+            b = self.tables[seq][i]
+            if b in self.cached_as:
+                break
+            self.cache[key] = b
+            self.cached_as[b] = key
+            self._take(b)
+        return "ok"
+
+    def cache_evict(self, max_blocks: int):
+        k = 0
+        while k < max_blocks and self.lru:
+            b = self.lru.pop(0)
+            del self.cache[self.cached_as.pop(b)]
+            self._drop(b)
+            k += 1
+        return "ok", k
 
     def slots(self, seq: int, start: int, count: int):
         """Slots (block * block_size + offset) of positions [start, start + count)."""
@@ -116,6 +288,8 @@ class BlockManagerModel:
         for s in seqs:
             if s not in self.tables:
                 return "enoent", None, None
+            if s in self.on_host:
+                return "einval", None, None
             t = self.tables[s]
             if len(t) > max_blocks:
                 return "einval", None, None
@@ -140,6 +314,8 @@ class BlockManagerModel:
         for s in seqs:
             if s not in self.tables:
                 return "enoent", None
+            if s in self.on_host:
+                return "einval", None
         bs = self.block_size
         firsts = {}
         for i, s in enumerate(seqs):
@@ -186,12 +362,22 @@ class BlockManagerModel:
     # invariants ---------------------------------------------------------------
     def check_invariants(self):
         counts = [0] * self.num_blocks
+        hcounts = [0] * len(self.host_ref)
         for seq, t in self.tables.items():
             assert len(t) == self._blocks_for(self.lens[seq]), "table length != ceil(len/bs)"
             assert len(t) * self.block_size - self.lens[seq] < self.block_size, "tail waste"
             for b in t:
-                counts[b] += 1
-        assert counts == self.ref, "refcount != number of table entries"
+                if seq in self.on_host:
+                    hcounts[b] += 1
+                else:
+                    counts[b] += 1
+        for b in self.cached_as:
+            counts[b] += 1                       # the cache's reference
+        assert counts == self.ref, "refcount != table entries + cache"
+        assert hcounts == self.host_ref, "host refcount != host table entries"
+        assert set(self.lru) == {b for b in self.cached_as if self.ref[b] == 1}, "evictable set"
+        assert len(self.lru) == len(set(self.lru))
+        assert set(self.host_free) == {c for c, r in enumerate(self.host_ref) if r == 0}
         free = set(self.free)
         assert len(free) == len(self.free), "duplicate free block"
         for b in range(self.num_blocks):

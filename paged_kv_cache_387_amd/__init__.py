@@ -30,6 +30,10 @@ EXPORTS = [
     "pkv_block_refcount", "pkv_seq_allocate", "pkv_seq_append_slot", "pkv_seq_append_slots",
     "pkv_seq_fork", "pkv_seq_free", "pkv_seq_len", "pkv_seq_slots", "pkv_export_tables",
     "pkv_export_shared_tables",
+    "pkv_alloc_set_host_blocks", "pkv_alloc_num_free_host", "pkv_alloc_free_list_host",
+    "pkv_host_block_refcount", "pkv_seq_on_host", "pkv_seq_swap_out", "pkv_seq_swap_in",
+    "pkv_seq_allocate_cached", "pkv_seq_cache_blocks", "pkv_prefix_cache_evict",
+    "pkv_prefix_cache_size", "pkv_prefix_cache_evictable", "paged_swap_blocks",
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_decode_step",
     "paged_attention_shared_workspace_bytes", "paged_attention_decode_shared",
@@ -83,6 +87,20 @@ def lib() -> ctypes.CDLL:
             "pkv_export_tables": ([P, P, i32, i32, P, P], ctypes.c_int),
             "pkv_export_shared_tables": ([P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P],
                                          ctypes.c_int),
+            "pkv_alloc_set_host_blocks": ([P, i32], ctypes.c_int),
+            "pkv_alloc_num_free_host": ([P], i32),
+            "pkv_alloc_free_list_host": ([P, P, i32], i32),
+            "pkv_host_block_refcount": ([P, i32], i32),
+            "pkv_seq_on_host": ([P, i64, P], ctypes.c_int),
+            "pkv_seq_swap_out": ([P, P, i32, P, i32, P], ctypes.c_int),
+            "pkv_seq_swap_in": ([P, P, i32, P, i32, P], ctypes.c_int),
+            "pkv_seq_allocate_cached": ([P, i64, P, i32, P], ctypes.c_int),
+            "pkv_seq_cache_blocks": ([P, i64, P, i32], ctypes.c_int),
+            "pkv_prefix_cache_evict": ([P, i32, P], ctypes.c_int),
+            "pkv_prefix_cache_size": ([P], i32),
+            "pkv_prefix_cache_evictable": ([P, P, i32], i32),
+            "paged_swap_blocks": ([P, P, P, P, P, P, P, P, i32, i32, i32, P, i32, i32, i32, i32,
+                                   i32, P], ctypes.c_int),
             "paged_kv_write": ([P, P, i32, i64, i64, P, i32, P, P, P, P, i32, i32, i32, i32,
                                 i32, P], ctypes.c_int),
             "paged_copy_blocks": ([P, P, P, P, i32, i32, P, i32, i32, i32, i32, P],
@@ -222,6 +240,81 @@ class BlockAllocator:
                                        _np_ptr(lens)), "pkv_export_tables")
         return tables[:n], lens[:n]
 
+    # ---- host pool and swapping ------------------------------------------------
+    def set_host_blocks(self, n: int):
+        _check(lib().pkv_alloc_set_host_blocks(self._h, n), "pkv_alloc_set_host_blocks")
+        self._num_host = n
+
+    @property
+    def num_free_host(self) -> int:
+        return lib().pkv_alloc_num_free_host(self._h)
+
+    def free_list_host(self) -> list:
+        n = self.num_free_host
+        out = np.empty(max(n, 1), np.int32)
+        lib().pkv_alloc_free_list_host(self._h, _np_ptr(out), n)
+        return out[:n].tolist()
+
+    def host_refcount(self, block: int) -> int:
+        return lib().pkv_host_block_refcount(self._h, block)
+
+    def on_host(self, seq: int) -> bool:
+        f = ctypes.c_int32(0)
+        _check(lib().pkv_seq_on_host(self._h, seq, ctypes.byref(f)), "pkv_seq_on_host")
+        return bool(f.value)
+
+    def _swap(self, fn, seqs, what):
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        # distinct blocks of a swap never exceed either pool
+        cap = 1 + self.num_blocks + self.num_free_host + sum(self._host_held())
+        pairs = np.empty((cap, 2), np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, _np_ptr(ids), len(ids), _np_ptr(pairs), cap, ctypes.byref(n)), what)
+        return pairs[:n.value].copy()
+
+    def _host_held(self):
+        # host blocks in use (the pool size minus the free ones)
+        return [self._num_host - self.num_free_host] if hasattr(self, "_num_host") else [0]
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """[device, host] block pairs to copy (paged_swap_blocks, to_host=True)."""
+        return self._swap(lib().pkv_seq_swap_out, seqs, "pkv_seq_swap_out")
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """[host, device] block pairs to copy (paged_swap_blocks, to_host=False)."""
+        return self._swap(lib().pkv_seq_swap_in, seqs, "pkv_seq_swap_in")
+
+    # ---- automatic prefix caching ---------------------------------------------
+    def allocate_cached(self, seq: int, tokens) -> int:
+        """New sequence for a prompt; returns how many leading tokens were found
+        in the prefix cache (their K/V are there already)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        got = ctypes.c_int32(0)
+        _check(lib().pkv_seq_allocate_cached(self._h, seq, _np_ptr(t), len(t), ctypes.byref(got)),
+               "pkv_seq_allocate_cached")
+        return got.value
+
+    def cache_blocks(self, seq: int, tokens, n: int | None = None):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(lib().pkv_seq_cache_blocks(self._h, seq, _np_ptr(t), len(t) if n is None else n),
+               "pkv_seq_cache_blocks")
+
+    def cache_evict(self, max_blocks: int) -> int:
+        k = ctypes.c_int32(0)
+        _check(lib().pkv_prefix_cache_evict(self._h, max_blocks, ctypes.byref(k)),
+               "pkv_prefix_cache_evict")
+        return k.value
+
+    @property
+    def cache_size(self) -> int:
+        return lib().pkv_prefix_cache_size(self._h)
+
+    def cache_evictable(self) -> list:
+        n = lib().pkv_prefix_cache_evictable(self._h, None, 0)
+        out = np.empty(max(n, 1), np.int32)
+        lib().pkv_prefix_cache_evictable(self._h, _np_ptr(out), n)
+        return out[:n].tolist()
+
     def export_shared(self, seqs, max_prefix_blocks: int, max_suffix_blocks: int,
                       min_prefix_tokens: int = 0) -> dict:
         """Tables split into shared prefixes and private suffixes (host numpy
@@ -328,6 +421,50 @@ class PagedKVCache:
 
     def copy_blocks(self, pairs, stream=None):
         paged_copy_blocks(self, pairs, stream=stream)
+
+
+class HostKVPool:
+    """Host-side block pools for swapped-out sequences: pinned (page-locked,
+    device-addressable) uint8 tensors in the device pools' layout, plus fp16
+    scale arrays for quantized caches."""
+
+    def __init__(self, num_host_blocks: int, like: PagedKVCache):
+        torch = _torch()
+        self.num_blocks = num_host_blocks
+        self.like = like
+        nbytes = cache_bytes(num_host_blocks, like.num_kv_heads, like.head_dim, like.cache_dtype,
+                             like.block_size)
+        self.k = torch.zeros(max(nbytes, 16), dtype=torch.uint8, pin_memory=True)
+        self.v = torch.zeros(max(nbytes, 16), dtype=torch.uint8, pin_memory=True)
+        self.k_scale = self.v_scale = None
+        if like.quantized:
+            n = max(num_host_blocks * like.num_kv_heads * like.block_size, 1)
+            self.k_scale = torch.zeros(n, dtype=torch.float16, pin_memory=True)
+            self.v_scale = torch.zeros(n, dtype=torch.float16, pin_memory=True)
+
+
+def paged_swap_blocks(cache: PagedKVCache, host: HostKVPool, pairs, to_host: bool,
+                      stream=None):
+    """Copy whole blocks between the device pools and the host pools: rows
+    [device, host] (to_host) or [host, device] of `pairs` (int32 device [n, 2])."""
+    torch = _torch()
+    n = 0 if pairs is None else pairs.shape[0]
+    if n == 0:
+        return
+    for t in (host.k, host.v):
+        if not t.is_pinned():
+            raise ValueError("host pools must be pinned memory")
+    ks, vs = cache._scales()
+    hks = hvs = None
+    if cache.quantized:
+        hks = ctypes.c_void_p(host.k_scale.data_ptr())
+        hvs = ctypes.c_void_p(host.v_scale.data_ptr())
+    _check(lib().paged_swap_blocks(
+        _dev(cache.k, "k_cache"), _dev(cache.v, "v_cache"), ks, vs,
+        ctypes.c_void_p(host.k.data_ptr()), ctypes.c_void_p(host.v.data_ptr()), hks, hvs,
+        cache.cache_dtype, cache.num_blocks, host.num_blocks,
+        _dev(pairs, "pairs", torch.int32, 2 * n), n, 1 if to_host else 0, cache.num_kv_heads,
+        cache.head_dim, cache.block_size, _stream_ptr(stream)), "paged_swap_blocks")
 
 
 def paged_kv_write(key, value, slot_mapping, cache: PagedKVCache, stream=None):

@@ -17,15 +17,19 @@
 // free or referenced, so it never overflows).  Sequences live in a hash map.
 #include <cstdint>
 #include <cstring>
+#include <deque>
+#include <list>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "pkv.h"
 
 struct pkv_seq {
-  std::vector<int32_t> blocks;
+  std::vector<int32_t> blocks;   // device blocks, or host blocks while swapped out
   int32_t len = 0;
+  bool on_host = false;
 };
 
 struct pkv_alloc {
@@ -34,8 +38,28 @@ struct pkv_alloc {
   std::vector<int32_t> ring;   // free list storage
   int32_t head = 0;            // index of the first free entry
   int32_t count = 0;           // number of free blocks
-  std::vector<int32_t> ref;    // table entries pointing at each block
+  std::vector<int32_t> ref;    // table entries (+1 when cached) pointing at each block
   std::unordered_map<int64_t, pkv_seq> seqs;
+
+  // host block pool for swapped-out sequences (FIFO free list like the device one)
+  int32_t num_host = 0;
+  std::deque<int32_t> host_free;
+  std::vector<int32_t> host_ref;
+
+  // prefix cache: full blocks indexed by the hash of the token prefix through
+  // them (chained block by block); each cached block keeps its own tokens and
+  // the key of the prefix before it, which a hit must match -- exact up to a
+  // 64-bit collision of that preceding key.  The cache holds one reference to
+  // each cached block; blocks only the cache holds are evictable, least
+  // recently released first.
+  std::unordered_map<uint64_t, int32_t> by_hash;
+  std::vector<char> cached;
+  std::vector<uint64_t> key;
+  std::vector<uint64_t> parent_key;
+  std::vector<std::vector<int32_t>> block_tokens;
+  std::list<int32_t> lru;
+  std::vector<std::list<int32_t>::iterator> lru_pos;
+  std::vector<char> in_lru;
 
   int32_t pop_front() {
     int32_t b = ring[head];
@@ -50,6 +74,41 @@ struct pkv_alloc {
     ++count;
   }
   int32_t blocks_for(int32_t n) const { return (n + block_size - 1) / block_size; }
+
+  // k table entries (or the cache's reference) of block b are gone
+  void unref(int32_t b, int32_t k = 1) {
+    ref[b] -= k;
+    if (ref[b] == 0) {
+      push_back(b);
+    } else if (ref[b] == 1 && cached[b] && !in_lru[b]) {
+      lru_pos[b] = lru.insert(lru.end(), b);
+      in_lru[b] = 1;
+    }
+  }
+  void addref(int32_t b) {
+    ref[b] += 1;
+    if (in_lru[b]) {
+      lru.erase(lru_pos[b]);
+      in_lru[b] = 0;
+    }
+  }
+  // Drop the least recently released cache-only block: uncached, freed.
+  void evict_one() {
+    const int32_t b = lru.front();
+    lru.pop_front();
+    in_lru[b] = 0;
+    by_hash.erase(key[b]);
+    cached[b] = 0;
+    block_tokens[b].clear();
+    unref(b);
+  }
+  // Room for `need` new blocks: evicts as many cache-only blocks as the free
+  // list lacks.  False (nothing changed) if even that is not enough.
+  bool make_room(int32_t need) {
+    if ((int64_t)count + (int64_t)lru.size() < need) return false;
+    while (count < need) evict_one();
+    return true;
+  }
 };
 
 namespace {
@@ -66,6 +125,8 @@ int grow(pkv_alloc *a, int64_t seq_id, int32_t n, bool create, int32_t *cow_src,
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) {
     if (!create) return PKV_ENOENT;
+  } else if (it->second.on_host) {
+    return PKV_EINVAL;   // swapped out: swap in first
   }
   const int32_t cur = (it == a->seqs.end()) ? 0 : it->second.len;
   const int32_t held = (it == a->seqs.end()) ? 0 : (int32_t)it->second.blocks.size();
@@ -77,7 +138,7 @@ int grow(pkv_alloc *a, int64_t seq_id, int32_t n, bool create, int32_t *cow_src,
   if (need < 0) need = 0;
   const bool cow = (it != a->seqs.end()) && (cur % a->block_size != 0) &&
                    a->ref[it->second.blocks.back()] > 1;
-  if (a->count < need + (cow ? 1 : 0)) return PKV_ENOMEM;
+  if (!a->make_room(need + (cow ? 1 : 0))) return PKV_ENOMEM;
   if (it == a->seqs.end()) it = a->seqs.emplace(seq_id, pkv_seq{}).first;
   pkv_seq &s = it->second;
   s.blocks.reserve((size_t)held + need);
@@ -85,7 +146,7 @@ int grow(pkv_alloc *a, int64_t seq_id, int32_t n, bool create, int32_t *cow_src,
     const int32_t src = s.blocks.back();
     const int32_t dst = a->pop_front();
     a->ref[dst] = 1;
-    a->ref[src] -= 1;
+    a->unref(src);
     s.blocks.back() = dst;
     set_pair(cow_src, cow_dst, src, dst);
   }
@@ -114,6 +175,12 @@ int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t *free
     a->block_size = block_size;
     a->ring.resize(num_blocks);
     a->ref.assign(num_blocks, 0);
+    a->cached.assign(num_blocks, 0);
+    a->key.assign(num_blocks, 0);
+    a->parent_key.assign(num_blocks, 0);
+    a->block_tokens.resize(num_blocks);
+    a->lru_pos.resize(num_blocks);
+    a->in_lru.assign(num_blocks, 0);
     if (free_order) {
       std::vector<char> seen(num_blocks, 0);
       for (int32_t i = 0; i < num_blocks; ++i) {
@@ -172,6 +239,7 @@ int pkv_seq_append_slot(pkv_alloc *a, int64_t seq_id, int64_t *slot, int32_t *co
   if (!a || !slot) return PKV_EINVAL;
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PKV_ENOENT;
+  if (it->second.on_host) return PKV_EINVAL;
   const int32_t pos = it->second.len;
   if (pos == INT32_MAX) return PKV_EINVAL;
   int st;
@@ -215,9 +283,10 @@ int pkv_seq_fork(pkv_alloc *a, int64_t parent, int64_t child) {
   auto p = a->seqs.find(parent);
   if (p == a->seqs.end()) return PKV_ENOENT;
   if (a->seqs.count(child)) return PKV_EEXIST;
+  if (p->second.on_host) return PKV_EINVAL;
   try {
     pkv_seq copy = p->second;
-    for (int32_t b : copy.blocks) a->ref[b] += 1;
+    for (int32_t b : copy.blocks) a->addref(b);
     a->seqs.emplace(child, std::move(copy));
   } catch (...) {
     return PKV_ENOMEM;
@@ -229,8 +298,11 @@ int pkv_seq_free(pkv_alloc *a, int64_t seq_id) {
   if (!a) return PKV_EINVAL;
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PKV_ENOENT;
-  for (int32_t b : it->second.blocks) {
-    if (--a->ref[b] == 0) a->push_back(b);
+  if (it->second.on_host) {
+    for (int32_t c : it->second.blocks)
+      if (--a->host_ref[c] == 0) a->host_free.push_back(c);
+  } else {
+    for (int32_t b : it->second.blocks) a->unref(b);
   }
   a->seqs.erase(it);
   return PKV_OK;
@@ -250,7 +322,7 @@ int pkv_seq_slots(const pkv_alloc *a, int64_t seq_id, int32_t start, int32_t cou
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PKV_ENOENT;
   const pkv_seq &s = it->second;
-  if ((int64_t)start + count > s.len) return PKV_EINVAL;
+  if (s.on_host || (int64_t)start + count > s.len) return PKV_EINVAL;
   const int32_t bs = a->block_size;
   for (int32_t i = 0; i < count; ++i) {
     const int32_t p = start + i;
@@ -268,6 +340,7 @@ int pkv_export_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
   for (int32_t i = 0; i < n; ++i) {  // validate everything before writing
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return PKV_ENOENT;
+    if (it->second.on_host) return PKV_EINVAL;
     if ((int32_t)it->second.blocks.size() > max_blocks_per_seq) return PKV_EINVAL;
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -298,6 +371,7 @@ int pkv_export_shared_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return PKV_ENOENT;
+    if (it->second.on_host) return PKV_EINVAL;
     sq[i] = &it->second;
   }
   const int32_t bs = a->block_size;
@@ -372,6 +446,276 @@ int pkv_export_shared_tables(const pkv_alloc *a, const int64_t *seq_ids, int32_t
   *num_groups = (int32_t)kept.size();
   *max_group_size = biggest;
   return PKV_OK;
+}
+
+// ---- host pool and swapping -------------------------------------------------
+
+int pkv_alloc_set_host_blocks(pkv_alloc *a, int32_t num_host_blocks) {
+  if (!a || num_host_blocks < 0) return PKV_EINVAL;
+  for (const auto &kv : a->seqs)
+    if (kv.second.on_host) return PKV_EINVAL;
+  try {
+    a->num_host = num_host_blocks;
+    a->host_free.clear();
+    for (int32_t i = 0; i < num_host_blocks; ++i) a->host_free.push_back(i);
+    a->host_ref.assign(num_host_blocks, 0);
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_num_free_host(const pkv_alloc *a) {
+  return a ? (int32_t)a->host_free.size() : PKV_EINVAL;
+}
+
+int32_t pkv_alloc_free_list_host(const pkv_alloc *a, int32_t *out, int32_t cap) {
+  if (!a || (cap > 0 && !out)) return PKV_EINVAL;
+  int32_t i = 0;
+  for (int32_t c : a->host_free) {
+    if (i >= cap) break;
+    out[i++] = c;
+  }
+  return (int32_t)a->host_free.size();
+}
+
+int32_t pkv_host_block_refcount(const pkv_alloc *a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_host) return PKV_EINVAL;
+  return a->host_ref[block];
+}
+
+int pkv_seq_on_host(const pkv_alloc *a, int64_t seq_id, int32_t *on_host) {
+  if (!a || !on_host) return PKV_EINVAL;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ENOENT;
+  *on_host = it->second.on_host ? 1 : 0;
+  return PKV_OK;
+}
+
+namespace {
+
+// The sequences of a swap call: known, all on the same side, no repeats.
+int collect(pkv_alloc *a, const int64_t *seq_ids, int32_t n, bool on_host,
+            std::vector<pkv_seq *> *out) {
+  std::unordered_set<int64_t> seen;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_ENOENT;
+    if (it->second.on_host != on_host || !seen.insert(seq_ids[i]).second) return PKV_EINVAL;
+    out->push_back(&it->second);
+  }
+  return PKV_OK;
+}
+
+// Distinct blocks of the sequences' tables in order of first appearance, and
+// how many of those table entries point at each.
+void distinct_blocks(const std::vector<pkv_seq *> &sq, std::vector<int32_t> *order,
+                     std::unordered_map<int32_t, int32_t> *count) {
+  for (const pkv_seq *q : sq)
+    for (int32_t b : q->blocks)
+      if ((*count)[b]++ == 0) order->push_back(b);
+}
+
+}  // namespace
+
+int pkv_seq_swap_out(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int32_t *pairs,
+                     int32_t cap, int32_t *num_pairs) {
+  if (num_pairs) *num_pairs = 0;
+  if (!a || n < 0 || !num_pairs || (n > 0 && !seq_ids) || cap < 0 || (cap > 0 && !pairs))
+    return PKV_EINVAL;
+  try {
+    std::vector<pkv_seq *> sq;
+    const int st = collect(a, seq_ids, n, false, &sq);
+    if (st != PKV_OK) return st;
+    std::vector<int32_t> order;
+    std::unordered_map<int32_t, int32_t> cnt;
+    distinct_blocks(sq, &order, &cnt);
+    if ((int64_t)order.size() > cap) return PKV_EINVAL;
+    if (order.size() > a->host_free.size()) return PKV_ENOMEM;
+    std::unordered_map<int32_t, int32_t> to_host;
+    for (size_t i = 0; i < order.size(); ++i) {
+      const int32_t b = order[i], c = a->host_free.front();
+      a->host_free.pop_front();
+      a->host_ref[c] = cnt[b];
+      to_host[b] = c;
+      pairs[2 * i] = b;
+      pairs[2 * i + 1] = c;
+    }
+    for (int32_t b : order) a->unref(b, cnt[b]);
+    for (pkv_seq *q : sq) {
+      for (int32_t &b : q->blocks) b = to_host[b];
+      q->on_host = true;
+    }
+    *num_pairs = (int32_t)order.size();
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
+int pkv_seq_swap_in(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int32_t *pairs,
+                    int32_t cap, int32_t *num_pairs) {
+  if (num_pairs) *num_pairs = 0;
+  if (!a || n < 0 || !num_pairs || (n > 0 && !seq_ids) || cap < 0 || (cap > 0 && !pairs))
+    return PKV_EINVAL;
+  try {
+    std::vector<pkv_seq *> sq;
+    const int st = collect(a, seq_ids, n, true, &sq);
+    if (st != PKV_OK) return st;
+    std::vector<int32_t> order;
+    std::unordered_map<int32_t, int32_t> cnt;
+    distinct_blocks(sq, &order, &cnt);
+    if ((int64_t)order.size() > cap) return PKV_EINVAL;
+    if (!a->make_room((int32_t)order.size())) return PKV_ENOMEM;
+    std::unordered_map<int32_t, int32_t> to_dev;
+    for (size_t i = 0; i < order.size(); ++i) {
+      const int32_t c = order[i], b = a->pop_front();
+      a->ref[b] = cnt[c];
+      to_dev[c] = b;
+      pairs[2 * i] = c;
+      pairs[2 * i + 1] = b;
+    }
+    for (int32_t c : order) {
+      a->host_ref[c] -= cnt[c];
+      if (a->host_ref[c] == 0) a->host_free.push_back(c);
+    }
+    for (pkv_seq *q : sq) {
+      for (int32_t &c : q->blocks) c = to_dev[c];
+      q->on_host = false;
+    }
+    *num_pairs = (int32_t)order.size();
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
+// ---- automatic prefix caching -------------------------------------------------
+
+namespace {
+
+// Hash of the token prefix through one more block, chained from the previous
+// block's (0 before the first): a 64-bit multiply-xorshift mix per token.
+uint64_t chain_hash(uint64_t h, const int32_t *tok, int32_t n) {
+  h ^= 0x9E3779B97F4A7C15ull;
+  for (int32_t i = 0; i < n; ++i) {
+    h ^= (uint32_t)tok[i];
+    h *= 0xBF58476D1CE4E5B9ull;
+    h ^= h >> 31;
+  }
+  return h;
+}
+
+// The cached block whose prefix key is h, preceded by the prefix with key
+// hprev, holding tokens tok; or -1.
+int32_t lookup(const pkv_alloc *a, uint64_t h, const int32_t *tok, uint64_t hprev) {
+  auto it = a->by_hash.find(h);
+  if (it == a->by_hash.end()) return -1;
+  const int32_t b = it->second;
+  if (a->parent_key[b] != hprev) return -1;
+  const std::vector<int32_t> &t = a->block_tokens[b];
+  if (std::memcmp(t.data(), tok, sizeof(int32_t) * a->block_size) != 0) return -1;
+  return b;
+}
+
+}  // namespace
+
+int pkv_seq_allocate_cached(pkv_alloc *a, int64_t seq_id, const int32_t *tokens, int32_t n,
+                            int32_t *num_cached_tokens) {
+  if (num_cached_tokens) *num_cached_tokens = 0;
+  if (!a || n < 0 || (n > 0 && !tokens) || !num_cached_tokens) return PKV_EINVAL;
+  if (a->seqs.count(seq_id)) return PKV_EEXIST;
+  try {
+    const int32_t bs = a->block_size;
+    std::vector<int32_t> hit;
+    uint64_t h = 0;
+    for (int32_t i = 0; (int64_t)(i + 1) * bs <= n; ++i) {
+      const uint64_t hp = h;
+      h = chain_hash(h, tokens + (size_t)i * bs, bs);
+      const int32_t b = lookup(a, h, tokens + (size_t)i * bs, hp);
+      if (b < 0) break;
+      hit.push_back(b);
+    }
+    const int32_t need = a->blocks_for(n) - (int32_t)hit.size();
+    // capacity: the free list plus the evictable blocks other than the hits
+    int32_t hit_evictable = 0;
+    for (int32_t b : hit) hit_evictable += a->in_lru[b] ? 1 : 0;
+    if ((int64_t)a->count + (int64_t)a->lru.size() - hit_evictable < need) return PKV_ENOMEM;
+    pkv_seq s;
+    s.blocks.reserve(a->blocks_for(n));
+    for (int32_t b : hit) {
+      a->addref(b);
+      s.blocks.push_back(b);
+    }
+    a->make_room(need);
+    for (int32_t i = 0; i < need; ++i) {
+      const int32_t b = a->pop_front();
+      a->ref[b] = 1;
+      s.blocks.push_back(b);
+    }
+    s.len = n;
+    a->seqs.emplace(seq_id, std::move(s));
+    *num_cached_tokens = (int32_t)hit.size() * bs;
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
+int pkv_seq_cache_blocks(pkv_alloc *a, int64_t seq_id, const int32_t *tokens, int32_t n) {
+  if (!a || n < 0 || (n > 0 && !tokens)) return PKV_EINVAL;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ENOENT;
+  pkv_seq &s = it->second;
+  if (s.on_host || n > s.len) return PKV_EINVAL;
+  try {
+    const int32_t bs = a->block_size;
+    uint64_t h = 0;
+    for (int32_t i = 0; (int64_t)(i + 1) * bs <= n; ++i) {
+      const int32_t *tok = tokens + (size_t)i * bs;
+      const uint64_t hp = h;
+      h = chain_hash(h, tok, bs);
+      if (lookup(a, h, tok, hp) >= 0) continue;   // this prefix is cached already
+      if (a->by_hash.count(h)) break;             // a different prefix holds this hash
+      const int32_t b = s.blocks[i];
+      if (a->cached[b]) break;                    // cached under another prefix
+      a->by_hash[h] = b;
+      a->cached[b] = 1;
+      a->key[b] = h;
+      a->parent_key[b] = hp;
+      a->block_tokens[b].assign(tok, tok + bs);
+      a->addref(b);                               // the cache's reference
+    }
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_evict(pkv_alloc *a, int32_t max_blocks, int32_t *num_evicted) {
+  if (num_evicted) *num_evicted = 0;
+  if (!a || max_blocks < 0) return PKV_EINVAL;
+  int32_t k = 0;
+  while (k < max_blocks && !a->lru.empty()) {
+    a->evict_one();
+    ++k;
+  }
+  if (num_evicted) *num_evicted = k;
+  return PKV_OK;
+}
+
+int32_t pkv_prefix_cache_size(const pkv_alloc *a) {
+  return a ? (int32_t)a->by_hash.size() : PKV_EINVAL;
+}
+
+int32_t pkv_prefix_cache_evictable(const pkv_alloc *a, int32_t *out, int32_t cap) {
+  if (!a || (cap > 0 && !out)) return PKV_EINVAL;
+  int32_t i = 0;
+  for (int32_t b : a->lru) {
+    if (i >= cap) break;
+    out[i++] = b;
+  }
+  return (int32_t)a->lru.size();
 }
 
 }  // extern "C"

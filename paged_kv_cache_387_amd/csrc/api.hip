@@ -633,4 +633,44 @@ int paged_copy_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale
   return status_of(launch_copy(p, static_cast<hipStream_t>(stream)));
 }
 
+int paged_swap_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale,
+                      void *host_k, void *host_v, void *host_k_scale, void *host_v_scale,
+                      int32_t cache_dtype, int32_t num_blocks, int32_t num_host_blocks,
+                      const int32_t *block_pairs, int32_t num_pairs, int32_t to_host,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      void *stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || num_host_blocks < 0 || num_kv_heads <= 0 ||
+      (to_host != 0 && to_host != 1))
+    return PKV_EINVAL;
+  if (!valid_block_size(block_size)) return PKV_ENOTSUP;
+  if (head_dim != 64 && head_dim != 128) return PKV_ENOTSUP;
+  if (!is_cache_dtype(cache_dtype)) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !host_k || !host_v || !block_pairs) return PKV_EINVAL;
+  if (is_quant(cache_dtype) && (!k_scale || !v_scale || !host_k_scale || !host_v_scale))
+    return PKV_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(host_k, 16) ||
+      !aligned(host_v, 16) || !aligned(block_pairs, 4))
+    return PKV_EINVAL;
+  const int dev = check_device();
+  if (dev != PKV_OK) return dev;
+  SwapParams p{};
+  p.dev_k = static_cast<uint8_t *>(k_cache);
+  p.dev_v = static_cast<uint8_t *>(v_cache);
+  p.dev_ks = static_cast<uint16_t *>(k_scale);
+  p.dev_vs = static_cast<uint16_t *>(v_scale);
+  p.host_k = static_cast<uint8_t *>(host_k);
+  p.host_v = static_cast<uint8_t *>(host_v);
+  p.host_ks = static_cast<uint16_t *>(host_k_scale);
+  p.host_vs = static_cast<uint16_t *>(host_v_scale);
+  p.pairs = block_pairs;
+  p.num_pairs = num_pairs;
+  p.num_blocks = num_blocks;
+  p.num_host_blocks = num_host_blocks;
+  p.to_host = to_host;
+  p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(cache_dtype);
+  p.scale_elems = is_quant(cache_dtype) ? (int64_t)num_kv_heads * block_size : 0;
+  return status_of(launch_swap(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -60,6 +60,44 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
   }
 }
 
+// Whole-block copy between a device pool and a host pool (one workgroup per
+// pair): row [src, dst] of the pairs, device -> host when to_host, else
+// host -> device.  Out-of-range rows are skipped.
+__global__ __launch_bounds__(256) void swap_kernel(SwapParams p) {
+  const int32_t a = p.pairs[2 * blockIdx.x];
+  const int32_t b = p.pairs[2 * blockIdx.x + 1];
+  const int32_t dev = p.to_host ? a : b, host = p.to_host ? b : a;
+  if (dev < 0 || host < 0 || dev >= p.num_blocks || host >= p.num_host_blocks) return;
+  const int64_t n16 = p.block_bytes / 16;
+  u4 *dk = reinterpret_cast<u4 *>(p.dev_k + (size_t)dev * p.block_bytes);
+  u4 *dv = reinterpret_cast<u4 *>(p.dev_v + (size_t)dev * p.block_bytes);
+  u4 *hk = reinterpret_cast<u4 *>(p.host_k + (size_t)host * p.block_bytes);
+  u4 *hv = reinterpret_cast<u4 *>(p.host_v + (size_t)host * p.block_bytes);
+  const u4 *sk = p.to_host ? dk : hk;
+  const u4 *sv = p.to_host ? dv : hv;
+  u4 *tk = p.to_host ? hk : dk;
+  u4 *tv = p.to_host ? hv : dv;
+  for (int64_t e = threadIdx.x; e < n16; e += blockDim.x) {
+    tk[e] = sk[e];
+    tv[e] = sv[e];
+  }
+  if (p.scale_elems > 0) {
+    uint16_t *dks = p.dev_ks + (size_t)dev * p.scale_elems;
+    uint16_t *dvs = p.dev_vs + (size_t)dev * p.scale_elems;
+    uint16_t *hks = p.host_ks + (size_t)host * p.scale_elems;
+    uint16_t *hvs = p.host_vs + (size_t)host * p.scale_elems;
+    for (int64_t e = threadIdx.x; e < p.scale_elems; e += blockDim.x) {
+      if (p.to_host) {
+        hks[e] = dks[e];
+        hvs[e] = dvs[e];
+      } else {
+        dks[e] = hks[e];
+        dvs[e] = hvs[e];
+      }
+    }
+  }
+}
+
 template <int SRC, int KV, int D>
 hipError_t launch_write_bs(const WriteParams &p, hipStream_t stream) {
   dim3 grid(p.num_tokens, p.num_kv_heads);
@@ -100,6 +138,11 @@ hipError_t launch_write(const WriteParams &p, int src_dtype, int cache_dtype, in
 hipError_t launch_copy(const CopyParams &p, hipStream_t stream) {
   if (p.num_pairs == 0) return hipSuccess;
   hipLaunchKernelGGL(copy_kernel, dim3(p.num_pairs), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap(const SwapParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL(swap_kernel, dim3(p.num_pairs), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -184,6 +184,22 @@ hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipS
 hipError_t launch_prefill(const PrefixParams &p, int cache_dtype, int out_dtype, int head_dim,
                           int block_size, hipStream_t stream);
 
+// Block swap between device pools and device-addressable host pools.
+struct SwapParams {
+  uint8_t *dev_k, *dev_v;
+  uint16_t *dev_ks, *dev_vs;
+  uint8_t *host_k, *host_v;
+  uint16_t *host_ks, *host_vs;
+  const int32_t *pairs;
+  int num_pairs;
+  int num_blocks;
+  int num_host_blocks;
+  int to_host;
+  int64_t block_bytes;
+  int64_t scale_elems;
+};
+hipError_t launch_swap(const SwapParams &p, hipStream_t stream);
+
 hipError_t launch_write(const WriteParams &p, int src_dtype, int cache_dtype, int head_dim,
                         hipStream_t stream);
 hipError_t launch_copy(const CopyParams &p, hipStream_t stream);
