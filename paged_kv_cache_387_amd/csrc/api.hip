@@ -65,7 +65,7 @@ int32_t choose_part_tiles(int32_t max_blocks, int32_t block_size, int32_t reques
     pt = (mt + 3) / 4;
     if (pt < kMinPartTiles) pt = kMinPartTiles;
     if (pt > kMaxPartTiles) pt = kMaxPartTiles;
-    pt = (pt + kWaves - 1) / kWaves * kWaves;
+    pt = (pt + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
   }
   return pt >= mt ? (int32_t)mt : (int32_t)pt;
 }

@@ -65,7 +65,7 @@ template <> struct Prefetch<PKV_E4M3> { static constexpr int NB = PKV_PREFETCH_Q
 // row count): a 32-token block is two tiles stored one after the other, a
 // 16-token tile spans two 8-token blocks.
 template <int KV, int D, int OUT, int SRC, int BS>
-__global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_kernel(DecodeParams p) {
   constexpr int EB = Kv<KV>::EB;
   constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
   constexpr int SLICE = BS * D * EB;          // bytes of one (block, kv head) slice
@@ -79,9 +79,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   constexpr int NB = Prefetch<KV>::NB;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
 
-  __shared__ float lds_o[kWaves][kMaxGroup][LDS_ROW];
-  __shared__ float lds_m[kWaves][kMaxGroup];
-  __shared__ float lds_l[kWaves][kMaxGroup];
+  __shared__ float lds_o[kDecodeWaves][kMaxGroup][LDS_ROW];
+  __shared__ float lds_m[kDecodeWaves][kMaxGroup];
+  __shared__ float lds_l[kDecodeWaves][kMaxGroup];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -109,12 +109,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   const int first = part * p.part_tiles;      // first tile of the partition
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks;
 
-  // Table entries of this wave's tiles first + w + j * kWaves, 64 at a time,
+  // Table entries of this wave's tiles first + w + j * kDecodeWaves, 64 at a time,
   // one per lane (readlane picks entry j): the tile's block (the first of its
   // two blocks when SPLIT; tvb holds the second).  Entries are clamped to
   // `lim` blocks.
   auto load_tv = [&](int c0, int lim, int *tvb) {
-    const int tile = first + w + (c0 + lane) * kWaves;
+    const int tile = first + w + (c0 + lane) * kDecodeWaves;
     int e = SPLIT ? 2 * tile : tile / TPB;
     e = e < lim ? e : lim - 1;
     if constexpr (SPLIT) {
@@ -175,16 +175,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   const int npre = prefix_parts_of(p, s);   // shared-prefix partials (merged later)
   if (first >= ntile) {
     if (part == 0 && npre == 0) {  // empty sequence: zero output rows
-      for (int e = threadIdx.x; e < G * D; e += 64 * kWaves)
+      for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves)
         store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
     }
     return;
   }
   const int last = min(first + p.part_tiles, ntile);
 
-  // Tiles of this wave: first + w + k * kWaves, k < nt_w.
+  // Tiles of this wave: first + w + k * kDecodeWaves, k < nt_w.
   const int nt_part = last - first;
-  const int nt_w = nt_part > w ? (nt_part - w + kWaves - 1) / kWaves : 0;
+  const int nt_w = nt_part > w ? (nt_part - w + kDecodeWaves - 1) / kDecodeWaves : 0;
 
   // ---- fused step: copy-on-write of the tail block, then the new token ----
   // The partition that holds a sequence's tail block first copies that
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
       const int src = p.cow_src ? p.cow_src[s] : -1;
       if (tail_ok && (unsigned)src < (unsigned)p.num_blocks && src != phys) {
         const size_t sslice = ((size_t)src * p.num_kv_heads + kvh) * SLICE;
-        for (int o = threadIdx.x * 16; o < SLICE; o += 64 * kWaves * 16) {
+        for (int o = threadIdx.x * 16; o < SLICE; o += 64 * kDecodeWaves * 16) {
           *reinterpret_cast<u4 *>(p.k_cache_w + tail_slice + o) =
               *reinterpret_cast<const u4 *>(p.k_cache_w + sslice + o);
           *reinterpret_cast<u4 *>(p.v_cache_w + tail_slice + o) =
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   };
   if constexpr (SRC >= 0) {
     const int tail_tile = ntile - 1;
-    if (tail_ok && w == (tail_tile - first) % kWaves) {
+    if (tail_ok && w == (tail_tile - first) % kDecodeWaves) {
       // the tail tile is this wave's last, entry nt_w - 1 of its walk
       if (nt_w - 1 < Prefetch<KV>::NB)
         step_write();
@@ -440,12 +440,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   for (int c0 = 0; c0 < nt_w; c0 += 64) {
     const int nc = min(64, nt_w - c0);
     const int tv = tv_next, tvb = tvb_next;
-    const int t0 = first + w + c0 * kWaves;   // tile of chunk entry 0
+    const int t0 = first + w + c0 * kDecodeWaves;   // tile of chunk entry 0
     Tile ring[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int jj = j < nc ? j : nc - 1;
-      issue(tv, tvb, jj, t0 + jj * kWaves, ring[j]);
+      issue(tv, tvb, jj, t0 + jj * kDecodeWaves, ring[j]);
     }
     if (step_pending) {   // overlaps with the loads just issued
       step_write();
@@ -455,20 +455,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
     for (; k0 + 2 * NB <= nc; k0 += NB) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        consume(t0 + (k0 + j) * kWaves, ring[j]);
-        issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kWaves, ring[j]);
+        consume(t0 + (k0 + j) * kDecodeWaves, ring[j]);
+        issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kDecodeWaves, ring[j]);
       }
     }
     // last round: the ring holds entries k0 .. k0+NB-1 (those < nc), at most
     // NB - 1 further entries remain to be loaded
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (k0 + j < nc) consume(t0 + (k0 + j) * kWaves, ring[j]);
-      if (k0 + j + NB < nc) issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kWaves, ring[j]);
+      if (k0 + j < nc) consume(t0 + (k0 + j) * kDecodeWaves, ring[j]);
+      if (k0 + j + NB < nc) issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kDecodeWaves, ring[j]);
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      if (k0 + NB + j < nc) consume(t0 + (k0 + NB + j) * kWaves, ring[j]);
+      if (k0 + NB + j < nc) consume(t0 + (k0 + NB + j) * kDecodeWaves, ring[j]);
     if (c0 + 64 < nt_w) tv_next = load_tv(c0 + 64, p.max_blocks, &tvb_next);
   }
 
@@ -492,14 +492,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_kernel(DecodeParams p) 
   __syncthreads();
 
   const bool direct = nparts_s == 1 && npre == 0;
-  for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) {
+  for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
     const int hh = e / D, d = e % D;
     float M = lds_m[0][hh];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, lds_m[ww][hh]);
+    for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, lds_m[ww][hh]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < kDecodeWaves; ++ww) {
       const float c = exp2f(lds_m[ww][hh] - M);
       num += c * lds_o[ww][hh][d];
       den += c * lds_l[ww][hh];
@@ -635,7 +635,7 @@ template <int KV, int D, int OUT, int SRC, int BS>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = decode_grid(p.num_units, p.num_parts);
   hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS>), dim3((unsigned)grid),
-                     dim3(64 * kWaves), 0, stream, p);
+                     dim3(64 * kDecodeWaves), 0, stream, p);
   hipError_t err = hipGetLastError();
   // with shared prefixes the caller launches the merge after the prefix pass
   if (err != hipSuccess || p.num_parts <= 1 || p.seq_group) return err;

@@ -14,7 +14,11 @@ constexpr int kTile = 16;        // tokens per decode tile (the MFMA row count)
 #ifndef PKV_WAVES
 #define PKV_WAVES 4
 #endif
-constexpr int kWaves = PKV_WAVES;  // wavefronts per decode workgroup
+constexpr int kWaves = PKV_WAVES;  // wavefronts per workgroup of the multi-query passes
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PKV_DECODE_WAVES;   // wavefronts per decode workgroup
 constexpr int kMaxGroup = 16;    // query heads per kv head (MFMA column count)
 constexpr int kXcds = 8;         // accelerator complex dies: workgroup i runs on die i % 8
 
