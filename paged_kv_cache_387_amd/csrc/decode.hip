@@ -167,6 +167,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     qbias = kI8Bias * qs;
   }
 
+  int cow_req = -1;   // fused step: the block to copy into the tail block, if any
+  if constexpr (SRC >= 0) cow_req = p.cow_src ? p.cow_src[s] : -1;
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.max_blocks * BS ? p.max_blocks * BS : L);
   const int nblk = (L + BS - 1) / BS;                 // blocks in use
@@ -186,71 +188,158 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   const int nt_part = last - first;
   const int nt_w = nt_part > w ? (nt_part - w + kDecodeWaves - 1) / kDecodeWaves : 0;
 
-  // ---- fused step: copy-on-write of the tail block, then the new token ----
-  // The partition that holds a sequence's tail block first copies that
-  // block's (kv head) slice from cow_src[s] when asked -- all threads of the
-  // workgroup, then a barrier, since with 32-token blocks another wave reads
-  // the other tile of the block.  The wave that consumes the tail tile then
-  // writes the new token at position L - 1 and waits for its stores before it
-  // issues the load of that tile, so the load sees them; when the tail tile is
-  // not among the wave's first NB loads, the write overlaps with those loads.
+  // ---- fused step: the new token, written behind ----
+  // The partition that holds a sequence's tail tile also stores the new token
+  // at position L - 1, after giving the tail block the contents of block
+  // cow_src[s] when that names another block.  Nothing waits for these stores:
+  //  * the tail block's tiles are read from the copy source, whose bytes the
+  //    copy reproduces;
+  //  * the wave that consumes the tail tile (the last tile of its walk) keeps
+  //    the token's stored form in LDS and puts it in place of slot L - 1 of
+  //    the loaded tile;
+  //  * that wave stores the token and does the copy after its tiles, merging
+  //    the new token into the chunks it copies, so where the copy and the
+  //    token's own stores meet they write equal bytes and their order does
+  //    not matter.  (Stores issued among the walk's loads would make every
+  //    later wait for a load a wait for all memory operations.)
   // Other sequences may read the copy source concurrently; nothing else
   // writes these bytes.
+  const int tail_tile = ntile - 1;
   const int tail_blk = nblk - 1;
+  const int new_row = (L - 1) % kTile;   // row of the new token in the tail tile
+  const int new_slot = (L - 1) % BS;     // its slot in the tail block
+  // The first loads of K/V depend on nothing here but cow_src[s] (read with
+  // seq_lens): the tail block's own table entry is read after they are issued.
+  const bool tail_here = SRC >= 0 && tail_tile >= first && tail_tile < last;
+  const int cow_from = tail_here && (unsigned)cow_req < (unsigned)p.num_blocks ? cow_req : -1;
+  const bool step_wave = tail_here && w == (tail_tile - first) % kDecodeWaves;
+  bool tail_ok = false;                  // the tail block's table entry is in the pool
+  int tail_phys = 0;
   size_t tail_slice = 0, tail_sc = 0;
-  bool tail_ok = false;
+  constexpr int NEWB = SRC >= 0 ? D * EB : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_new[2][NEWB];   // stored K, V rows
+  __shared__ uint16_t lds_new_sc[2];
+  float new_x[2][D / 64];
   if constexpr (SRC >= 0) {
-    const int tail_tile = ntile - 1;
-    if (tail_tile >= first && tail_tile < last) {
-      const int phys = trow[tail_blk];
-      tail_ok = (unsigned)phys < (unsigned)p.num_blocks;
-      tail_slice = ((size_t)(tail_ok ? phys : 0) * p.num_kv_heads + kvh) * SLICE;
-      tail_sc = ((size_t)(tail_ok ? phys : 0) * p.num_kv_heads + kvh) * BS;
-      const int src = p.cow_src ? p.cow_src[s] : -1;
-      if (tail_ok && (unsigned)src < (unsigned)p.num_blocks && src != phys) {
-        const size_t sslice = ((size_t)src * p.num_kv_heads + kvh) * SLICE;
-        for (int o = threadIdx.x * 16; o < SLICE; o += 64 * kDecodeWaves * 16) {
-          *reinterpret_cast<u4 *>(p.k_cache_w + tail_slice + o) =
-              *reinterpret_cast<const u4 *>(p.k_cache_w + sslice + o);
-          *reinterpret_cast<u4 *>(p.v_cache_w + tail_slice + o) =
-              *reinterpret_cast<const u4 *>(p.v_cache_w + sslice + o);
-        }
-        if constexpr (QUANT) {
-          const size_t ssc = ((size_t)src * p.num_kv_heads + kvh) * BS;
-          if (threadIdx.x < BS) {
-            p.k_scale_w[tail_sc + threadIdx.x] = p.k_scale_w[ssc + threadIdx.x];
-            p.v_scale_w[tail_sc + threadIdx.x] = p.v_scale_w[ssc + threadIdx.x];
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // the copy lands before anyone reads the block
-        __syncthreads();
-      }
-    }
-  }
-  bool step_pending = false;
-  auto step_write = [&]() {
-    if constexpr (SRC >= 0) {
-      const int t = (L - 1) % BS;
+    if (step_wave) {
       constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
       const size_t row = ((size_t)s * p.num_kv_heads + kvh) * D * esz;
-      write_token_wave<SRC, KV, D, BS>(static_cast<const uint8_t *>(p.key_new) + row,
-                                       static_cast<const uint8_t *>(p.value_new) + row,
-                                       p.k_cache_w + tail_slice, p.v_cache_w + tail_slice,
-                                       QUANT ? p.k_scale_w + tail_sc + t : nullptr,
-                                       QUANT ? p.v_scale_w + tail_sc + t : nullptr, t, lane);
-      __builtin_amdgcn_s_waitcnt(0);     // stores complete before the tail tile is loaded
-    }
-  };
-  if constexpr (SRC >= 0) {
-    const int tail_tile = ntile - 1;
-    if (tail_ok && w == (tail_tile - first) % kDecodeWaves) {
-      // the tail tile is this wave's last, entry nt_w - 1 of its walk
-      if (nt_w - 1 < Prefetch<KV>::NB)
-        step_write();
-      else
-        step_pending = true;
+      load_token<SRC, D>(static_cast<const uint8_t *>(p.key_new) + row,
+                         static_cast<const uint8_t *>(p.value_new) + row, new_x, lane);
     }
   }
+  // Right after the wave's first loads: encode the new token and keep its
+  // row-order bytes in LDS.  (A tail entry outside the pool writes nothing;
+  // its tile is skipped.)
+  auto step_write = [&]() {
+    if constexpr (SRC >= 0) {
+      constexpr int PER = D / 64;
+      tail_phys = trow[tail_blk];
+      tail_ok = (unsigned)tail_phys < (unsigned)p.num_blocks;
+      if (!tail_ok) return;
+      tail_slice = ((size_t)tail_phys * p.num_kv_heads + kvh) * SLICE;
+      tail_sc = ((size_t)tail_phys * p.num_kv_heads + kvh) * BS;
+      const TokenCodes<D> tc = encode_token<KV, D>(new_x);
+#pragma unroll
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          uint8_t *dst = &lds_new[which][(lane * PER + k) * EB];
+          if constexpr (EB == 4) *reinterpret_cast<uint32_t *>(dst) = tc.c[which][k];
+          else if constexpr (EB == 2) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)tc.c[which][k];
+          else *dst = (uint8_t)tc.c[which][k];
+        }
+      if (lane == 0) {
+        lds_new_sc[0] = tc.sc[0];
+        lds_new_sc[1] = tc.sc[1];
+      }
+    }
+  };
+  // After the wave's tiles: the new token's stores (from the staged row), and
+  // the copy.  Issued after the last load of the walk, so no wait for a load
+  // ever has a store before it, and nothing waits for these stores.
+  auto step_store = [&]() {
+    if constexpr (SRC >= 0) {
+      constexpr int PER = D / 64;
+      TokenCodes<D> tc;
+#pragma unroll
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const uint8_t *src = &lds_new[which][(lane * PER + k) * EB];
+          if constexpr (EB == 4) tc.c[which][k] = *reinterpret_cast<const uint32_t *>(src);
+          else if constexpr (EB == 2) tc.c[which][k] = *reinterpret_cast<const uint16_t *>(src);
+          else tc.c[which][k] = *src;
+        }
+      tc.sc[0] = lds_new_sc[0];
+      tc.sc[1] = lds_new_sc[1];
+      store_token<KV, D, BS>(tc, p.k_cache_w + tail_slice, p.v_cache_w + tail_slice,
+                             QUANT ? p.k_scale_w + tail_sc + new_slot : nullptr,
+                             QUANT ? p.v_scale_w + tail_sc + new_slot : nullptr, new_slot, lane);
+    }
+  };
+  // The copy (its registers are free after the tiles).
+  auto cow_copy = [&]() {
+    if constexpr (SRC >= 0) {
+      // copy the slice 16 bytes at a time; chunks that hold bytes of slot
+      // new_slot take them from the staged row
+      const size_t sslice = ((size_t)cow_from * p.num_kv_heads + kvh) * SLICE;
+      constexpr int CHUNKS = SLICE / 16;
+      constexpr int TILE_CH = TB * D * EB / 16;   // chunks per stored tile
+      constexpr int ROUND = 4;                    // chunks per lane in flight
+      for (int q0 = 0; q0 < CHUNKS; q0 += 64 * ROUND) {
+        u4 ck[ROUND], cv[ROUND];
+#pragma unroll
+        for (int k = 0; k < ROUND; ++k) {
+          const int q = q0 + 64 * k + lane;
+          if (q < CHUNKS) {
+            ck[k] = *reinterpret_cast<const u4 *>(p.k_cache_w + sslice + 16 * (size_t)q);
+            cv[k] = *reinterpret_cast<const u4 *>(p.v_cache_w + sslice + 16 * (size_t)q);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < ROUND; ++k) {
+          const int q = q0 + 64 * k + lane;
+          if (q >= CHUNKS) continue;
+          const int tb = q / TILE_CH, tq = q % TILE_CH;   // stored tile, chunk in it
+          // K chunk: 16-byte column tq / TB of token tb*TB + tq % TB
+          if (tb * TB + tq % TB == new_slot)
+            ck[k] = *reinterpret_cast<const u4 *>(&lds_new[0][16 * (tq / TB)]);
+          if constexpr (EB == 1) {
+            // V chunk: elements 4c .. 4c+3 of tokens tb*TB + 4u .. +3
+            const int c = tq / (TB / 4), u = tq % (TB / 4);
+            const int v0 = new_slot - (tb * TB + 4 * u);
+            if ((unsigned)v0 < 4u) {
+              const uint32_t nw = *reinterpret_cast<const uint32_t *>(&lds_new[1][4 * c]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                cv[k][e] = (cv[k][e] & ~(0xFFu << (8 * v0))) | (((nw >> (8 * e)) & 0xFFu) << (8 * v0));
+            }
+          } else {
+            // V chunk: 4-byte column c of tokens tb*TB + u0 .. +3
+            const int c = (4 * tq) / TB, u0 = (4 * tq) % TB;
+            const int v0 = new_slot - (tb * TB + u0);
+            if ((unsigned)v0 < 4u) {
+              const uint32_t nw = *reinterpret_cast<const uint32_t *>(&lds_new[1][4 * c]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) cv[k][e] = e == v0 ? nw : cv[k][e];
+            }
+          }
+          *reinterpret_cast<u4 *>(p.k_cache_w + tail_slice + 16 * (size_t)q) = ck[k];
+          *reinterpret_cast<u4 *>(p.v_cache_w + tail_slice + 16 * (size_t)q) = cv[k];
+        }
+      }
+      if constexpr (QUANT) {
+        const size_t ssc = ((size_t)cow_from * p.num_kv_heads + kvh) * BS;
+        if (lane < BS) {
+          const uint16_t ksc = lane == new_slot ? lds_new_sc[0] : p.k_scale_w[ssc + lane];
+          const uint16_t vsc = lane == new_slot ? lds_new_sc[1] : p.v_scale_w[ssc + lane];
+          p.k_scale_w[tail_sc + lane] = ksc;
+          p.v_scale_w[tail_sc + lane] = vsc;
+        }
+      }
+    }
+  };
 
   // ---- per-wave running state ----
   float m = -INFINITY;   // running max of column r (base-2 scaled scores)
@@ -276,9 +365,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   // block and 8-15 from the second.
   auto issue = [&](int tv, int tvb, int j, int tile, Tile &t) {
     int pa = __builtin_amdgcn_readlane(tv, j);
+    if (SRC >= 0 && cow_from >= 0 && (SPLIT ? 2 * tile : tile / TPB) == tail_blk &&
+        (unsigned)pa < (unsigned)p.num_blocks)
+      pa = cow_from;
     // with SPLIT, a second block past the sequence's end (its tokens are all
     // masked) is read from the first block instead
     int pb = SPLIT && 2 * tile + 1 < nblk ? __builtin_amdgcn_readlane(tvb, j) : pa;
+    if (SRC >= 0 && SPLIT && cow_from >= 0 && 2 * tile + 1 == tail_blk &&
+        (unsigned)pb < (unsigned)p.num_blocks)
+      pb = cow_from;
     t.ok = (unsigned)pa < (unsigned)p.num_blocks && (unsigned)pb < (unsigned)p.num_blocks;
     pa = t.ok ? pa : 0;
     pb = t.ok ? pb : 0;
@@ -311,6 +406,40 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
 
   // Fold tile `tile` (its data already loaded) into the running state.
   auto consume = [&](int tile, Tile &t) {
+    if constexpr (SRC >= 0) {
+      // the tail tile: slot L - 1 takes the new token as staged in LDS
+      if (step_wave && tile == tail_tile) {
+        if (r == new_row) {
+#pragma unroll
+          for (int i = 0; i < NL; ++i) t.k[i] = *reinterpret_cast<const u4 *>(&lds_new[0][16 * (4 * i + g)]);
+        }
+        const int v0 = new_row - 4 * g;   // word (2- and 4-byte V) or byte (1-byte V)
+        if ((unsigned)v0 < 4u) {
+#pragma unroll
+          for (int i = 0; i < NL; ++i) {
+            const uint32_t nw = *reinterpret_cast<const uint32_t *>(&lds_new[1][4 * (16 * i + r)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (EB == 1)
+                t.v[i][e] = (t.v[i][e] & ~(0xFFu << (8 * v0))) | (((nw >> (8 * e)) & 0xFFu) << (8 * v0));
+              else
+                t.v[i][e] = e == v0 ? nw : t.v[i][e];
+            }
+          }
+          if constexpr (QUANT) {
+            const uint32_t sh = 16 * (v0 & 1), keep = ~(0xFFFFu << sh);
+            const uint32_t nk = (uint32_t)lds_new_sc[0] << sh, nv = (uint32_t)lds_new_sc[1] << sh;
+            if (v0 < 2) {
+              t.ks[0] = (t.ks[0] & keep) | nk;
+              t.vs[0] = (t.vs[0] & keep) | nv;
+            } else {
+              t.ks[1] = (t.ks[1] & keep) | nk;
+              t.vs[1] = (t.vs[1] & keep) | nv;
+            }
+          }
+        }
+      }
+    }
     // q.K for the tile: S^T[token 4g+v][head r] in sc[v]
     f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -447,10 +576,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
       const int jj = j < nc ? j : nc - 1;
       issue(tv, tvb, jj, t0 + jj * kDecodeWaves, ring[j]);
     }
-    if (step_pending) {   // overlaps with the loads just issued
-      step_write();
-      step_pending = false;
-    }
+    if (c0 == 0 && step_wave) step_write();   // the ring's loads are in flight
     int k0 = 0;
     for (; k0 + 2 * NB <= nc; k0 += NB) {
 #pragma unroll
@@ -472,6 +598,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     if (c0 + 64 < nt_w) tv_next = load_tv(c0 + 64, p.max_blocks, &tvb_next);
   }
 
+  if (SRC >= 0 && step_wave && tail_ok) {
+    step_store();
+    if (cow_from >= 0 && cow_from != tail_phys) cow_copy();
+  }
+
   // ---- combine the waves through LDS ----
   if constexpr (KV == PKV_I8) {
 #pragma unroll
@@ -489,7 +620,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
 #pragma unroll
     for (int v = 0; v < 4; ++v) lds_o[w][r][E * (16 * i + 4 * g + v) + e] = acc[a][v];
   }
-  __syncthreads();
+  // A barrier for the LDS exchange only: the fused step's stores may still be
+  // in flight (nothing here reads them).
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   const bool direct = nparts_s == 1 && npre == 0;
   for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {

@@ -68,19 +68,20 @@ __device__ __forceinline__ size_t v_byte(int t, int j) {
     return tile + (size_t)((j >> 2) * TB + u) * 4 + (j & 3);
 }
 
-// One wavefront writes token slot t of the K and V slices of one (block, kv
-// head) of BS tokens: src rows k_row / v_row hold D elements of SRC type; the scale
-// pointers address the slot's fp16 scale (quantized caches only).  Lane l
-// owns elements l*D/64 .. (l+1)*D/64 - 1.  The source loads are issued before
-// anything else so they overlap.
-template <int SRC, int KV, int D, int BS>
-__device__ __forceinline__ void write_token_wave(const void *k_row, const void *v_row,
-                                                 uint8_t *k_tile, uint8_t *v_tile,
-                                                 uint16_t *k_scale, uint16_t *v_scale, int t,
-                                                 int lane) {
-  constexpr int EB = ebytes<KV>();
+// The stored form of one token's K and V vectors of one kv head: lane l owns
+// elements l*D/64 .. (l+1)*D/64 - 1 as codes of the cache type (fp32 bits,
+// fp16 bits or one byte), plus the two fp16 scales of quantized caches.
+template <int D> struct TokenCodes {
+  uint32_t c[2][D / 64];   // [K, V][element]
+  uint16_t sc[2];          // [K, V] fp16 scale bits (quantized caches)
+};
+
+// Loads lane l's elements of the source rows k_row / v_row (D elements of
+// SRC type) as fp32.
+template <int SRC, int D>
+__device__ __forceinline__ void load_token(const void *k_row, const void *v_row,
+                                           float (&xs)[2][D / 64], int lane) {
   constexpr int PER = D / 64;
-  float xs[2][PER];
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const void *src = which ? v_row : k_row;
@@ -93,20 +94,25 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
         xs[which][k] = (float)reinterpret_cast<const _Float16 *>(src)[d];
     }
   }
+}
+
+// Converts (fp32 / fp16 caches) or quantizes (int8 / E4M3, one scale per
+// vector) a token held as in load_token.  All 64 lanes take part.
+template <int KV, int D>
+__device__ __forceinline__ TokenCodes<D> encode_token(const float (&xs)[2][D / 64]) {
+  constexpr int PER = D / 64;
+  TokenCodes<D> tc;
+  tc.sc[0] = tc.sc[1] = 0;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const float *x = xs[which];
-    uint8_t *tile = which ? v_tile : k_tile;
-    if constexpr (KV == PKV_F32 || KV == PKV_F16) {
+    if constexpr (KV == PKV_F32) {
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int j = (lane * PER + k) * EB;
-        const size_t off = which ? v_byte<BS, D, EB>(t, j) : k_byte<BS, D, EB>(t, j);
-        if constexpr (KV == PKV_F32)
-          *reinterpret_cast<float *>(tile + off) = x[k];
-        else
-          *reinterpret_cast<_Float16 *>(tile + off) = (_Float16)x[k];
-      }
+      for (int k = 0; k < PER; ++k) tc.c[which][k] = __float_as_uint(x[k]);
+    } else if constexpr (KV == PKV_F16) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        tc.c[which][k] = __builtin_bit_cast(uint16_t, (_Float16)x[k]);
     } else {
       float a = 0.0f;
 #pragma unroll
@@ -117,7 +123,6 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
       const float s = (float)s16;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
-        const int j = lane * PER + k;
         uint32_t code = 0u;
         if (s != 0.0f) {
           const float y = x[k] / s;
@@ -126,11 +131,54 @@ __device__ __forceinline__ void write_token_wave(const void *k_row, const void *
           else
             code = e4m3_encode_sat(y);
         }
-        tile[which ? v_byte<BS, D, 1>(t, j) : k_byte<BS, D, 1>(t, j)] = (uint8_t)code;
+        tc.c[which][k] = code;
       }
-      if (lane == 0) *(which ? v_scale : k_scale) = __builtin_bit_cast(uint16_t, s16);
+      tc.sc[which] = __builtin_bit_cast(uint16_t, s16);
     }
   }
+  return tc;
+}
+
+// Stores an encoded token into slot t of the K and V slices of one (block, kv
+// head) of BS tokens; the scale pointers address the slot's fp16 scale
+// (quantized caches only).
+template <int KV, int D, int BS>
+__device__ __forceinline__ void store_token(const TokenCodes<D> &tc, uint8_t *k_tile,
+                                            uint8_t *v_tile, uint16_t *k_scale,
+                                            uint16_t *v_scale, int t, int lane) {
+  constexpr int EB = ebytes<KV>();
+  constexpr int PER = D / 64;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    uint8_t *tile = which ? v_tile : k_tile;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int j = (lane * PER + k) * EB;
+      const size_t off = which ? v_byte<BS, D, EB>(t, j) : k_byte<BS, D, EB>(t, j);
+      if constexpr (EB == 4)
+        *reinterpret_cast<uint32_t *>(tile + off) = tc.c[which][k];
+      else if constexpr (EB == 2)
+        *reinterpret_cast<uint16_t *>(tile + off) = (uint16_t)tc.c[which][k];
+      else
+        tile[off] = (uint8_t)tc.c[which][k];
+    }
+    if constexpr (EB == 1)
+      if (lane == 0) *(which ? v_scale : k_scale) = tc.sc[which];
+  }
+}
+
+// One wavefront writes token slot t of the K and V slices of one (block, kv
+// head) of BS tokens: src rows k_row / v_row hold D elements of SRC type; the
+// scale pointers address the slot's fp16 scale (quantized caches only).  The
+// source loads are issued before anything else so they overlap.
+template <int SRC, int KV, int D, int BS>
+__device__ __forceinline__ void write_token_wave(const void *k_row, const void *v_row,
+                                                 uint8_t *k_tile, uint8_t *v_tile,
+                                                 uint16_t *k_scale, uint16_t *v_scale, int t,
+                                                 int lane) {
+  float xs[2][D / 64];
+  load_token<SRC, D>(k_row, v_row, xs, lane);
+  store_token<KV, D, BS>(encode_token<KV, D>(xs), k_tile, v_tile, k_scale, v_scale, t, lane);
 }
 
 // One wavefront copies `bytes` (a multiple of 16) from src to dst with

@@ -86,7 +86,16 @@ STEP = {
     "c5_cow_f16": lambda bs: workloads.with_block_size(
         workloads.c5_shared_prefix(num_seqs=8, prefix=96, suffix_lo=1, suffix_hi=47,
                                    cow_pairs=True, H=16, Hkv=2, D=128, num_blocks=96), bs),
+    "c5_cow_e4m3": lambda bs: workloads.with_block_size(_c5_e4m3(), bs),
 }
+
+
+def _c5_e4m3():
+    w = workloads.c5_shared_prefix(num_seqs=8, prefix=96, suffix_lo=1, suffix_hi=47,
+                                   cow_pairs=True, H=16, Hkv=2, D=128, num_blocks=96)
+    w.cache_dtype = "e4m3"
+    w.name += "_e4m3"
+    return w
 
 
 @pytest.mark.parametrize("bs", BS)

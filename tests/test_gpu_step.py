@@ -30,6 +30,10 @@ STEP_CASES = {
     "e4m3_d64_g4": _ragged("e4m3", D=64, H=8, Hkv=2),
     "mha_f16": _ragged("f16", H=4, Hkv=4),
     "long_f16": _ragged("f16", lens=(1500, 2047, 2048), H=8, Hkv=1),
+    # the new token lands on every row of its 16-token tile
+    "rows_f16": _ragged("f16", lens=tuple(range(16, 32)) + (100,)),
+    "rows_i8": _ragged("i8", lens=tuple(range(16, 32)) + (100,)),
+    "rows_f32": _ragged("f32", D=64, H=8, Hkv=2, lens=tuple(range(16, 32))),
     "c5_small": lambda: workloads.c5_shared_prefix(num_seqs=6, prefix=160, suffix_lo=5,
                                                    suffix_hi=40, H=16, Hkv=2, D=128,
                                                    num_blocks=96),
