@@ -75,6 +75,33 @@ int32_t num_parts_of(int32_t max_blocks, int32_t block_size, int32_t part_tiles)
   return odd_up((int32_t)((mt + part_tiles - 1) / part_tiles));
 }
 
+// Runs of partitions.  A partition sets the granularity of the partial
+// results; a workgroup need not stop at its end.  When partitions are whole
+// multiples of the wave count, one workgroup walks `run_parts` consecutive
+// partitions of its unit, keeping its load ring primed across their
+// boundaries and emitting one partial per partition: a run spans about as
+// many tiles as an automatic partition would, so small explicit partitions
+// keep the long per-workgroup walks that stream well.  The run's finished
+// partials wait in LDS (stage_floats) until its last load has been issued.
+int32_t choose_run_parts(int32_t max_blocks, int32_t block_size, int32_t part_tiles,
+                         int32_t group, int32_t head_dim) {
+  if (part_tiles <= 0 || part_tiles % kDecodeWaves) return 1;
+  const int64_t mt = max_tiles_of(max_blocks, block_size);
+  const int64_t parts = (mt + part_tiles - 1) / part_tiles;
+  int64_t rp = choose_part_tiles(max_blocks, block_size, 0) / part_tiles;
+  const int64_t cap = 1 + stage_floats(head_dim) / ((int64_t)group * (head_dim + 1));
+  if (rp > cap) rp = cap;
+  if (rp > parts) rp = parts;
+  return rp < 1 ? 1 : (int32_t)rp;
+}
+
+int32_t num_runs_of(int32_t max_blocks, int32_t block_size, int32_t part_tiles,
+                    int32_t run_parts) {
+  const int64_t mt = max_tiles_of(max_blocks, block_size);
+  const int64_t parts = (mt + part_tiles - 1) / part_tiles;
+  return odd_up((int32_t)((parts + run_parts - 1) / run_parts));
+}
+
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Workspace: [partial outputs][partial lse], each part 256-byte aligned.
@@ -316,6 +343,9 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   p.block_size = block_size;
   p.part_tiles = pt;
   p.num_parts = parts;
+  p.run_parts = choose_run_parts(max_blocks_per_seq, block_size, pt, num_heads / num_kv_heads,
+                                 head_dim);
+  p.num_runs = num_runs_of(max_blocks_per_seq, block_size, pt, p.run_parts);
   p.ws_stride = parts + extra_parts;
   p.ws_pre = parts;
   p.num_units = num_seqs * num_kv_heads;

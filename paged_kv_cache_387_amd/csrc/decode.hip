@@ -9,9 +9,11 @@
 // log-sum-exp reduction ("partial accumulate, then merge" of paged_attention_v2,
 // "vLLM PagedAttention deep dive", jsqmd.com, section 4.1).
 //
-// Work decomposition.  One workgroup = 4 wavefronts handles one (partition,
-// kv head, sequence).  Wave w takes blocks first+w, first+w+4, ... of the
-// partition.  For one 16-token block a wave computes
+// Work decomposition.  One workgroup = 4 wavefronts handles one (run of
+// partitions, kv head, sequence); a run is one partition, or several
+// consecutive ones when their size is a multiple of 4 tiles (each still ends
+// in its own partial).  Wave w takes blocks first+w, first+w+4, ... of the
+// run.  For one 16-token block a wave computes
 //   S^T[t][h] = K[t] . q[h]      one 16x16 MFMA tile: rows = the block's 16
 //                                 tokens, columns = the G <= 16 query heads of
 //                                 the GQA group (columns >= G have q = 0)
@@ -82,31 +84,40 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   __shared__ float lds_o[kDecodeWaves][kMaxGroup][LDS_ROW];
   __shared__ float lds_m[kDecodeWaves][kMaxGroup];
   __shared__ float lds_l[kDecodeWaves][kMaxGroup];
+  // finished partials of the run's earlier partitions: [partition][head][D + 1]
+  __shared__ float lds_stage[stage_floats(D)];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int r = lane & 15;
   const int g = lane >> 4;
 
-  // Workgroup -> (unit, partition).  Workgroups are dealt to the dies round
+  // Workgroup -> (unit, run of partitions).  Workgroups are dealt to the dies round
   // robin, so unit u runs on die u % kXcds (with 8 kv heads: one kv head per
   // die, whose L2 then serves the blocks that sequences share).  Ids go
   // partition-major: workgroups resident together work on the same region of
   // their sequences, so a shared prefix is read while it is still cached.
-  // The unit-group count is odd (unit_groups), so the partitions of one unit
-  // land on different compute units.
+  // The unit-group count is odd (unit_groups), so the runs of one unit land
+  // on different compute units.
   const int bid = blockIdx.x;
   const int die_slot = bid / kXcds;
   const int ugroups = unit_groups(p.num_units);
-  const int part = die_slot / ugroups;
+  const int run = die_slot / ugroups;
   const int u = (die_slot % ugroups) * kXcds + bid % kXcds;
   if (u >= p.num_units) return;
   const int s = u / p.num_kv_heads;
   const int kvh = u - s * p.num_kv_heads;
   const int G = p.group;
   const int H = p.num_heads;
+  // A run of several partitions needs partitions of whole wave rounds (every
+  // wave then ends each partition but the last at the same step) and room
+  // for its staged partials; the host only sets up such runs.
+  if (p.run_parts > 1 && (p.part_tiles % kDecodeWaves != 0 ||
+                          (p.run_parts - 1) * G * (D + 1) > stage_floats(D)))
+    return;
 
-  const int first = part * p.part_tiles;      // first tile of the partition
+  const int part0 = run * p.run_parts;        // first partition of the run
+  const int first = part0 * p.part_tiles;     // first tile of the run
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks;
 
   // Table entries of this wave's tiles first + w + j * kDecodeWaves, 64 at a time,
@@ -176,17 +187,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   const int nparts_s = (ntile + p.part_tiles - 1) / p.part_tiles;
   const int npre = prefix_parts_of(p, s);   // shared-prefix partials (merged later)
   if (first >= ntile) {
-    if (part == 0 && npre == 0) {  // empty sequence: zero output rows
+    if (run == 0 && npre == 0) {  // empty sequence: zero output rows
       for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves)
         store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
     }
     return;
   }
-  const int last = min(first + p.part_tiles, ntile);
+  const int last = min(first + p.run_parts * p.part_tiles, ntile);
 
   // Tiles of this wave: first + w + k * kDecodeWaves, k < nt_w.
   const int nt_part = last - first;
   const int nt_w = nt_part > w ? (nt_part - w + kDecodeWaves - 1) / kDecodeWaves : 0;
+  // Partitions of the run.  Every one but the last is full, and with
+  // part_tiles a multiple of the wave count each wave walks exactly
+  // tpw = part_tiles / kDecodeWaves of its tiles: partition j of the run ends
+  // for every wave after its step (j + 1) * tpw - 1.
+  const int nparts_run = (nt_part + p.part_tiles - 1) / p.part_tiles;
+  const int tpw = p.part_tiles / kDecodeWaves;
 
   // ---- fused step: the new token, written behind ----
   // The partition that holds a sequence's tail tile also stores the new token
@@ -560,6 +577,72 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     }
   };
 
+  // ---- ends of partitions ----
+  // The waves' states go to LDS (the barrier waits for LDS only: loads and
+  // the fused step's stores may be in flight), and combine() merges the four
+  // of element (head hh, dim d) into the normalized output and its base-2
+  // log-sum-exp (M + log2 den).
+  auto publish = [&]() {
+    if constexpr (KV == PKV_I8) {
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) acc[a] -= kI8Bias * accp;
+    }
+    float lt = l + xor16(l);
+    lt += xor32(lt);
+    if (g == 0) {
+      lds_m[w][r] = m;
+      lds_l[w][r] = lt;
+    }
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) {
+      const int i = a / E, e = a % E;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) lds_o[w][r][E * (16 * i + 4 * g + v) + e] = acc[a][v];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto combine = [&](int hh, int d, float &o, float &M, float &den) {
+    M = lds_m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, lds_m[ww][hh]);
+    float num = 0.f;
+    den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecodeWaves; ++ww) {
+      const float c = exp2f(lds_m[ww][hh] - M);
+      num += c * lds_o[ww][hh][d];
+      den += c * lds_l[ww][hh];
+    }
+    o = num / den;
+    if constexpr (QUANT) o *= (1.0f / kPvBoost);
+  };
+  // A partition of the run other than its last ends: its partial goes to
+  // lds_stage (thread t keeps elements t, t + 64 * kDecodeWaves, ... and
+  // stores them itself after the walk), and the state restarts.  All waves
+  // reach this at the same step; the second barrier frees lds_o for the next.
+  int flush_at = nparts_run > 1 ? tpw - 1 : -1;   // step that ends partition `staged`
+  int staged = 0;
+  auto end_partition = [&](int k) {
+    if (__builtin_expect(k != flush_at, 1)) return;
+    publish();
+    for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
+      const int hh = e / D, d = e % D;
+      float o, M, den;
+      combine(hh, d, o, M, den);
+      float *row = lds_stage + (staged * G + hh) * (D + 1);
+      row[d] = o;
+      if (d == 0) row[D] = M + log2f(den);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
+    accp = f4{0.f, 0.f, 0.f, 0.f};
+    ++staged;
+    flush_at = staged < nparts_run - 1 ? flush_at + tpw : -1;
+  };
+
   // ---- tile loop: a ring of NB tiles, each refilled right after use ----
   // The wave's tiles are walked in chunks of up to 64 (one table entry per
   // lane).  Within a chunk the steady-state rounds issue every load
@@ -583,6 +666,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
       for (int j = 0; j < NB; ++j) {
         consume(t0 + (k0 + j) * kDecodeWaves, ring[j]);
         issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kDecodeWaves, ring[j]);
+        end_partition(c0 + k0 + j);
       }
     }
     // last round: the ring holds entries k0 .. k0+NB-1 (those < nc), at most
@@ -591,10 +675,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     for (int j = 0; j < NB; ++j) {
       if (k0 + j < nc) consume(t0 + (k0 + j) * kDecodeWaves, ring[j]);
       if (k0 + j + NB < nc) issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kDecodeWaves, ring[j]);
+      if (k0 + j < nc) end_partition(c0 + k0 + j);
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (k0 + NB + j < nc) consume(t0 + (k0 + NB + j) * kDecodeWaves, ring[j]);
+    for (int j = 0; j < NB; ++j) {
+      if (k0 + NB + j < nc) {
+        consume(t0 + (k0 + NB + j) * kDecodeWaves, ring[j]);
+        end_partition(c0 + k0 + NB + j);
+      }
+    }
     if (c0 + 64 < nt_w) tv_next = load_tv(c0 + 64, p.max_blocks, &tvb_next);
   }
 
@@ -603,42 +692,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     if (cow_from >= 0 && cow_from != tail_phys) cow_copy();
   }
 
-  // ---- combine the waves through LDS ----
-  if constexpr (KV == PKV_I8) {
-#pragma unroll
-    for (int a = 0; a < NACC; ++a) acc[a] -= kI8Bias * accp;
-  }
-  l += xor16(l);
-  l += xor32(l);
-  if (g == 0) {
-    lds_m[w][r] = m;
-    lds_l[w][r] = l;
-  }
-#pragma unroll
-  for (int a = 0; a < NACC; ++a) {
-    const int i = a / E, e = a % E;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) lds_o[w][r][E * (16 * i + 4 * g + v) + e] = acc[a][v];
-  }
-  // A barrier for the LDS exchange only: the fused step's stores may still be
-  // in flight (nothing here reads them).
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
+  // ---- the run's last partition: combine the waves through LDS ----
+  publish();
   const bool direct = nparts_s == 1 && npre == 0;
+  const int part = part0 + nparts_run - 1;
   for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
     const int hh = e / D, d = e % D;
-    float M = lds_m[0][hh];
-#pragma unroll
-    for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, lds_m[ww][hh]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kDecodeWaves; ++ww) {
-      const float c = exp2f(lds_m[ww][hh] - M);
-      num += c * lds_o[ww][hh][d];
-      den += c * lds_l[ww][hh];
-    }
-    float o = num / den;
-    if constexpr (QUANT) o *= (1.0f / kPvBoost);
+    float o, M, den;
+    combine(hh, d, o, M, den);
     const int h = kvh * G + hh;
     if (direct) {
       store_out<OUT>(p.out, ((size_t)s * H + h) * D + d, o);
@@ -646,6 +707,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
       const size_t row = ((size_t)s * H + h) * p.ws_stride + part;
       p.ws_o[row * D + d] = o;
       if (d == 0) p.ws_lse[row] = M + log2f(den);
+    }
+  }
+  // the staged partials of the run's earlier partitions (each thread stores
+  // the elements it staged)
+  for (int j = 0; j < nparts_run - 1; ++j) {
+    for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
+      const int hh = e / D, d = e % D;
+      const float *src = lds_stage + (j * G + hh) * (D + 1);
+      const size_t row = ((size_t)s * H + kvh * G + hh) * p.ws_stride + part0 + j;
+      p.ws_o[row * D + d] = src[d];
+      if (d == 0) p.ws_lse[row] = src[D];
     }
   }
 }
@@ -766,7 +838,7 @@ hipError_t launch_merge_d(const DecodeParams &p, hipStream_t stream) {
 
 template <int KV, int D, int OUT, int SRC, int BS>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
-  const int64_t grid = decode_grid(p.num_units, p.num_parts);
+  const int64_t grid = decode_grid(p.num_units, p.num_runs);
   hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS>), dim3((unsigned)grid),
                      dim3(64 * kDecodeWaves), 0, stream, p);
   hipError_t err = hipGetLastError();

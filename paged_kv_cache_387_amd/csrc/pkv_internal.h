@@ -45,7 +45,10 @@ struct DecodeParams {
   int group;        // num_heads / num_kv_heads
   int block_size;   // tokens per physical block: 8, 16 or 32
   int part_tiles;   // 16-token tiles per partition (whole blocks)
-  int num_parts;    // partitions in the grid (>= ceil(max tokens / 16 / part_tiles))
+  int num_parts;    // partition slots per (sequence, head) workspace row (>= ceil(max tokens / 16 / part_tiles))
+  int run_parts;    // consecutive partitions one workgroup walks (>= 1; > 1 only when
+                    // part_tiles is a multiple of kDecodeWaves)
+  int num_runs;     // run slots per unit in the grid (>= ceil(partitions / run_parts))
   int num_units;    // num_seqs * num_kv_heads
   float qk_scale;   // scale * log2(e): scores are kept in base 2
   // Fused decode step only: the new token of each sequence (row s of
@@ -139,10 +142,17 @@ __host__ __device__ inline int odd_up(int n) { return n > 1 && n % 2 == 0 ? n + 
 // Unit groups per die: units are dealt to dies u % kXcds.
 __host__ __device__ inline int unit_groups(int num_units) { return odd_up((num_units + kXcds - 1) / kXcds); }
 
-// Grid of the decode kernel: one workgroup per (unit group, die, partition).
-inline int64_t decode_grid(int num_units, int num_parts) {
-  return (int64_t)unit_groups(num_units) * kXcds * num_parts;
+// Grid of the decode kernel: one workgroup per (unit group, die, run of
+// partitions).
+inline int64_t decode_grid(int num_units, int num_runs) {
+  return (int64_t)unit_groups(num_units) * kXcds * num_runs;
 }
+
+// LDS floats a decode workgroup sets aside for the finished partials of a
+// run (all but its last partition, which is stored directly): (D + 1) floats
+// (the normalized output row and its log-sum-exp) per query head and staged
+// partition.  Room for 7 partitions of 8 heads.
+__host__ __device__ constexpr int stage_floats(int head_dim) { return 7 * 8 * (head_dim + 1); }
 
 struct WriteParams {
   const void *key;
