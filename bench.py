@@ -163,7 +163,8 @@ def pmc_copy(nbytes: int = 1 << 30, reps: int = 5) -> int:
 
 # Sources that determine what one paged_attention_decode call moves: the
 # counter-based traffic figure is used only while these are unchanged.
-DECODE_SOURCES = ("decode.hip", "api.hip", "pkv_internal.h")
+DECODE_SOURCES = ("decode_kernel.h", "decode.hip", "decode_runs.hip", "api.hip",
+                  "pkv_internal.h")
 
 
 def decode_source_hash() -> str:
@@ -458,6 +459,75 @@ def bench_swap(args, torch, pkv) -> int:
     return 0
 
 
+def bench_len_sweep(args, torch, pkv) -> int:
+    """Cost of one paged_attention_decode call at the Qwen3-32B layer shape
+    (32 sequences, 64 query / 8 kv heads, head_dim 128, fp16, 12480-block
+    pool) against the sequence length: every sequence gets the same length,
+    then the configuration's U[512, 768] mix.  Eight disjoint sets of block
+    tables (a seeded permutation of the pool) rotate, as in the main bench.
+    A straight-line fit over lengths >= 256 gives the fixed cost per call (the
+    intercept) and the streaming rate of the KV bytes beyond it (the slope)."""
+    S, H, HKV, D, NBLK, MAXB, R = 32, 64, 8, 128, 12480, 48, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(387)
+    cache = pkv.PagedKVCache(NBLK, HKV, D, "f16")
+    cache.k.view(torch.float16).normal_(generator=gen)
+    cache.v.view(torch.float16).normal_(generator=gen)
+    rng = np.random.default_rng(387)
+    perm = rng.permutation(NBLK)[: R * S * MAXB].reshape(R, S, MAXB).astype(np.int32)
+    tables = [torch.from_numpy(perm[r].copy()).cuda() for r in range(R)]
+    q = torch.randn(S, H, D, device="cuda", generator=gen).half()
+    out = torch.empty(S, H, D, device="cuda", dtype=torch.float16)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    n = max(R, args.steps)
+
+    def per_call_us(lens_np):
+        lens = torch.from_numpy(lens_np.astype(np.int32)).cuda()
+        for r in range(R):
+            pkv.paged_attention_decode(q, cache, tables[r], lens, scale, out=out)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                pkv.paged_attention_decode(q, cache, tables[i % R], lens, scale, out=out)
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+        return best
+
+    rows, fit_x, fit_y = [], [], []
+    for L in (0, 1, 16, 128, 256, 384, 512, 640, 768):
+        us = per_call_us(np.full(S, L))
+        kv = S * L * HKV * 2 * D * 2
+        rows.append({"len": L, "us": round(us, 3), "kv_gbs": round(kv / us / 1e3, 1)})
+        print(f"# len {L:4d}: {us:7.2f} us per call", file=sys.stderr, flush=True)
+        if L >= 256:
+            fit_x.append(kv)
+            fit_y.append(us)
+    mix = rng.integers(512, 769, S)
+    us = per_call_us(mix)
+    kv = int(mix.sum()) * HKV * 2 * D * 2
+    rows.append({"len": "U[512,768]", "us": round(us, 3), "kv_gbs": round(kv / us / 1e3, 1)})
+    slope, icept = np.polyfit(np.asarray(fit_x, np.float64), np.asarray(fit_y, np.float64), 1)
+    print(json.dumps({
+        "metric": "paged_attention_decode cost per call vs sequence length (C2 shape)",
+        "config": {"workload": "c2_shape_len_sweep", "num_seqs": S, "num_heads": H,
+                   "num_kv_heads": HKV, "head_dim": D, "kv_dtype": "f16", "pool_blocks": NBLK,
+                   "rotating_batches": R, "calls_per_graph": n},
+        "points": rows,
+        "fit_len_ge_256": {"fixed_us": round(float(icept), 3),
+                           "marginal_gbs": round(1e-3 / float(slope), 1)},
+    }), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +550,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--len-sweep", action="store_true",
+                    help="decode cost per call against sequence length at the C2 shape")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run the plain copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=4,
@@ -513,6 +585,8 @@ def main():
     torch.cuda.set_device(0)
     if args.pmc_copy:
         return pmc_copy()
+    if args.len_sweep:
+        return bench_len_sweep(args, torch, pkv)
     if args.workload == "prefill":
         return bench_prefill(args, torch, pkv, driver)
     if args.workload == "swap":

@@ -186,6 +186,10 @@ hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, 
                          hipStream_t stream);
 hipError_t launch_decode_step(const DecodeParams &p, int cache_dtype, int src_dtype,
                               int out_dtype, int head_dim, hipStream_t stream);
+// The decode kernel for run_parts > 1 (decode only, or the fused step when
+// `step`); the caller launches the merge.
+hipError_t launch_decode_runs(const DecodeParams &p, int cache_dtype, bool step, int out_dtype,
+                              int head_dim, hipStream_t stream);
 // Columns (query vectors) one prefix workgroup handles: 16 per MFMA chunk.
 inline int prefix_chunks(int cache_dtype) { return cache_dtype == PKV_F32 ? 2 : 4; }
 inline int64_t prefix_grid(const PrefixParams &p) {
