@@ -89,7 +89,7 @@ int32_t choose_run_parts(int32_t max_blocks, int32_t block_size, int32_t part_ti
   const int64_t mt = max_tiles_of(max_blocks, block_size);
   const int64_t parts = (mt + part_tiles - 1) / part_tiles;
   int64_t rp = choose_part_tiles(max_blocks, block_size, 0) / part_tiles;
-  const int64_t cap = 1 + stage_floats(head_dim) / ((int64_t)group * (head_dim + 1));
+  const int64_t cap = 1 + stage_floats(head_dim) / ((int64_t)group * (head_dim + 4));
   if (rp > cap) rp = cap;
   if (rp > parts) rp = parts;
   return rp < 1 ? 1 : (int32_t)rp;

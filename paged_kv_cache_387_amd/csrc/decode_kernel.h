@@ -63,6 +63,16 @@ template <> struct Prefetch<PKV_F32> { static constexpr int NB = PKV_PREFETCH_F3
 template <> struct Prefetch<PKV_I8> { static constexpr int NB = PKV_PREFETCH_Q8; };
 template <> struct Prefetch<PKV_E4M3> { static constexpr int NB = PKV_PREFETCH_Q8; };
 
+// Four consecutive output elements (idx a multiple of 4).
+template <int OUT>
+__device__ __forceinline__ void store_out4(void *out, size_t idx, f4 v) {
+  if constexpr (OUT == PKV_F32)
+    *reinterpret_cast<f4 *>(reinterpret_cast<float *>(out) + idx) = v;
+  else
+    *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(out) + idx) =
+        h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+}
+
 // RUNS: the workgroup may walk several partitions (DecodeParams::run_parts >
 // 1); without it run_parts is taken as 1 and the walk carries no partition
 // ends.  SRC < 0: decode only.  SRC = PKV_F16 / PKV_F32: fused decode step, the new
@@ -85,11 +95,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   constexpr int NB = Prefetch<KV>::NB;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
 
-  __shared__ float lds_o[kDecodeWaves][kMaxGroup][LDS_ROW];
+  __shared__ __attribute__((aligned(16))) float lds_o[kDecodeWaves][kMaxGroup][LDS_ROW];
   __shared__ float lds_m[kDecodeWaves][kMaxGroup];
   __shared__ float lds_l[kDecodeWaves][kMaxGroup];
-  // finished partials of the run's earlier partitions: [partition][head][D + 1]
-  __shared__ float lds_stage[RUNS ? stage_floats(D) : 1];
+  // finished partials of the run's earlier partitions: [partition][head][D + 4]
+  // (the output row, then its log-sum-exp)
+  __shared__ __attribute__((aligned(16))) float lds_stage[RUNS ? stage_floats(D) : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   // for its staged partials; the host only sets up such runs.
   const int rp = RUNS ? p.run_parts : 1;      // partitions of the run
   if (RUNS && (rp < 1 || p.part_tiles % kDecodeWaves != 0 ||
-               (rp - 1) * G * (D + 1) > stage_floats(D)))
+               (rp - 1) * G * (D + 4) > stage_floats(D)))
     return;
 
   const int part0 = run * rp;                 // first partition of the run
@@ -598,31 +609,34 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
       lds_m[w][r] = m;
       lds_l[w][r] = lt;
     }
+    if (r < G) {   // columns r >= G repeat head 0 and are never read
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) {
-      const int i = a / E, e = a % E;
+      for (int a = 0; a < NACC; ++a) {
+        const int i = a / E, e = a % E;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) lds_o[w][r][E * (16 * i + 4 * g + v) + e] = acc[a][v];
+        for (int v = 0; v < 4; ++v) lds_o[w][r][E * (16 * i + 4 * g + v) + e] = acc[a][v];
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  auto combine = [&](int hh, int d, float &o, float &M, float &den) __attribute__((always_inline)) {
+  // Elements d0 .. d0+3 of head hh (one LDS row read per wave).
+  auto combine = [&](int hh, int d0, f4 &o, float &M, float &den) __attribute__((always_inline)) {
     M = lds_m[0][hh];
 #pragma unroll
     for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, lds_m[ww][hh]);
-    float num = 0.f;
+    f4 num = f4{0.f, 0.f, 0.f, 0.f};
     den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecodeWaves; ++ww) {
       const float c = exp2f(lds_m[ww][hh] - M);
-      num += c * lds_o[ww][hh][d];
+      num += c * *reinterpret_cast<const f4 *>(&lds_o[ww][hh][d0]);
       den += c * lds_l[ww][hh];
     }
     o = num / den;
     if constexpr (QUANT) o *= (1.0f / kPvBoost);
   };
   // A partition of the run other than its last ends: its partial goes to
-  // lds_stage (thread t keeps elements t, t + 64 * kDecodeWaves, ... and
+  // lds_stage (thread t keeps element quads t, t + 64 * kDecodeWaves, ... and
   // stores them itself after the walk), and the state restarts.  All waves
   // reach this at the same step; the second barrier frees lds_o for the next.
   int flush_at = nparts_run > 1 ? tpw - 1 : -1;   // step that ends partition `staged`
@@ -631,13 +645,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     if constexpr (!RUNS) return;
     if (__builtin_expect(k != flush_at, 1)) return;
     publish();
-    for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
-      const int hh = e / D, d = e % D;
-      float o, M, den;
-      combine(hh, d, o, M, den);
-      float *row = lds_stage + (staged * G + hh) * (D + 1);
-      row[d] = o;
-      if (d == 0) row[D] = M + log2f(den);
+    for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
+      const int hh = 4 * qd / D, d0 = 4 * qd % D;
+      f4 o;
+      float M, den;
+      combine(hh, d0, o, M, den);
+      float *row = lds_stage + (staged * G + hh) * (D + 4);
+      *reinterpret_cast<f4 *>(row + d0) = o;
+      if (d0 == 0) row[D] = M + log2f(den);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     m = -INFINITY;
@@ -702,29 +717,39 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   publish();
   const bool direct = nparts_s == 1 && npre == 0;
   const int part = part0 + nparts_run - 1;
-  for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
-    const int hh = e / D, d = e % D;
-    float o, M, den;
-    combine(hh, d, o, M, den);
+  // out needs only element alignment; vector stores when it allows them
+  const bool out_vec =
+      (reinterpret_cast<uintptr_t>(p.out) & (OUT == PKV_F32 ? 15u : 7u)) == 0;
+  for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
+    const int hh = 4 * qd / D, d0 = 4 * qd % D;
+    f4 o;
+    float M, den;
+    combine(hh, d0, o, M, den);
     const int h = kvh * G + hh;
     if (direct) {
-      store_out<OUT>(p.out, ((size_t)s * H + h) * D + d, o);
+      const size_t idx = ((size_t)s * H + h) * D + d0;
+      if (out_vec) {
+        store_out4<OUT>(p.out, idx, o);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_out<OUT>(p.out, idx + i, o[i]);
+      }
     } else {
       const size_t row = ((size_t)s * H + h) * p.ws_stride + part;
-      p.ws_o[row * D + d] = o;
-      if (d == 0) p.ws_lse[row] = M + log2f(den);
+      *reinterpret_cast<f4 *>(p.ws_o + row * D + d0) = o;
+      if (d0 == 0) p.ws_lse[row] = M + log2f(den);
     }
   }
   // the staged partials of the run's earlier partitions (each thread stores
   // the elements it staged)
   if constexpr (RUNS)
   for (int j = 0; j < nparts_run - 1; ++j) {
-    for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves) {
-      const int hh = e / D, d = e % D;
-      const float *src = lds_stage + (j * G + hh) * (D + 1);
+    for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
+      const int hh = 4 * qd / D, d0 = 4 * qd % D;
+      const float *src = lds_stage + (j * G + hh) * (D + 4);
       const size_t row = ((size_t)s * H + kvh * G + hh) * p.ws_stride + part0 + j;
-      p.ws_o[row * D + d] = src[d];
-      if (d == 0) p.ws_lse[row] = src[D];
+      *reinterpret_cast<f4 *>(p.ws_o + row * D + d0) = *reinterpret_cast<const f4 *>(src + d0);
+      if (d0 == 0) p.ws_lse[row] = src[D];
     }
   }
 }

@@ -149,10 +149,10 @@ inline int64_t decode_grid(int num_units, int num_runs) {
 }
 
 // LDS floats a decode workgroup sets aside for the finished partials of a
-// run (all but its last partition, which is stored directly): (D + 1) floats
-// (the normalized output row and its log-sum-exp) per query head and staged
-// partition.  Room for 7 partitions of 8 heads.
-__host__ __device__ constexpr int stage_floats(int head_dim) { return 7 * 8 * (head_dim + 1); }
+// run (all but its last partition, which is stored directly): a row of
+// D + 4 floats (the normalized output, its log-sum-exp, padding to 16 bytes)
+// per query head and staged partition.  Room for 7 partitions of 8 heads.
+__host__ __device__ constexpr int stage_floats(int head_dim) { return 7 * 8 * (head_dim + 4); }
 
 struct WriteParams {
   const void *key;
