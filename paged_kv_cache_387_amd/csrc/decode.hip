@@ -82,11 +82,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   if (!merge) return;
   const f4 r = acc * (1.0f / z);
   const size_t oi = (size_t)row * D + 4 * dv;
-  if constexpr (OUT == PKV_F32) {
-    *reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.out) + oi) = r;
+  // out needs only element alignment; vector stores when it allows them
+  if ((reinterpret_cast<uintptr_t>(p.out) & (OUT == PKV_F32 ? 15u : 7u)) == 0) {
+    store_out4<OUT>(p.out, oi, r);
   } else {
-    *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(p.out) + oi) =
-        h4{(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_out<OUT>(p.out, oi + i, r[i]);
   }
 }
 

@@ -205,3 +205,30 @@ def test_decode_out_of_range_entries_stay_in_bounds(pkv):
                                      out_dtype=torch.float16)
     torch.cuda.synchronize()
     check_close(out[0:1], ref[0:1], "f16", "untouched sequence")
+
+
+@pytest.mark.parametrize("odt", ["f16", "f32"])
+def test_decode_output_with_element_alignment_only(pkv, odt):
+    """The ABI asks only for element alignment of `out`: an output view that
+    starts one element into its buffer (not 8- or 16-byte aligned) gets the
+    same values as an aligned one, single-pass and split."""
+    from paged_kv_cache_387_amd import driver
+    w = _ragged("f16", lens=(1, 16, 17, 100, 257, 700))()
+    w.memo = {}
+    ro = oracle_replay(w)
+    rg = driver.replay(w)
+    ref = oracle_output(ro, w)
+    dt = torch.float16 if odt == "f16" else torch.float32
+    S, H, D = w.num_seqs, w.num_heads, w.head_dim
+    for ps in (0, 64):
+        buf = torch.full((S * H * D + 8,), 7.0, dtype=dt, device="cuda")
+        out = buf[1:1 + S * H * D].view(S, H, D)
+        assert out.data_ptr() % 8 != 0
+        pkv.paged_attention_decode(rg.query, rg.cache, rg.block_tables, rg.seq_lens,
+                                   float(np.float32(w.scale)), out=out, partition_size=ps)
+        torch.cuda.synchronize()
+        check_close(out, ref, "f16", f"element-aligned {odt} out partition={ps}")
+        assert float(buf[0]) == 7.0 and bool((buf[1 + S * H * D:] == 7.0).all())
+        aligned = driver.decode(rg, w, partition_size=ps, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(out, aligned)
