@@ -49,6 +49,9 @@ def _workloads():
         # name: (factory(replica) -> Workload, replicas, pool blocks or None)
         "c2": (lambda r: W.c2_qwen3_32b_layer(seed_offset=r), 8, 12480),
         "c3": (lambda r: W.c3_long_context(), 1, None),
+        # the same long uniform sequences over an int8 / E4M3 cache
+        "c3_i8": (lambda r: _quantized(W.c3_long_context(), "i8"), 1, None),
+        "c3_e4m3": (lambda r: _quantized(W.c3_long_context(), "e4m3"), 1, None),
         "c4_i8": (lambda r: W.c4_quantized("i8"), 2, None),
         "c4_e4m3": (lambda r: W.c4_quantized("e4m3"), 2, None),
         "c5": (lambda r: W.c5_shared_prefix(), 2, 8192),
@@ -59,6 +62,14 @@ def _workloads():
         # block swap to pinned host memory and back, bench_swap
         "swap": (lambda r: W.c2_qwen3_32b_layer(), 1, None),
     }
+
+
+def _quantized(w, cache_dtype: str):
+    """Workload `w` with its fp16 K/V stored in an int8 or E4M3 cache (the
+    cache write quantizes them)."""
+    w.cache_dtype = cache_dtype
+    w.name += "_" + cache_dtype
+    return w
 
 
 def kv_bytes(lens, w) -> int:

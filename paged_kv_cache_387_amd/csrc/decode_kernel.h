@@ -56,7 +56,7 @@ namespace {
 #define PKV_PREFETCH_F16 3
 #endif
 #ifndef PKV_PREFETCH_Q8
-#define PKV_PREFETCH_Q8 6
+#define PKV_PREFETCH_Q8 4
 #endif
 template <int KV> struct Prefetch { static constexpr int NB = PKV_PREFETCH_F16; };
 template <> struct Prefetch<PKV_F32> { static constexpr int NB = PKV_PREFETCH_F32; };
