@@ -331,7 +331,9 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  * (the attention formula of [fairy, s01]; paging does not change the math
  * [jsqmd, section 9]).  Query head h uses kv head h / (num_heads/num_kv_heads)
  * (grouped-query attention, num_kv_heads <= num_heads [fairy, s11]).
- *   out:     device [num_seqs][num_heads][head_dim] of out_dtype (F32 or F16).
+ *   out:     device [num_seqs][num_heads][head_dim] of out_dtype (F32 or F16),
+ *            aligned to its element size (written with 4-element vector
+ *            stores when 16-byte (F32) or 8-byte (F16) aligned).
  *   query:   device [num_seqs][num_heads][head_dim], q_dtype = F32 when
  *            cache_dtype is F32, else F16; 16-byte aligned.
  *   k_cache, v_cache, k_scale, v_scale, cache_dtype, num_blocks: the pools.
@@ -341,11 +343,14 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *   seq_lens: device int32 [num_seqs], tokens already in the cache including
  *            the one just written; 0 gives a zero output row.
  *   head_dim 64 or 128; block_size 8, 16 or 32; num_heads/num_kv_heads <= 16.
- *   partition_size: tokens per work unit along the sequence (a multiple of
+ *   partition_size: tokens per partition along the sequence (a multiple of
  *            16 and of block_size; 0 = library choice).  Longer sequences are split;
- *            the partial results (max, sum, weighted V) are merged by a
- *            log-sum-exp reduction ("partial accumulate, then merge",
- *            paged_attention_v2 of [jsqmd, section 4.1]).
+ *            the partial results (max, sum, weighted V) of the partitions are
+ *            merged by a log-sum-exp reduction ("partial accumulate, then
+ *            merge", paged_attention_v2 of [jsqmd, section 4.1]).  When the
+ *            size is a multiple of 64 tokens, one workgroup may walk several
+ *            consecutive partitions of a sequence (up to the library's own
+ *            partition size); that changes the schedule, not the partials.
  *   workspace: device, >= paged_attention_workspace_bytes(...) bytes,
  *            256-byte aligned (may be NULL when that size is 0); its contents
  *            on entry do not matter.  Calls that share a workspace must not
