@@ -86,7 +86,8 @@ def _run(name, step, part, min_prefix=0):
     return sh
 
 
-@pytest.mark.parametrize("part", [0, "min"])
+# 64 tokens = 4 tiles: suffix decodes walk runs of partitions
+@pytest.mark.parametrize("part", [0, "min", 64])
 @pytest.mark.parametrize("step", [False, True])
 @pytest.mark.parametrize("name", list(CASES))
 def test_shared_matches_oracle(name, step, part):
