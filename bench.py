@@ -528,8 +528,8 @@ def bench_len_sweep(args, torch, pkv) -> int:
     rows.append({"len": "U[512,768]", "us": round(us, 3), "kv_gbs": round(kv / us / 1e3, 1)})
     slope, icept = np.polyfit(np.asarray(fit_x, np.float64), np.asarray(fit_y, np.float64), 1)
     print(json.dumps({
-        "metric": "paged_attention_decode cost per call vs sequence length (C2 shape)",
-        "config": {"workload": "c2_shape_len_sweep", "num_seqs": S, "num_heads": H,
+        "metric": "paged_attention_decode cost per call vs sequence length (Qwen3-32B layer shape)",
+        "config": {"workload": "qwen3_32b_layer_len_sweep", "num_seqs": S, "num_heads": H,
                    "num_kv_heads": HKV, "head_dim": D, "kv_dtype": "f16", "pool_blocks": NBLK,
                    "rotating_batches": R, "calls_per_graph": n},
         "points": rows,
@@ -562,7 +562,7 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
     ap.add_argument("--len-sweep", action="store_true",
-                    help="decode cost per call against sequence length at the C2 shape")
+                    help="decode cost per call against sequence length at the Qwen3-32B layer shape")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run the plain copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=4,

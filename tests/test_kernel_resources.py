@@ -3,7 +3,8 @@
 The decode kernel keeps its K/V prefetch ring and its accumulators in
 registers; if the compiler moves them to per-lane scratch memory the kernel
 still computes the right answer but its time multiplies (a run-enabled build
-once did: 224-240 bytes of scratch per lane, C3 at 500 us instead of 180).
+once did: 224-240 bytes of scratch per lane, and the 8 x 32K-token decode
+took 500 us instead of 180).
 This test reads each kernel's private segment size from the gfx950 code
 objects of the in-tree build (_build/*.o, written by
 paged_kv_cache_387_amd.build) with the ROCm LLVM tools and requires:
