@@ -14,6 +14,9 @@ import numpy as np
 from . import Pools, copy_blocks, decode, prefill, write
 from .allocator_model import BlockManagerModel
 
+# positions of sequence ids in each op
+_SEQ_FIELDS = {"allocate": (1,), "fork": (1, 2), "free": (1,), "append": (1,), "write": (1,)}
+
 
 @dataclass
 class OracleReplay:
@@ -27,17 +30,29 @@ class OracleReplay:
     log: list = field(default_factory=list)
 
 
-def replay(w, sentinel=Pools.SENTINEL) -> OracleReplay:
-    mgr = BlockManagerModel(w.num_blocks, w.block_size, w.free_order)
-    pools = Pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, w.block_size,
-                  sentinel=sentinel)
+def replay(w, sentinel=Pools.SENTINEL, model: BlockManagerModel | None = None,
+           pools: Pools | None = None, seq_offset: int = 0,
+           stop_at_step: bool = False) -> OracleReplay:
+    """Run the script of workload `w`.  `model` / `pools` may be shared between
+    several replays (sequence ids are then shifted by `seq_offset`); with
+    `stop_at_step` the ops after the ("step",) marker are left out."""
+    mgr = model if model is not None else BlockManagerModel(w.num_blocks, w.block_size,
+                                                            w.free_order)
+    if pools is None:
+        pools = Pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, w.block_size,
+                      sentinel=sentinel)
     log, step_slots, step_pairs = [], [], []
     in_step = False
-    for op in w.ops:
-        kind = op[0]
+    for op0 in w.ops:
+        kind = op0[0]
         if kind == "step":
+            if stop_at_step:
+                break
             in_step = True
             continue
+        # sequence ids shifted; the content owner is looked up unshifted
+        op = (kind,) + tuple(x + seq_offset if k in _SEQ_FIELDS.get(kind, ()) else x
+                             for k, x in enumerate(op0[1:], start=1))
         if kind == "allocate":
             st, pair = mgr.allocate(op[1], op[2])
             log.append((op, st, pair))
@@ -66,14 +81,14 @@ def replay(w, sentinel=Pools.SENTINEL) -> OracleReplay:
             seq, start, count = op[1], op[2], op[3]
             st, slots = mgr.slots(seq, start, count)
             assert st == "ok", (op, st)
-            owner = w.owner_of(seq, start)
-            assert owner == w.owner_of(seq, start + count - 1)
+            owner = w.owner_of(seq - seq_offset, start)
+            assert owner == w.owner_of(seq - seq_offset, start + count - 1)
             k = w.kv_rows("k", owner, start, count)
             v = w.kv_rows("v", owner, start, count)
             write(pools, k, v, np.asarray(slots, np.int64))
         else:
             raise ValueError(op)
-    st, rows, lens = mgr.export(w.decode_seqs, w.max_blocks_per_seq)
+    st, rows, lens = mgr.export([s + seq_offset for s in w.decode_seqs], w.max_blocks_per_seq)
     assert st == "ok"
     return OracleReplay(
         pools=pools, model=mgr, block_tables=np.asarray(rows, np.int32).reshape(

@@ -39,8 +39,9 @@
 // and 16x16x16 f16 (P.V); int8 / E4M3 codes are widened exactly to fp16 (int8
 // by a byte permute under an fp16 exponent, E4M3 by the gfx950 fp8
 // conversion) and use the fp16 MFMAs, the K scale multiplies the scores and
-// the V scale is folded into P (P' = p * s_v * 64 in fp16; the factor 64 keeps
-// P' out of fp16's subnormal range and is divided out at the end).
+// the V scale is folded into P (P' = p * s_v * b in fp16, b a power-of-two
+// boost that keeps P' out of fp16's subnormal range and below its largest
+// value; see lower_boost).
 #pragma once
 
 #include "attn_common.h"
@@ -70,7 +71,7 @@ __device__ __forceinline__ void store_out4(void *out, size_t idx, f4 v) {
     *reinterpret_cast<f4 *>(reinterpret_cast<float *>(out) + idx) = v;
   else
     *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(out) + idx) =
-        h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        h4{to_f16_out(v[0]), to_f16_out(v[1]), to_f16_out(v[2]), to_f16_out(v[3])};
 }
 
 // RUNS: the workgroup may walk several partitions (DecodeParams::run_parts >
@@ -177,21 +178,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
       qf16[i][QUANT ? 1 : 0] =
           __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp + 8)));
     }
-  }
-
-  // int8: 1152 * (sum of head r's q), taken out of the biased q.K scores
-  float qbias = 0.0f;
-  if constexpr (KV == PKV_I8) {
-    float qs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qs += (float)qf16[i][h][e];
-    qs += xor16(qs);
-    qs += xor32(qs);
-    qbias = kI8Bias * qs;
   }
 
   int cow_req = -1;   // fused step: the block to copy into the tail block, if any
@@ -381,6 +367,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
 #pragma unroll
   for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
   f4 accp = f4{0.f, 0.f, 0.f, 0.f};   // int8: sum_t P'_t of column r (every row)
+  float vboost = kVBoost0;             // quantized V: the wave's boost b and the
+  float vlim = kFoldMax / kVBoost0;    // largest V scale it admits (weights <= 1)
 
   const size_t kv_head_off = (size_t)kvh * SLICE;
   const size_t block_stride = (size_t)p.num_kv_heads * SLICE;
@@ -487,7 +475,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
                                                     sc, 0, 0, 0);
       } else {
         h8 lo, hi;
-        codes16_to_h8<KV>(t.k[i], lo, hi);
+        k_codes16<KV>(t.k[i], lo, hi);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, qf16[i][0], sc, 0, 0, 0);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qf16[i][QUANT ? 1 : 0], sc, 0, 0, 0);
       }
@@ -497,10 +485,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      if constexpr (KV == PKV_I8)
-        x[v] = (sc[v] - qbias) * p.qk_scale;
-      else
-        x[v] = sc[v] * p.qk_scale;
+      x[v] = sc[v] * p.qk_scale;
       if constexpr (QUANT) x[v] *= (float)as_h2(t.ks[v >> 1])[v & 1];
     }
     u4 vw[NL];
@@ -575,9 +560,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
             __builtin_bit_cast(h4, u2{hi01, hi23}), pb, acc[2 * i + 1], 0, 0, 0);
       }
     } else {
+      float sv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv[v] = (float)as_h2(vs[v >> 1])[v & 1];
+      // A V scale above what the wave's boost admits (never one of an fp16
+      // value): lower the boost first.  Lanes of one row group g hold the
+      // same tokens' scales.
+      const float smax = fmaxf(fmaxf(fabsf(sv[0]), fabsf(sv[1])), fmaxf(fabsf(sv[2]), fabsf(sv[3])));
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(smax > vlim) != 0, 0)) {
+        float sw = fmaxf(smax, xor16(smax));
+        sw = fmaxf(sw, xor32(sw));
+        const float nb = lower_boost(vboost, sw, 1.0f);
+        const float f = nb / vboost;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[a] *= f;
+        if constexpr (KV == PKV_I8) accp *= f;
+        vboost = nb;
+        vlim = kFoldMax / nb;
+      }
       float ps[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ps[v] = pr[v] * (float)as_h2(vs[v >> 1])[v & 1] * kPvBoost;
+      for (int v = 0; v < 4; ++v) ps[v] = pr[v] * sv[v] * vboost;
       const h4 pb = h4{(_Float16)ps[0], (_Float16)ps[1], (_Float16)ps[2], (_Float16)ps[3]};
       if constexpr (KV == PKV_I8) {
         const h4 ones = h4{(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
@@ -602,6 +605,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     if constexpr (KV == PKV_I8) {
 #pragma unroll
       for (int a = 0; a < NACC; ++a) acc[a] -= kI8Bias * accp;
+    }
+    if constexpr (QUANT) {   // undo the wave's V-scale boost (a power of two: exact)
+      const float ib = 1.0f / vboost;
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) acc[a] *= ib;
     }
     float lt = l + xor16(l);
     lt += xor32(lt);
@@ -633,7 +641,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
       den += c * lds_l[ww][hh];
     }
     o = num / den;
-    if constexpr (QUANT) o *= (1.0f / kPvBoost);
   };
   // A partition of the run other than its last ends: its partial goes to
   // lds_stage (thread t keeps element quads t, t + 64 * kDecodeWaves, ... and

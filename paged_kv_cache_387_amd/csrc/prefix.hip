@@ -15,16 +15,14 @@
 // concatenation equals the merge of softmaxes over the pieces.
 //
 // Work decomposition.  A group of n sequences has n*G query columns per kv
-// head (G query heads per kv head).  One workgroup (4 waves) takes CW = 16*C
-// columns and one partition of the prefix; wave w takes the partition's tiles
-// w, w+4, ...  Per 16-token tile a wave computes, for each of its C chunks of
-// 16 columns, the 16x16 score tile S^T = K q (MFMA, K as loaded is the A
-// operand), the online softmax per column, and O^T += V^T P^T (MFMA); the K and
-// V operands (and their widening from int8 / E4M3) are prepared once per tile
-// and reused by the C chunks, so the MFMA work per byte loaded is C times that
-// of decode.  The waves' states are combined through LDS at the end.  Tiles
-// are read with ordinary loads: the workgroups of the other column blocks read
-// the same tiles at about the same time from L2.
+// head (G query heads per kv head).  One workgroup (4 waves) takes a block of
+// the group's columns and one partition of the prefix; the waves split the
+// partition's tokens, every wave applies its tokens to all the block's
+// columns, and the waves' states are combined through LDS at the end.  fp16,
+// int8 and E4M3 caches run on 32x32x16 MFMAs (prefix32_kernel below); fp32
+// caches, which have no such MFMA, on 16x16x4 f32 MFMAs (prefix_kernel).  The
+// K and V operands of a tile are prepared once and reused by every column, so
+// the MFMA work per byte loaded is the column count times that of decode.
 #include "attn_common.h"
 
 namespace pkv {
@@ -71,19 +69,19 @@ __device__ __forceinline__ void lds_read_row(uint32_t addr, u4 *out) {
   }
 }
 
-template <int KV, int D, int BS, int C>
+// ---------------------------------------------------------------------------
+// fp32 caches: 16x16 MFMA blocks (fp32 operands have no 32x32x16 form).
+template <int D, int BS, int C>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) {
-  constexpr int EB = Kv<KV>::EB;
-  constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
+  constexpr int EB = 4;
   constexpr int SLICE = BS * D * EB;
   constexpr int TPB = BS >= kTile ? BS / kTile : 1;
   constexpr bool SPLIT = BS < kTile;
   constexpr int TB = SPLIT ? BS : kTile;
   constexpr int NL = D * EB / 64;
   constexpr int NACC = D / 16;
-  constexpr int E = 4 / EB;
   constexpr int NR = 2;                   // tiles in flight per wave (LDS ring slots)
-  constexpr int LPT = 2 * NL + (QUANT ? 2 : 0);   // vector-memory loads per tile
+  constexpr int LPT = 2 * NL;             // vector-memory loads per tile
   constexpr int CW = 16 * C;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert((NR - 1) * LPT < 64, "wait count");
@@ -166,53 +164,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
     col_head[ch] = kvh * G + cc % G;
   }
   float qf32[C][NL][4];
-  h8 qf16[C][NL][QUANT ? 2 : 1];
 #pragma unroll
   for (int ch = 0; ch < C; ++ch) {
     const size_t qrow = ((size_t)col_seq[ch] * H + col_head[ch]) * D;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      if constexpr (KV == PKV_F32) {
-        const float *qp = reinterpret_cast<const float *>(p.q) + qrow + (4 * i + g) * 4;
-        const u4 raw = load16(reinterpret_cast<const uint8_t *>(qp));
+      const float *qp = reinterpret_cast<const float *>(p.q) + qrow + (4 * i + g) * 4;
+      const u4 raw = load16(reinterpret_cast<const uint8_t *>(qp));
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) qf32[ch][i][jj] = as_f32(raw[jj]);
-      } else if constexpr (KV == PKV_F16) {
-        const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 8;
-        qf16[ch][i][0] = __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp)));
-      } else {
-        const _Float16 *qp = reinterpret_cast<const _Float16 *>(p.q) + qrow + (4 * i + g) * 16;
-        qf16[ch][i][0] = __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp)));
-        qf16[ch][i][QUANT ? 1 : 0] =
-            __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qp + 8)));
-      }
-    }
-  }
-  // int8: 1152 * (sum of the column's q), taken out of the biased scores
-  float qbias[C];
-#pragma unroll
-  for (int ch = 0; ch < C; ++ch) {
-    qbias[ch] = 0.0f;
-    if constexpr (KV == PKV_I8) {
-      float qs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qs += (float)qf16[ch][i][h][e];
-      qbias[ch] = kI8Bias * row_sum4(qs);
+      for (int jj = 0; jj < 4; ++jj) qf32[ch][i][jj] = as_f32(raw[jj]);
     }
   }
 
   float m[C], l[C];
   f4 acc[C][NACC];
-  f4 accp[C];
 #pragma unroll
   for (int ch = 0; ch < C; ++ch) {
     m[ch] = -INFINITY;
     l[ch] = 0.0f;
-    accp[ch] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int a = 0; a < NACC; ++a) acc[ch][a] = f4{0.f, 0.f, 0.f, 0.f};
   }
@@ -220,31 +189,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
   const size_t kv_head_off = (size_t)kvh * SLICE;
   const size_t block_stride = (size_t)p.num_kv_heads * SLICE;
   // Headroom (base-2 units) a column's maximum may rise before the running
-  // state is rescaled.  Quantized V folds its scale (and the factor 64) into
-  // the fp16 weights, which must stay below fp16's maximum: 4 * 64 * s_v.
-  constexpr float kTau = QUANT ? 2.0f : 8.0f;
+  // state is rescaled: the fp32 weights exp2(x - m) then stay below 2^8.
+  constexpr float kTau = 8.0f;
   bool fresh = true;     // no tile consumed yet (wave-uniform)
-
-  struct Tile {
-    u4 k[NL];
-    u4 v[NL];
-    u2 ks, vs;
-    bool ok;
-  };
-  struct Slot {   // what of a tile in flight lives in registers
-    u2 ks, vs;
-    bool ok;
-  };
 
   // Loads of prefix tile `tile` (table entries: lane j of tv / tvb) into ring
   // slot `slot`, with the addressing of the decode kernel (all prefix tiles
-  // are full): K and V straight into LDS, the scales into registers.
-  auto issue = [&](int tv, int tvb, int j, int tile, int slot, Slot &t) {
+  // are full): K and V straight into LDS.  Returns whether both table entries
+  // are in the pool.
+  auto issue = [&](int tv, int tvb, int j, int tile, int slot) {
     int pa = __builtin_amdgcn_readlane(tv, j);
     int pb = SPLIT ? __builtin_amdgcn_readlane(tvb, j) : pa;
-    t.ok = (unsigned)pa < (unsigned)p.num_blocks && (unsigned)pb < (unsigned)p.num_blocks;
-    pa = t.ok ? pa : 0;
-    pb = t.ok ? pb : 0;
+    const bool ok = (unsigned)pa < (unsigned)p.num_blocks && (unsigned)pb < (unsigned)p.num_blocks;
+    pa = ok ? pa : 0;
+    pb = ok ? pb : 0;
     const int tq = SPLIT ? 0 : tile % TPB;
     const size_t tile_off = (size_t)tq * (TB * D * EB);
     const int pk = SPLIT && r >= 8 ? pb : pa;
@@ -257,23 +215,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
     for (int i = 0; i < NL; ++i)
       load16_to_lds(kb + (size_t)((4 * i + g) * TB + tk) * 16, &lds_ring[w][slot][i][0]);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      if constexpr (EB == 1)
-        load16_to_lds(vb + (size_t)((16 * i + r) * (TB / 4) + tv0 / 4) * 16,
-                      &lds_ring[w][slot][NL + i][0]);
-      else
-        load16_to_lds(vb + (size_t)((16 * i + r) * TB + tv0) * 4, &lds_ring[w][slot][NL + i][0]);
-    }
-    if constexpr (QUANT) {
-      const size_t so = ((size_t)pv * p.num_kv_heads + kvh) * BS + tq * kTile + tv0;
-      t.ks = *reinterpret_cast<const u2 *>(p.k_scale + so);
-      t.vs = *reinterpret_cast<const u2 *>(p.v_scale + so);
-    }
+    for (int i = 0; i < NL; ++i)
+      load16_to_lds(vb + (size_t)((16 * i + r) * TB + tv0) * 4, &lds_ring[w][slot][NL + i][0]);
+    return ok;
   };
 
-  auto consume = [&](int slot, const Slot &sl) {
-    if (!sl.ok) return;  // table entry outside the pool: tile skipped
-    Tile t;
+  auto consume = [&](int slot, bool ok) {
+    if (!ok) return;  // table entry outside the pool: tile skipped
     const uint32_t base = (uint32_t)(size_t)(
         (__attribute__((address_space(3))) const u4 *)&lds_ring[w][slot][0][lane]);
     u4 kv[2 * NL];
@@ -281,75 +229,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
     lds_wait();
 #pragma unroll
     for (int i = 0; i < 2 * NL; ++i) after_wait(kv[i]);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      t.k[i] = kv[i];
-      t.v[i] = kv[NL + i];
-    }
-    t.ks = sl.ks;
-    t.vs = sl.vs;
-    // Operands shared by the C chunks.
-    h8 kq[NL][2];        // widened K codes (quantized)
-    h4 vh[NL][4];        // V^T operands: [i][0..1] fp16, [i][e] widened codes
-    float ksf[4], vsf[4];
-    if constexpr (QUANT) {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) codes16_to_h8<KV>(t.k[i], kq[i][0], kq[i][1]);
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vh[i][e] = codes4_to_h4<KV>(t.v[i][e]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        ksf[v] = (float)as_h2(t.ks[v >> 1])[v & 1];
-        vsf[v] = (float)as_h2(t.vs[v >> 1])[v & 1] * kPvBoost;
-      }
-    } else if constexpr (KV == PKV_F16) {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const uint32_t lo01 = __builtin_amdgcn_perm(t.v[i][1], t.v[i][0], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(t.v[i][3], t.v[i][2], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(t.v[i][1], t.v[i][0], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(t.v[i][3], t.v[i][2], 0x07060302u);
-        vh[i][0] = __builtin_bit_cast(h4, u2{lo01, lo23});
-        vh[i][1] = __builtin_bit_cast(h4, u2{hi01, hi23});
-      }
-    }
     // q.K of every chunk: C independent accumulator chains
     f4 sc[C];
 #pragma unroll
     for (int ch = 0; ch < C; ++ch) sc[ch] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    for (int i = 0; i < NL; ++i)
 #pragma unroll
-      for (int ch = 0; ch < C; ++ch) {
-        if constexpr (KV == PKV_F32) {
+      for (int ch = 0; ch < C; ++ch)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            sc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(t.k[i][jj]), qf32[ch][i][jj],
-                                                          sc[ch], 0, 0, 0);
-        } else if constexpr (KV == PKV_F16) {
-          sc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, t.k[i]),
-                                                          qf16[ch][i][0], sc[ch], 0, 0, 0);
-        } else {
-          sc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kq[i][0], qf16[ch][i][0], sc[ch], 0,
-                                                          0, 0);
-          sc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kq[i][1], qf16[ch][i][QUANT ? 1 : 0],
-                                                          sc[ch], 0, 0, 0);
-        }
-      }
-    }
-    // base-2 scores (the K scale is per token: the same for every chunk)
-    float coef[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) coef[v] = QUANT ? p.qk_scale * ksf[v] : p.qk_scale;
+        for (int jj = 0; jj < 4; ++jj)
+          sc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kv[i][jj]), qf32[ch][i][jj],
+                                                        sc[ch], 0, 0, 0);
     float x[C][4], mn[C];
     bool over = false;
 #pragma unroll
     for (int ch = 0; ch < C; ++ch) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        x[ch][v] = (KV == PKV_I8 ? sc[ch][v] - qbias[ch] : sc[ch][v]) * coef[v];
+      for (int v = 0; v < 4; ++v) x[ch][v] = sc[ch][v] * p.qk_scale;
       const float bm = row_max4(fmaxf(fmaxf(x[ch][0], x[ch][1]), fmaxf(x[ch][2], x[ch][3])));
       mn[ch] = fmaxf(m[ch], bm);
       over = over || mn[ch] > m[ch] + kTau;
@@ -368,7 +265,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
         l[ch] *= alpha;
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[ch][a] *= alpha;
-        if constexpr (KV == PKV_I8) accp[ch] *= alpha;
         m[ch] = mn[ch];
       }
     }
@@ -378,38 +274,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
 #pragma unroll
       for (int v = 0; v < 4; ++v) pr[v] = fast_exp2(x[ch][v] - m[ch]);
       l[ch] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      if constexpr (KV == PKV_F32) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
+      for (int i = 0; i < NL; ++i)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            acc[ch][i] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(t.v[i][jj]), pr[jj],
-                                                              acc[ch][i], 0, 0, 0);
-      } else if constexpr (KV == PKV_F16) {
-        const h4 pb = h4{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          acc[ch][2 * i] =
-              __builtin_amdgcn_mfma_f32_16x16x16f16(vh[i][0], pb, acc[ch][2 * i], 0, 0, 0);
-          acc[ch][2 * i + 1] =
-              __builtin_amdgcn_mfma_f32_16x16x16f16(vh[i][1], pb, acc[ch][2 * i + 1], 0, 0, 0);
-        }
-      } else {
-        float ps[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) ps[v] = pr[v] * vsf[v];
-        const h4 pb = h4{(_Float16)ps[0], (_Float16)ps[1], (_Float16)ps[2], (_Float16)ps[3]};
-        if constexpr (KV == PKV_I8) {
-          const h4 ones = h4{(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-          accp[ch] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accp[ch], 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[ch][4 * i + e] =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(vh[i][e], pb, acc[ch][4 * i + e], 0, 0, 0);
-      }
+        for (int jj = 0; jj < 4; ++jj)
+          acc[ch][i] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(kv[NL + i][jj]), pr[jj],
+                                                            acc[ch][i], 0, 0, 0);
     }
   };
 
@@ -421,11 +291,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
     const int nc = min(64, nt_w - cc);
     const int tv = tv_next, tvb = tvb_next;
     const int t0 = first + w + cc * kWaves;
-    Slot ring[NR];
+    bool ring[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int jj = j < nc ? j : nc - 1;
-      issue(tv, tvb, jj, t0 + jj * kWaves, j, ring[j]);
+      ring[j] = issue(tv, tvb, jj, t0 + jj * kWaves, j);
     }
     int k0 = 0;
     for (; k0 + 2 * NR <= nc; k0 += NR) {
@@ -434,7 +304,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
         wait_vmcnt<(NR - 1) * LPT>();
         consume(j, ring[j]);
         asm volatile("" ::: "memory");   // the slot's reads before its refill
-        issue(tv, tvb, k0 + j + NR, t0 + (k0 + j + NR) * kWaves, j, ring[j]);
+        ring[j] = issue(tv, tvb, k0 + j + NR, t0 + (k0 + j + NR) * kWaves, j);
       }
     }
 #pragma unroll
@@ -444,7 +314,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
         consume(j, ring[j]);
       }
       asm volatile("" ::: "memory");
-      if (k0 + j + NR < nc) issue(tv, tvb, k0 + j + NR, t0 + (k0 + j + NR) * kWaves, j, ring[j]);
+      if (k0 + j + NR < nc) ring[j] = issue(tv, tvb, k0 + j + NR, t0 + (k0 + j + NR) * kWaves, j);
     }
 #pragma unroll
     for (int j = 0; j < NR; ++j)
@@ -460,10 +330,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
   // accumulators one wave after the other; the last wave writes the partials.
 #pragma unroll
   for (int ch = 0; ch < C; ++ch) {
-    if constexpr (KV == PKV_I8) {
-#pragma unroll
-      for (int a = 0; a < NACC; ++a) acc[ch][a] -= kI8Bias * accp[ch];
-    }
     l[ch] = row_sum4(l[ch]);
     if (g == 0) {
       lds_m[w][16 * ch + r] = m[ch];
@@ -506,25 +372,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
     if (!col_ok[ch]) continue;
     const size_t row =
         ((size_t)col_seq[ch] * H + col_head[ch]) * p.ws_stride + p.ws_pre + part;
-    float inv = 1.0f / den[ch];
-    if constexpr (QUANT) inv *= (1.0f / kPvBoost);
+    const float inv = 1.0f / den[ch];
     float *dst = p.ws_o + row * D;
-    // acc[ch][E*i + e][v] is output element E*(16i + 4g + v) + e: for each i
-    // the lane holds 4E consecutive elements.
+    // acc[ch][i][v] is output element 16i + 4g + v
 #pragma unroll
-    for (int i = 0; i < NACC / E; ++i) {
-      float vals[4 * E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const f4 a = acc[ch][E * i + e] + lds_acc[ch][E * i + e][lane];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) vals[E * v + e] = a[v] * inv;
-      }
-#pragma unroll
-      for (int k = 0; k < E; ++k)
-        *reinterpret_cast<f4 *>(dst + E * (16 * i + 4 * g) + 4 * k) =
-            f4{vals[4 * k], vals[4 * k + 1], vals[4 * k + 2], vals[4 * k + 3]};
-    }
+    for (int i = 0; i < NACC; ++i)
+      *reinterpret_cast<f4 *>(dst + 16 * i + 4 * g) = (acc[ch][i] + lds_acc[ch][i][lane]) * inv;
     if (g == 0) p.ws_lse[row] = Mx[ch] + log2f(den[ch]);
   }
 }
@@ -701,22 +554,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
       qf[nb][kk] = __builtin_bit_cast(h8, load16(reinterpret_cast<const uint8_t *>(qr + d0)));
     }
   }
-  float qbias[NB2];
-#pragma unroll
-  for (int nb = 0; nb < NB2; ++nb) {
-    qbias[nb] = 0.0f;
-    if constexpr (KV == PKV_I8) {
-      float qs = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qs += (float)qf[nb][kk][e];
-      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(qs), __float_as_uint(qs),
-                                                      false, false);
-      qbias[nb] = kI8Bias * (__uint_as_float(a[0]) + __uint_as_float(a[1]));
-    }
-  }
-
   float m[NB2], l[NB2];
   f16v acc[NB2][NT];
   float psum[NB2];   // int8: sum of the fp16 weights P' of this lane's rows
@@ -728,8 +565,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[nb][t] = f16v{};
   }
+  // Headroom (base-2 units) a column's maximum may rise before the running
+  // state is rescaled: the weights exp2(x - m) stay below kWMax = 2^kTau
+  // (with the rounding of fast_exp2).  Quantized V folds its scale times the
+  // wave's boost into the fp16 weights (lower_boost keeps them below fp16's
+  // largest value); a smaller headroom there keeps the boost high.
   constexpr float kTau = QUANT ? 2.0f : 8.0f;
+  constexpr float kWMax = QUANT ? 4.0f * 1.0001f : 256.0f * 1.0001f;
   bool fresh = true;
+  float vboost = kVBoost0;                      // quantized V: the wave's boost
+  float vlim = kFoldMax / (kWMax * kVBoost0);   // and the largest scale it admits
 
   const size_t kv_head_off = (size_t)kvh * SLICE;
   const size_t block_stride = (size_t)p.num_kv_heads * SLICE;
@@ -855,7 +700,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           ksf[4 * jj + v] = (float)as_h2(ksw[jj][v >> 1])[v & 1];
-          vsf[4 * jj + v] = (float)as_h2(vsw[jj][v >> 1])[v & 1] * kPvBoost;
+          vsf[4 * jj + v] = (float)as_h2(vsw[jj][v >> 1])[v & 1];
         }
       }
     }
@@ -863,7 +708,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
     h8 ka[NKK];
     if constexpr (QUANT) {
 #pragma unroll
-      for (int k = 0; k < KLD; ++k) codes16_to_h8<KV>(raw[k], ka[2 * k], ka[2 * k + 1]);
+      for (int k = 0; k < KLD; ++k) k_codes16<KV>(raw[k], ka[2 * k], ka[2 * k + 1]);
     } else {
 #pragma unroll
       for (int k = 0; k < KLD; ++k) ka[k] = __builtin_bit_cast(h8, raw[k]);
@@ -917,6 +762,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
           if (sl.t0 + 8 * (i / 4) + 4 * h + (i % 4) >= ltok) vsf[i] = 0.0f;
       }
     }
+    if constexpr (QUANT) {
+      // A V scale above what the wave's boost admits for weights up to
+      // 2^kTau (never one of an fp16 value at the initial boost of an E4M3
+      // cache): lower the boost first.  Lane (n, h) holds the scales of the
+      // step's tokens 8j + 4h + v, the same for every n.
+      float smax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) smax = fmaxf(smax, fabsf(vsf[i]));
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(smax > vlim) != 0, 0)) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax),
+                                                        __float_as_uint(smax), false, false);
+        const float sw = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        const float nbst = lower_boost(vboost, sw, kWMax);
+        const float f = nbst / vboost;
+#pragma unroll
+        for (int nb = 0; nb < NB2; ++nb) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[nb][t] *= f;
+          if constexpr (KV == PKV_I8) psum[nb] *= f;
+        }
+        vboost = nbst;
+        vlim = kFoldMax / (kWMax * nbst);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vsf[i] *= vboost;
+    }
     // Scores.  Base-2 score x = k * s (fp16 cache: k = qk_scale for every
     // token, so the block maximum is taken on the raw s and the scale is
     // applied inside the exponent's fma; quantized caches: the per-token K
@@ -954,7 +825,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
         bm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          x[nb][i] = (KV == PKV_I8 ? sc[i] - qbias[nb] : sc[i]) * ks * ksf[i];
+          x[nb][i] = sc[i] * ks * ksf[i];
           if (!masked || !((dead[nb] >> i) & 1u)) bm = fmaxf(bm, x[nb][i]);
         }
       } else {
@@ -1104,7 +975,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
     }
     Mx[nb] = M;
     den[nb] = z;
-    const float f = m[nb] == -INFINITY ? 0.0f : exp2f(m[nb] - M);
+    float f = m[nb] == -INFINITY ? 0.0f : exp2f(m[nb] - M);
+    if constexpr (QUANT) f *= 1.0f / vboost;   // undo the wave's V-scale boost
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[nb][t] *= f;
   }
@@ -1124,8 +996,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
     const bool direct = PREFILL && p.num_pparts == 1;
     const size_t orow = (size_t)col_seq[nb] * H + col_head[nb];
     const size_t row = orow * p.ws_stride + p.ws_pre + part;
-    float inv = 1.0f / den[nb];
-    if constexpr (QUANT) inv *= (1.0f / kPvBoost);
+    const float inv = 1.0f / den[nb];
     float *dst = direct ? nullptr : p.ws_o + row * D;
     f4 o[NT];
 #pragma unroll
@@ -1148,7 +1019,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
           *reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.out) + orow * D + e0) = v;
         else
           *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(p.out) + orow * D + e0) =
-              h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+              h4{to_f16_out(v[0]), to_f16_out(v[1]), to_f16_out(v[2]), to_f16_out(v[3])};
       } else {
         *reinterpret_cast<f4 *>(dst + e0) = v;
       }
@@ -1173,7 +1044,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p
 template <int KV, int D, int BS>
 hipError_t launch_prefix_typed(const PrefixParams &p, hipStream_t stream) {
   if constexpr (KV == PKV_F32)
-    hipLaunchKernelGGL((prefix_kernel<KV, D, BS, 2>), dim3((unsigned)prefix_grid(p)),
+    hipLaunchKernelGGL((prefix_kernel<D, BS, 2>), dim3((unsigned)prefix_grid(p)),
                        dim3(64 * kWaves), 0, stream, p);
   else
     hipLaunchKernelGGL((prefix32_kernel<KV, D, BS, kModeShared, PKV_F32>),
@@ -1246,7 +1117,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefixParams p) {
     *reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.out) + oi) = r;
   else
     *reinterpret_cast<h4 *>(reinterpret_cast<_Float16 *>(p.out) + oi) =
-        h4{(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
+        h4{to_f16_out(r[0]), to_f16_out(r[1]), to_f16_out(r[2]), to_f16_out(r[3])};
 }
 
 template <int KV, int D, int BS, int OUT>

@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import normal, permutation, randint, stream_key
+from . import normal, permutation, randint, stream_key, uniform01
 
 NP_DTYPE = {"f32": np.float32, "f16": np.float16}
 SEED_BASE = 387 * 1000
@@ -59,6 +59,8 @@ class Workload:
     description: str = ""
     memo: dict | None = None          # set to {} to keep generated K/V rows for reuse
     q_lens: list | None = None        # multi-token queries: query tokens per decode sequence
+    value_profile: str = "normal"     # K/V value distribution, see PROFILES
+    q_scale: float = 1.0              # queries are N(0, q_scale^2): large logits for q_scale >> 1
 
     @property
     def num_seqs(self) -> int:
@@ -73,7 +75,7 @@ class Workload:
         key = stream_key(self.seed, "q")
         rows = self.num_seqs if self.q_lens is None else int(sum(self.q_lens))
         n = rows * self.num_heads * self.head_dim
-        q = normal(key, 0, n).reshape(rows, self.num_heads, self.head_dim)
+        q = normal(key, 0, n).reshape(rows, self.num_heads, self.head_dim) * self.q_scale
         return q.astype(NP_DTYPE[self.q_dtype])
 
     def q_offsets(self) -> np.ndarray:
@@ -90,6 +92,8 @@ class Workload:
         key = stream_key(self.seed, "kv", which, owner)
         row = self.num_kv_heads * self.head_dim
         x = normal(key, start * row, count * row).reshape(count, self.num_kv_heads, self.head_dim)
+        if self.value_profile != "normal":
+            x = _apply_profile(x, self, which, owner, start)
         x = x.astype(NP_DTYPE[self.src_dtype])
         if self.memo is not None:
             self.memo[mk] = x
@@ -105,6 +109,67 @@ class Workload:
             if lo <= pos < hi:
                 return owner
         return seq
+
+
+# Value profiles of K/V (the pages name outliers as the weak point of int8 and
+# FP8 KV caches: single tokens, or particular positions of some KV heads, with
+# a far larger spread than the rest -- "KVcache-learning", s09).  Every draw is
+# keyed by (seed, which, owner, position, kv head), so a row's values do not
+# depend on how the rows are requested.
+#   normal            N(0, 1)
+#   row_outliers      about one (token, kv head) row in 24 is scaled by 2^e,
+#                     e uniform in [3, 16]; every 97th such row (and the row
+#                     of position 5 of every owner, kv head 0) is scaled so
+#                     that its largest magnitude is exactly the source
+#                     format's limit (65504 for fp16)
+#   channel_outliers  in each kv head, 2 dims (chosen per kv head) have
+#                     standard deviation 2^e, e uniform in [6, 12]
+# Values are clipped to the source format's finite range (fp16: +-65504,
+# fp32 sources: +-ROW_MAX_F32).
+PROFILES = ("normal", "row_outliers", "channel_outliers")
+ROW_MAX_F32 = 4.0e6          # fp32-source limit: its int8 scale 4e6/127 is a finite fp16
+
+
+def _apply_profile(x: np.ndarray, w: "Workload", which: str, owner: int, start: int):
+    count, hkv, d = x.shape
+    limit = 65504.0 if w.src_dtype == "f16" else ROW_MAX_F32
+    if w.value_profile == "row_outliers":
+        key = stream_key(w.seed, "outlier_rows", which, owner)
+        u = uniform01(key, 2 * start * hkv, 2 * count * hkv).reshape(count, hkv, 2)
+        pos = np.arange(start, start + count)[:, None]
+        hit = u[:, :, 0] < 1.0 / 24.0
+        e = 3.0 + 13.0 * u[:, :, 1]
+        f = np.where(hit, 2.0 ** e, 1.0)
+        amax = np.abs(x).max(axis=2)
+        full = (hit & ((np.floor(u[:, :, 1] * 1e6).astype(np.int64) % 97) == 0)) | \
+            ((pos == 5) & (np.arange(hkv)[None, :] == 0))
+        f = np.where(full, limit / np.maximum(amax, 1e-300), f)
+        x = x * f[:, :, None]
+    elif w.value_profile == "channel_outliers":
+        key = stream_key(w.seed, "outlier_channels", which)
+        u = uniform01(key, 0, 3 * hkv).reshape(hkv, 3)
+        dims = np.stack([np.floor(u[:, 0] * d), np.floor(u[:, 1] * d)], 1).astype(np.int64)
+        sd = 2.0 ** (6.0 + 6.0 * u[:, 2])
+        x = x.copy()
+        for h in range(hkv):
+            x[:, h, dims[h]] *= sd[h]
+    else:
+        raise ValueError(f"unknown value profile {w.value_profile!r}")
+    return np.clip(x, -limit, limit)
+
+
+def with_values(w: "Workload", profile: str = "normal", q_scale: float = 1.0) -> "Workload":
+    """The same workload (same script, shapes and seeds) with K/V drawn from
+    `profile` and queries scaled by q_scale."""
+    import copy
+    if profile not in PROFILES:
+        raise ValueError(profile)
+    w2 = copy.copy(w)
+    w2.value_profile = profile
+    w2.q_scale = float(q_scale)
+    w2.memo = None
+    w2.name = f"{w.name}_{profile}_q{q_scale:g}"
+    return w2
 
 
 def _cfg_seed(i: int) -> int:
