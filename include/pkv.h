@@ -12,7 +12,9 @@
  *  - Plain C types only.  Pointers documented "device" must point to device
  *    memory of the current HIP device; "host" pointers to host memory.
  *  - The caller owns every buffer.  The library never allocates device memory
- *    and keeps no pointer after a call returns.  Device work is enqueued
+ *    (its one device array, the fixed scratch of the allocation-free decode
+ *    entry point, exists from the library's load) and keeps no pointer after
+ *    a call returns.  Device work is enqueued
  *    asynchronously on `stream` (a hipStream_t passed as void*, NULL = the
  *    default stream); buffers must stay alive until that work completes.
  *  - Arguments are validated on the host before anything is launched; a
@@ -41,6 +43,7 @@ extern "C" {
 #define PKV_EEXIST   (-4)  /* sequence id already exists */
 #define PKV_EDEVICE  (-5)  /* HIP error while launching */
 #define PKV_ENOTSUP  (-6)  /* valid but unsupported (dtype combination, head_dim, GPU arch) */
+#define PKV_ESCRATCH (-7)  /* needs more scratch than an allocation-free entry point holds */
 
 /* Static text for a status code. */
 const char *pkv_strerror(int status);
@@ -365,6 +368,28 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            float scale, int32_t partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it): the same call as
+ * paged_attention_decode, with the same results and the same kernels, but the
+ * split-K partials go to the library's own scratch array instead of a caller
+ * workspace -- one static device array of PKV_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends.  Nothing is allocated or freed.  A call whose
+ * partials need more than that (paged_attention_workspace_bytes of the same
+ * arguments) returns PKV_ESCRATCH and enqueues nothing.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, not otherwise ordered) race and must not be issued; calls on one
+ * stream are ordered and safe.  The array's contents on entry do not matter.
+ * Other arguments and errors as paged_attention_decode. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int paged_attention_decode_noalloc(void *out, int32_t out_dtype, const void *query,
+                                   int32_t q_dtype, const void *k_cache, const void *v_cache,
+                                   const void *k_scale, const void *v_scale,
+                                   int32_t cache_dtype, int32_t num_blocks,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   float scale, int32_t partition_size, void *stream);
 
 /* Fused decode step: for every sequence s with L = seq_lens[s] > 0,
  *   1. if cow_src (nullable, device int32 [num_seqs]) has cow_src[s] >= 0,

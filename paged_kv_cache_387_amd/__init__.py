@@ -17,7 +17,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-OK, EINVAL, ENOMEM, ENOENT, EEXIST, EDEVICE, ENOTSUP = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, ENOMEM, ENOENT, EEXIST, EDEVICE, ENOTSUP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 F32, F16, I8, E4M3 = 0, 1, 3, 4
 DTYPE = {"f32": F32, "f16": F16, "i8": I8, "e4m3": E4M3}
 ELEM_BYTES = {F32: 4, F16: 2, I8: 1, E4M3: 1}
@@ -35,7 +36,8 @@ EXPORTS = [
     "pkv_seq_allocate_cached", "pkv_seq_cache_blocks", "pkv_prefix_cache_evict",
     "pkv_prefix_cache_size", "pkv_prefix_cache_evictable", "paged_swap_blocks",
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
-    "paged_attention_workspace_bytes", "paged_attention_decode", "paged_decode_step",
+    "paged_attention_workspace_bytes", "paged_attention_decode",
+    "paged_attention_decode_noalloc", "paged_decode_step",
     "paged_attention_shared_workspace_bytes", "paged_attention_decode_shared",
     "paged_attention_prefill_workspace_bytes", "paged_attention_prefill",
     "pkv_stream_read", "pkv_stream_copy",
@@ -109,6 +111,9 @@ def lib() -> ctypes.CDLL:
             "paged_attention_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
             "paged_attention_decode": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32, P, i32,
                                         i32, i32, i32, i32, f32, i32, P, sz, P], ctypes.c_int),
+            "paged_attention_decode_noalloc": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32,
+                                                P, i32, i32, i32, i32, i32, f32, i32, P],
+                                               ctypes.c_int),
             "paged_decode_step": ([P, i32, P, i32, P, P, i32, P, P, P, P, P, i32, i32, P, i32,
                                    P, i32, i32, i32, i32, i32, f32, i32, P, sz, P],
                                   ctypes.c_int),
@@ -566,6 +571,34 @@ def paged_attention_decode(query, cache: PagedKVCache, block_tables, seq_lens, s
         _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
         cache.block_size, float(scale), partition_size, ws_ptr, ws_len, _stream_ptr(stream)),
         "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(query, cache: PagedKVCache, block_tables, seq_lens,
+                                   scale: float, out, partition_size: int = 0, stream=None):
+    """paged_attention_decode with the split-K partials in the library's own
+    scratch array (no workspace, nothing allocated by the library; `out` is
+    the caller's)."""
+    torch = _torch()
+    S, H, D = query.shape
+    q_dt = {torch.float32: F32, torch.float16: F16}.get(query.dtype)
+    o_dt = {torch.float32: F32, torch.float16: F16}.get(out.dtype)
+    if q_dt is None or o_dt is None or tuple(out.shape) != (S, H, D):
+        raise ValueError("query / out must be float32 or float16 [num_seqs, num_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    maxb = block_tables.shape[1]
+    nbytes = cache_bytes(cache.num_blocks, cache.num_kv_heads, D, cache.cache_dtype,
+                         cache.block_size)
+    ks, vs = cache._scales()
+    _check(lib().paged_attention_decode_noalloc(
+        _dev(out, "out"), o_dt, _dev(query, "query"), q_dt,
+        _dev(cache.k, "k_cache", numel=nbytes), _dev(cache.v, "v_cache", numel=nbytes), ks, vs,
+        cache.cache_dtype, cache.num_blocks,
+        _dev(block_tables, "block_tables", torch.int32, S * maxb), maxb,
+        _dev(seq_lens, "seq_lens", torch.int32, S), S, H, cache.num_kv_heads, D,
+        cache.block_size, float(scale), partition_size, _stream_ptr(stream)),
+        "paged_attention_decode_noalloc")
     return out
 
 

@@ -213,6 +213,7 @@ const char *pkv_strerror(int status) {
     case PKV_EEXIST: return "sequence id already exists";
     case PKV_EDEVICE: return "HIP device error";
     case PKV_ENOTSUP: return "unsupported configuration or device";
+    case PKV_ESCRATCH: return "more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -375,6 +376,68 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
   if (st != PKV_OK || num_seqs == 0) return st;
   return status_of(launch_decode(p, cache_dtype, out_dtype, head_dim,
                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of paged_attention_decode_noalloc: the split-K partials live in
+// this file-scope device array instead of a caller's workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  On the host the
+// name `scratch` is only a stand-in for the symbol, never a device address:
+// host code uses the address scratch_ptr looks up.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+// This device's address of `scratch`, looked up with hipGetSymbolAddress the
+// first time a device calls (with that device current) and kept per device.
+int scratch_ptr(void **out) {
+  static std::mutex mu;
+  static void *ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EDEVICE;
+  if (dev < 0 || dev >= 64) return PKV_ENOTSUP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return PKV_EDEVICE;
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode_noalloc(void *out, int32_t out_dtype, const void *query,
+                                   int32_t q_dtype, const void *k_cache, const void *v_cache,
+                                   const void *k_scale, const void *v_scale,
+                                   int32_t cache_dtype, int32_t num_blocks,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   float scale, int32_t partition_size, void *stream) {
+  // the partials this call needs (0 for one pass per sequence, and for
+  // arguments paged_attention_decode rejects)
+  const size_t need = paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                                      head_dim, max_blocks_per_seq, block_size,
+                                                      partition_size);
+  if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ESCRATCH;
+  void *ws = nullptr;
+  if (need > 0) {
+    const int dev = check_device();
+    if (dev != PKV_OK) return dev;
+    const int st = scratch_ptr(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return paged_attention_decode(out, out_dtype, query, q_dtype, k_cache, v_cache, k_scale,
+                                v_scale, cache_dtype, num_blocks, block_tables,
+                                max_blocks_per_seq, seq_lens, num_seqs, num_heads, num_kv_heads,
+                                head_dim, block_size, scale, partition_size, ws,
+                                need > 0 ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int paged_decode_step(void *out, int32_t out_dtype, const void *query, int32_t q_dtype,

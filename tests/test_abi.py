@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_and_version():
     assert pkv.strerror(0) == "ok"
-    for st in (-1, -2, -3, -4, -5, -6):
+    for st in (-1, -2, -3, -4, -5, -6, -7):
         assert pkv.strerror(st) and pkv.strerror(st) != "unknown status"
     assert pkv.lib().pkv_version() >= 100
 
