@@ -13,19 +13,25 @@ one paged_decode_step call (copy, write and decode fused in one launch);
 The host allocator's results for all steps are computed before the timed
 region and uploaded, so the timed steps read resident inputs; the allocator's
 own cost is reported separately (host_alloc_us_per_step).  The timed steps are
-captured in one HIP graph and replayed once.  Several disjoint batches from
+captured in one HIP graph, replayed once untimed and then five times, each
+replay timed on its own; the median is reported.  Several disjoint batches from
 one block pool are used in rotation so that the working set exceeds the 256 MB
 Infinity Cache and the KV reads come from HBM (stand-in for the per-layer
 caches of a real model).
 
 value = KV bytes read per step / step time (GB/s).  roofline: the decode
-kernel's algorithmic bytes per launch / its average duration (HIP events
-around a graph of back-to-back decode launches on the launch stream).
+call's algorithmic bytes per launch (each physical block once) / its average
+duration (HIP events around graph replays of back-to-back decode launches on
+the launch stream, median of five).  The default run reports the
+Qwen3-32B-shaped layer and, in "configs", the 8 x 32K split-K decode, the
+quantized decode over int8 and E4M3 caches and the shared-prefix step, each
+measured the same way in the same process.
 cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -369,18 +375,7 @@ def bench_prefill(args, torch, pkv, driver) -> int:
         for _ in range(Wm):
             fn()
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(n):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return float(np.median(graph_ms(torch, [fn] * n))) / n
 
     step_ms = timed(step, K)
     attn_ms = timed(attn, K)
@@ -449,18 +444,7 @@ def bench_swap(args, torch, pkv) -> int:
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return float(np.median(graph_ms(torch, [fn] * reps))) / reps
 
     out_ms = timed(lambda: pkv.paged_swap_blocks(cache, host, out_pairs, to_host=True))
     in_ms = timed(lambda: pkv.paged_swap_blocks(cache, host, in_pairs, to_host=False))
@@ -553,12 +537,278 @@ def bench_len_sweep(args, torch, pkv) -> int:
     return 0
 
 
+def unique_kv_bytes(tables, lens, w) -> int:
+    """Algorithmic bytes of one decode call counting each physical block once:
+    a block that several sequences share (a forked prefix) is read for all of
+    them from the same place, so it counts once, with its filled tokens.  Plus
+    q, out, the table entries and the lengths, as kv_bytes."""
+    bs = w.block_size
+    filled = {}
+    ntab = 0
+    for row, L in zip(tables, lens):
+        nb = -(-int(L) // bs)
+        ntab += nb
+        for i in range(nb):
+            b = int(row[i])
+            filled[b] = max(filled.get(b, 0), min(bs, int(L) - i * bs))
+    b = kv_read_bytes([sum(filled.values())], w)
+    b += len(lens) * w.num_heads * w.head_dim * (EB[w.q_dtype] + EB[w.out_dtype])
+    return b + 4 * ntab + 4 * len(lens)
+
+
+TIMED_REPLAYS = 5
+
+
+def graph_ms(torch, calls, reps: int = TIMED_REPLAYS):
+    """Capture `calls` (a list of no-argument launches) in one HIP graph,
+    replay it once untimed, then `reps` times, each timed with HIP events on
+    the launch stream and synchronized on both sides.  Returns the
+    milliseconds of each timed replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del g
+    return out
+
+
+def measure(args, name: str, torch, pkv, driver, shared: bool = False, partition: int = -1,
+            steps: int = 200, warmup: int = 20, block_size: int = 16, replicas: int = 0,
+            unfused: bool = False, no_graph: bool = False, memo=None):
+    """One workload's decode steps, timed: returns the result fields (value,
+    ms_per_step, roofline, ...) of its bench line."""
+    factory, replicas_default, pool = _workloads()[name]
+    R = replicas or replicas_default
+    bs = block_size
+    ws = [factory(r) for r in range(R)]
+    if bs != 16:
+        from synth.workloads import with_block_size
+        ws = [with_block_size(w, bs) for w in ws]
+        pool = pool and -(-pool * 16 // bs)   # the same token capacity
+    w0 = ws[0]
+    K, Wm = steps, warmup
+    total_steps = Wm + K
+    growth = -(-total_steps // R) + 1
+    max_len = max(max(int(op[2]) for op in w.ops if op[0] == "allocate") for w in ws)
+    maxb = -(-(max_len + growth) // bs)
+    need_blocks = sum(sum(-(-int(op[2]) // bs) for op in w.ops if op[0] == "allocate")
+                      for w in ws)
+    num_blocks = pool or int(math.ceil((need_blocks + R * len(w0.decode_seqs) * (growth // bs + 2))
+                                       * 1.1))
+    if pool and num_blocks == w0.num_blocks:
+        order = w0.free_order
+    else:
+        from synth import permutation, stream_key
+        order = permutation(stream_key(w0.seed, "bench_pool"), num_blocks)
+    part = w0.partition_size if partition < 0 else partition
+    print(f"# setup {name}: {R} batch(es) of {w0.num_seqs} seqs, pool {num_blocks} "
+          f"blocks, table width {maxb}, partition {part}", file=sys.stderr, flush=True)
+
+    alloc = pkv.BlockAllocator(num_blocks, bs, order)
+    cache = pkv.PagedKVCache(num_blocks, w0.num_kv_heads, w0.head_dim, w0.cache_dtype,
+                             block_size=bs)
+    OFF = 1 << 24
+    batches = []
+    for r, w in enumerate(ws):
+        if memo is not None:      # K/V rows shared with another run of the same script
+            w.memo = memo.setdefault(r, {})
+        driver.replay(w, alloc=alloc, cache=cache, seq_offset=r * OFF, stop_at_step=True)
+        w.memo = None
+        seqs = [s + r * OFF for s in w.decode_seqs]
+        q = torch.from_numpy(w.query()).cuda()
+        rng = np.random.default_rng(r)
+        newk = torch.from_numpy(rng.standard_normal(
+            (len(seqs), w.num_kv_heads, w.head_dim)).astype(np.float16)).cuda()
+        newv = torch.from_numpy(rng.standard_normal(
+            (len(seqs), w.num_kv_heads, w.head_dim)).astype(np.float16)).cuda()
+        if w.src_dtype == "f32":
+            newk, newv = newk.float(), newv.float()
+        odt = torch.float16 if w.out_dtype == "f16" else torch.float32
+        out = torch.empty((len(seqs), w.num_heads, w.head_dim), dtype=odt, device="cuda")
+        batches.append(dict(seqs=seqs, ids=np.ascontiguousarray(seqs, dtype=np.int64), q=q,
+                            k=newk, v=newv, out=out))
+    torch.cuda.synchronize()
+
+    # host allocator for every step, ahead of time: one pkv_seq_step call per
+    # step (appends, copy sources, tables, lengths), timed around the C call
+    # itself; the same call with an empty batch (argument passing only) is
+    # timed too and subtracted, which leaves the allocator's own work
+    steps_l = []
+    t_host, t_empty = 0.0, 0.0
+    L_ = pkv.lib()
+    n_ = len(batches[0]["seqs"])
+    buf = {"tables": np.empty((n_, maxb), np.int32), "lens": np.empty(n_, np.int32),
+           "cow_src": np.empty(n_, np.int32), "slots": np.empty(n_, np.int64)}
+    ptrs = [b_.ctypes.data_as(ctypes.c_void_p) for b_ in
+            (buf["slots"], buf["cow_src"], buf["tables"], buf["lens"])]
+    for i in range(total_steps):
+        b = batches[i % R]
+        ids = b["ids"]
+        idp = ids.ctypes.data_as(ctypes.c_void_p)
+        t0 = time.perf_counter()
+        st_ = L_.pkv_seq_step(alloc._h, idp, n_, maxb, *ptrs)
+        t1 = time.perf_counter()
+        L_.pkv_seq_step(alloc._h, idp, 0, maxb, *ptrs)
+        t2 = time.perf_counter()
+        if st_ != 0:
+            raise pkv.PkvError(st_, "pkv_seq_step")
+        t_host += t1 - t0
+        t_empty += t2 - t1
+        tables, lens = buf["tables"].copy(), buf["lens"].copy()
+        src, slots = buf["cow_src"].copy(), buf["slots"].copy()
+        sh = alloc.export_shared(b["seqs"], maxb, maxb) if shared else None
+        pairs = np.stack([src, tables[np.arange(n_), (lens - 1) // bs]], 1)[src >= 0]
+        steps_l.append(dict(b=i % R, slots=torch.from_numpy(slots).cuda(),
+                            cow_src=torch.from_numpy(src).cuda(),
+                            pairs=torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
+                            if len(pairs) else None, npairs=len(pairs),
+                            tables=torch.from_numpy(tables).cuda(), tables_host=tables,
+                            lens=torch.from_numpy(lens).cuda(), lens_host=lens, sh=sh))
+    host_alloc_us = max(0.0, t_host - t_empty) / total_steps * 1e6
+    host_call_us = t_host / total_steps * 1e6
+    S, H, D, Hkv = w0.num_seqs, w0.num_heads, w0.head_dim, w0.num_kv_heads
+    workspace = pkv.alloc_workspace(S, H, Hkv, D, maxb, part, block_size=bs)
+    if shared:
+        # suffix tables cut to the widest suffix of any step; device group arrays
+        msb = max(1, max(-(-int(st["sh"]["suffix_lens"].max()) // bs) for st in steps_l))
+        ws_need = 0
+        for st in steps_l:
+            sh = st["sh"]
+            st["grp"] = pkv.PrefixGroups(sh)
+            st["stables"] = torch.from_numpy(
+                np.ascontiguousarray(sh["suffix_tables"][:, :msb])).cuda()
+            st["slens"] = torch.from_numpy(sh["suffix_lens"]).cuda()
+            ws_need = max(ws_need, pkv.shared_workspace_bytes(S, H, Hkv, D, msb, st["grp"],
+                                                              part, bs))
+        workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device="cuda")
+        print(f"# shared: {steps_l[0]['sh']['num_groups']} group(s), prefix "
+              f"{steps_l[0]['sh']['group_prefix_lens'].tolist()}, suffix width {msb} blocks",
+              file=sys.stderr, flush=True)
+    scale = float(np.float32(w0.scale))
+    torch.cuda.synchronize()
+
+    def run_step(st):
+        b = batches[st["b"]]
+        if shared:
+            pkv.paged_attention_decode_shared(b["q"], cache, st["stables"], st["slens"], scale,
+                                              st["grp"], key=b["k"], value=b["v"],
+                                              cow_src=st["cow_src"], out=b["out"],
+                                              partition_size=part, workspace=workspace)
+        elif unfused:
+            if st["pairs"] is not None:
+                pkv.paged_copy_blocks(cache, st["pairs"])
+            pkv.paged_kv_write(b["k"], b["v"], st["slots"], cache)
+            pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale,
+                                       out=b["out"], partition_size=part, workspace=workspace)
+        else:
+            pkv.paged_decode_step(b["q"], b["k"], b["v"], cache, st["tables"], st["lens"], scale,
+                                  cow_src=st["cow_src"], out=b["out"], partition_size=part,
+                                  workspace=workspace)
+
+    for st in steps_l[:Wm]:
+        run_step(st)
+    torch.cuda.synchronize()
+
+    timed = steps_l[Wm:]
+    if no_graph:
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for st in timed:
+            run_step(st)
+        ev1.record()
+        torch.cuda.synchronize()
+        step_reps = [ev0.elapsed_time(ev1)]
+    else:
+        step_reps = graph_ms(torch, [lambda st=st: run_step(st) for st in timed])
+    step_ms = float(np.median(step_reps)) / K
+    bytes_step = np.mean([kv_read_bytes(st["lens_host"], w0) for st in timed])
+    value = bytes_step / (step_ms * 1e-3) / 1e9
+
+    # the decode call alone: back-to-back launches in a graph, HIP events
+    # around each replay, median of the replays
+    last = {}
+    for st in timed:
+        last[st["b"]] = st
+    dec_steps = [last[i % R] for i in range(K)] if len(last) == R else timed
+    single_pass = pkv.workspace_bytes(S, H, Hkv, D, maxb, part, bs) == 0
+
+    def run_decode(st):
+        b = batches[st["b"]]
+        if shared:
+            pkv.paged_attention_decode_shared(b["q"], cache, st["stables"], st["slens"], scale,
+                                              st["grp"], out=b["out"], partition_size=part,
+                                              workspace=workspace)
+            return
+        pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale, out=b["out"],
+                                   partition_size=part, workspace=workspace)
+
+    dec_reps = graph_ms(torch, [lambda st=st: run_decode(st) for st in dec_steps])
+    dec_ms = float(np.median(dec_reps)) / len(dec_steps)
+    logical = np.mean([kv_bytes(st["lens_host"], w0) for st in dec_steps])
+    if shared:
+        dec_alg = np.mean([kv_bytes_shared(st["sh"], w0) for st in dec_steps])
+    else:
+        dec_alg = np.mean([unique_kv_bytes(st["tables_host"], st["lens_host"], w0)
+                           for st in dec_steps])
+    achieved = dec_alg / (dec_ms * 1e-3) / 1e9
+    traffic = read_traffic(name) if not shared else None
+
+    mean_len = float(np.mean([st["lens_host"].mean() for st in timed]))
+    res = {
+        "value": round(value, 2), "unit": "GB/s", "ms_per_step": round(step_ms, 5),
+        "dtype": w0.cache_dtype,
+        "config": {"workload": w0.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": bs, "kv_dtype": w0.cache_dtype,
+                   "mean_seq_len": round(mean_len, 1), "pool_blocks": num_blocks,
+                   "rotating_batches": R, "partition_size": part,
+                   "split_k": not single_pass, "graph": not no_graph,
+                   "fused_step": not unfused, "shared_prefix": bool(shared)},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "seqs_per_s": round(S / (step_ms * 1e-3), 1),
+        "tokens_per_s": round(S / (step_ms * 1e-3), 1),
+        "host_alloc_us_per_step": round(host_alloc_us, 2),
+        "host_alloc_call_us_per_step": round(host_call_us, 2),
+        "decode_kernel_ms": round(dec_ms, 5),
+        "timing": f"median of {len(step_reps)} graph replays of {K} steps (decode call: of "
+                  f"{len(dec_reps)} replays of {len(dec_steps)} calls)",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": int(dec_alg)},
+    }
+    if abs(logical - dec_alg) > 0.01 * dec_alg:
+        res["roofline"]["logical_bytes_per_launch"] = int(logical)
+    del cache, workspace, batches, steps_l
+    torch.cuda.empty_cache()
+    return res, factory
+
+
+# The default run's further configurations: the 8 x 32K split-K decode (its
+# 512-token partitions), the quantized decode over int8 and E4M3 caches, and
+# the shared-prefix step through the shared-prefix path.
+DEFAULT_CONFIGS = [("c3", dict()), ("c4_i8", dict(memo="c4")), ("c4_e4m3", dict(memo="c4")),
+                   ("c5", dict(shared=True))]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=sorted(_workloads()))
+    ap.add_argument("--workload", default=None, choices=sorted(_workloads()),
+                    help="one workload only (default: c2, plus the configurations of "
+                         "DEFAULT_CONFIGS in the same line)")
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens (-1: the workload's, 0: library choice)")
     ap.add_argument("--replicas", type=int, default=0, help="rotating batches (0: default)")
@@ -575,6 +825,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default run: leave out the further configurations")
     ap.add_argument("--len-sweep", action="store_true",
                     help="decode cost per call against sequence length at the Qwen3-32B layer shape")
     ap.add_argument("--pmc-copy", action="store_true",
@@ -589,10 +841,12 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize-*: command line that produced a CSV")
     args = ap.parse_args()
+    default_run = args.workload is None
+    workload = args.workload or "c2"
     if args.summarize_traffic:
-        return summarize_traffic(args.workload, *args.summarize_traffic, args.command)
+        return summarize_traffic(workload, *args.summarize_traffic, args.command)
     if args.summarize_trace:
-        wl = args.workload + ("_shared" if args.shared else "")
+        wl = workload + ("_shared" if args.shared else "")
         return summarize_trace(wl, *args.summarize_trace, args.command)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
@@ -612,204 +866,37 @@ def main():
         return pmc_copy()
     if args.len_sweep:
         return bench_len_sweep(args, torch, pkv)
-    if args.workload == "prefill":
+    if workload == "prefill":
         return bench_prefill(args, torch, pkv, driver)
-    if args.workload == "swap":
+    if workload == "swap":
         return bench_swap(args, torch, pkv)
-    factory, replicas, pool = _workloads()[args.workload]
-    R = args.replicas or replicas
-    bs = args.block_size
-    ws = [factory(r) for r in range(R)]
-    if bs != 16:
-        from synth.workloads import with_block_size
-        ws = [with_block_size(w, bs) for w in ws]
-        pool = pool and -(-pool * 16 // bs)   # the same token capacity
-    w0 = ws[0]
+
     K, Wm = args.steps, args.warmup
-    total_steps = Wm + K
-    growth = -(-total_steps // R) + 1
-    max_len = max(max(int(op[2]) for op in w.ops if op[0] == "allocate") for w in ws)
-    maxb = -(-(max_len + growth) // bs)
-    need_blocks = sum(sum(-(-int(op[2]) // bs) for op in w.ops if op[0] == "allocate")
-                      for w in ws)
-    num_blocks = pool or int(math.ceil((need_blocks + R * len(w0.decode_seqs) * (growth // bs + 2))
-                                       * 1.1))
-    if pool and num_blocks == w0.num_blocks:
-        order = w0.free_order
-    else:
-        from synth import permutation, stream_key
-        order = permutation(stream_key(w0.seed, "bench_pool"), num_blocks)
-    part = w0.partition_size if args.partition < 0 else args.partition
-    print(f"# setup {args.workload}: {R} batch(es) of {w0.num_seqs} seqs, pool {num_blocks} "
-          f"blocks, table width {maxb}, partition {part}", file=sys.stderr, flush=True)
-
-    alloc = pkv.BlockAllocator(num_blocks, bs, order)
-    cache = pkv.PagedKVCache(num_blocks, w0.num_kv_heads, w0.head_dim, w0.cache_dtype,
-                             block_size=bs)
-    OFF = 1 << 24
-    batches = []
-    for r, w in enumerate(ws):
-        driver.replay(w, alloc=alloc, cache=cache, seq_offset=r * OFF, stop_at_step=True)
-        seqs = [s + r * OFF for s in w.decode_seqs]
-        q = torch.from_numpy(w.query()).cuda()
-        rng = np.random.default_rng(r)
-        newk = torch.from_numpy(rng.standard_normal(
-            (len(seqs), w.num_kv_heads, w.head_dim)).astype(np.float16)).cuda()
-        newv = torch.from_numpy(rng.standard_normal(
-            (len(seqs), w.num_kv_heads, w.head_dim)).astype(np.float16)).cuda()
-        if w.src_dtype == "f32":
-            newk, newv = newk.float(), newv.float()
-        odt = torch.float16 if w.out_dtype == "f16" else torch.float32
-        out = torch.empty((len(seqs), w.num_heads, w.head_dim), dtype=odt, device="cuda")
-        batches.append(dict(seqs=seqs, q=q, k=newk, v=newv, out=out))
-    torch.cuda.synchronize()
-
-    # host allocator for every step, ahead of time
-    steps = []
-    t_host = 0.0
-    for i in range(total_steps):
-        b = batches[i % R]
-        t0 = time.perf_counter()
-        slots, pairs, src = alloc.append_slots(b["seqs"], with_src=True)
-        tables, lens = alloc.export_tables(b["seqs"], maxb)
-        sh = alloc.export_shared(b["seqs"], maxb, maxb) if args.shared else None
-        t_host += time.perf_counter() - t0
-        steps.append(dict(b=i % R, slots=torch.from_numpy(slots).cuda(),
-                          cow_src=torch.from_numpy(src.astype(np.int32)).cuda(),
-                          pairs=torch.from_numpy(np.ascontiguousarray(pairs)).cuda()
-                          if len(pairs) else None, npairs=len(pairs),
-                          tables=torch.from_numpy(tables).cuda(),
-                          lens=torch.from_numpy(lens).cuda(), lens_host=lens, sh=sh))
-    host_alloc_us = t_host / total_steps * 1e6
-    S, H, D, Hkv = w0.num_seqs, w0.num_heads, w0.head_dim, w0.num_kv_heads
-    workspace = pkv.alloc_workspace(S, H, Hkv, D, maxb, part, block_size=bs)
-    if args.shared:
-        # suffix tables cut to the widest suffix of any step; device group arrays
-        msb = max(1, max(-(-int(st["sh"]["suffix_lens"].max()) // bs) for st in steps))
-        ws_need = 0
-        for st in steps:
-            sh = st["sh"]
-            st["grp"] = pkv.PrefixGroups(sh)
-            st["stables"] = torch.from_numpy(
-                np.ascontiguousarray(sh["suffix_tables"][:, :msb])).cuda()
-            st["slens"] = torch.from_numpy(sh["suffix_lens"]).cuda()
-            ws_need = max(ws_need, pkv.shared_workspace_bytes(S, H, Hkv, D, msb, st["grp"],
-                                                              part, bs))
-        workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device="cuda")
-        print(f"# shared: {steps[0]['sh']['num_groups']} group(s), prefix "
-              f"{steps[0]['sh']['group_prefix_lens'].tolist()}, suffix width {msb} blocks",
-              file=sys.stderr, flush=True)
-    scale = float(np.float32(w0.scale))
-    torch.cuda.synchronize()
-
-    def run_step(st):
-        b = batches[st["b"]]
-        if args.shared:
-            pkv.paged_attention_decode_shared(b["q"], cache, st["stables"], st["slens"], scale,
-                                              st["grp"], key=b["k"], value=b["v"],
-                                              cow_src=st["cow_src"], out=b["out"],
-                                              partition_size=part, workspace=workspace)
-        elif args.unfused:
-            if st["pairs"] is not None:
-                pkv.paged_copy_blocks(cache, st["pairs"])
-            pkv.paged_kv_write(b["k"], b["v"], st["slots"], cache)
-            pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale,
-                                       out=b["out"], partition_size=part, workspace=workspace)
-        else:
-            pkv.paged_decode_step(b["q"], b["k"], b["v"], cache, st["tables"], st["lens"], scale,
-                                  cow_src=st["cow_src"], out=b["out"], partition_size=part,
-                                  workspace=workspace)
-
-    for st in steps[:Wm]:
-        run_step(st)
-    torch.cuda.synchronize()
-
-    timed = steps[Wm:]
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
-        torch.cuda.synchronize()
-        ev0.record()
-        for st in timed:
-            run_step(st)
-        ev1.record()
-        torch.cuda.synchronize()
-    else:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for st in timed:
-                run_step(st)
-        g.replay()                      # untimed: first launch of the graph
-        torch.cuda.synchronize()
-        ev0.record()
-        g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-    step_ms = ev0.elapsed_time(ev1) / K
-    bytes_step = np.mean([kv_read_bytes(st["lens_host"], w0) for st in timed])
-    alg_step = np.mean([kv_bytes(st["lens_host"], w0) for st in timed])
-    value = bytes_step / (step_ms * 1e-3) / 1e9
-
-    # decode kernel alone: back-to-back launches in a graph, HIP events around it
-    last = {}
-    for st in timed:
-        last[st["b"]] = st
-    dec_steps = [last[i % R] for i in range(K)] if len(last) == R else timed
-    single_pass = pkv.workspace_bytes(S, H, Hkv, D, maxb, part, bs) == 0
-
-    def run_decode(st):
-        b = batches[st["b"]]
-        if args.shared:
-            pkv.paged_attention_decode_shared(b["q"], cache, st["stables"], st["slens"], scale,
-                                              st["grp"], out=b["out"], partition_size=part,
-                                              workspace=workspace)
-            return
-        pkv.paged_attention_decode(b["q"], cache, st["tables"], st["lens"], scale, out=b["out"],
-                                   partition_size=part, workspace=workspace)
-
-    gd = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gd):
-        for st in dec_steps:
-            run_decode(st)
-    gd.replay()
-    torch.cuda.synchronize()
-    ev0.record()
-    gd.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    dec_ms = ev0.elapsed_time(ev1) / len(dec_steps)
-    if args.shared:
-        dec_alg = np.mean([kv_bytes_shared(st["sh"], w0) for st in dec_steps])
-    else:
-        dec_alg = np.mean([kv_bytes(st["lens_host"], w0) for st in dec_steps])
-    achieved = dec_alg / (dec_ms * 1e-3) / 1e9
-
-    traffic = read_traffic(args.workload)
-
-    mean_len = float(np.mean([st["lens_host"].mean() for st in timed]))
-    result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": Wm, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w0.cache_dtype, "data": "synthetic",
-        "config": {"workload": w0.name, "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": bs, "kv_dtype": w0.cache_dtype,
-                   "mean_seq_len": round(mean_len, 1), "pool_blocks": num_blocks,
-                   "rotating_batches": R, "partition_size": part,
-                   "split_k": not single_pass, "graph": not args.no_graph,
-                   "fused_step": not args.unfused, "shared_prefix": bool(args.shared)},
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "seqs_per_s": round(S / (step_ms * 1e-3), 1),
-        "tokens_per_s": round(S / (step_ms * 1e-3), 1),
-        "host_alloc_us_per_step": round(host_alloc_us, 2),
-        "decode_kernel_ms": round(dec_ms, 5),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": int(dec_alg)},
-        "cpu_baseline": None,
-        "hbm_read_ceiling_gbs": None if args.no_ceiling else read_ceiling(torch, pkv),
-    }
+    res, factory = measure(args, workload, torch, pkv, driver, shared=args.shared,
+                           partition=args.partition, steps=K, warmup=Wm,
+                           block_size=args.block_size, replicas=args.replicas,
+                           unfused=args.unfused, no_graph=args.no_graph)
+    result = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"),
+              "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": res.pop("ms_per_step"),
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": res.pop("dtype"), "data": "synthetic", "config": res.pop("config")}
+    result.update(res)
+    result["cpu_baseline"] = None
+    result["hbm_read_ceiling_gbs"] = None if args.no_ceiling else read_ceiling(torch, pkv)
+    if default_run and not args.no_configs:
+        configs, memos = {}, {}
+        for name, kw in DEFAULT_CONFIGS:
+            memo = memos.setdefault(kw["memo"], {}) if "memo" in kw else None
+            r2, _ = measure(args, name, torch, pkv, driver, shared=kw.get("shared", False),
+                            steps=K, warmup=Wm, memo=memo)
+            configs[name + ("_shared" if kw.get("shared") else "")] = r2
+            print(f"# {name}: {r2['decode_kernel_ms'] * 1e3:.2f} us per decode call, "
+                  f"roofline frac {r2['roofline']['frac']}", file=sys.stderr, flush=True)
+        memos.clear()
+        result["configs"] = configs
     if not args.no_cpu_baseline:
         wb = factory(0)
-        if args.workload == "c3":
+        if workload == "c3":
             from synth import workloads as W
             wb = W.c3_long_context(num_seqs=1)
         result["cpu_baseline"] = cpu_baseline(wb, args.cpu_budget)

@@ -136,11 +136,28 @@ int pkv_seq_append_slot(pkv_alloc *a, int64_t seq_id, int64_t *slot, int32_t *co
  * [src, dst] rows and their count to *num_cow (cow_pairs needs room for n
  * rows); cow_src (nullable, [n]) receives for each sequence the source block
  * of its copy (the destination is its new tail block), -1 if none -- the form
- * paged_decode_step takes.  Stops at the first failure and returns its
- * status; *num_done (nullable) receives how many sequences were appended. */
+ * paged_decode_step takes.  All or nothing: the blocks the whole batch takes
+ * (a new block at each block boundary, a copy for each shared partly filled
+ * tail; a sequence may appear more than once) are counted first, and a
+ * failing call (PKV_ENOENT, PKV_EINVAL for a swapped-out sequence, PKV_ENOMEM)
+ * changes nothing.  *num_done (nullable) receives how many sequences were
+ * appended: n on success, 0 on failure. */
 int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_t *slots,
                          int32_t *cow_pairs, int32_t *num_cow, int32_t *cow_src,
                          int32_t *num_done);
+/* One decode step of the allocator in one call: pkv_seq_append_slots for the
+ * n sequences (all or nothing, as there), then their block tables and lengths
+ * as pkv_export_tables writes them -- the inputs of paged_decode_step
+ * (block_tables, seq_lens, cow_src) for a batch whose every sequence gains
+ * one token [fairy, s06 decode-phase allocation].  slots (host [n], nullable)
+ * receives the new tokens' slots, cow_src (host [n]) each sequence's copy
+ * source block or -1, out_block_tables (host [n][max_blocks_per_seq], padded
+ * with -1) and out_seq_lens (host [n]) the state after the appends.
+ * PKV_EINVAL, and no change, also when a table would outgrow
+ * max_blocks_per_seq. */
+int pkv_seq_step(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int32_t max_blocks_per_seq,
+                 int64_t *slots, int32_t *cow_src, int32_t *out_block_tables,
+                 int32_t *out_seq_lens);
 /* Make child share every block of parent (reference counts + 1). */
 int pkv_seq_fork(pkv_alloc *a, int64_t parent, int64_t child);
 /* Release a sequence; blocks whose count drops to zero go to the free-list tail

@@ -29,6 +29,7 @@ EXPORTS = [
     "pkv_strerror", "pkv_version",
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_num_free", "pkv_alloc_free_list",
     "pkv_block_refcount", "pkv_seq_allocate", "pkv_seq_append_slot", "pkv_seq_append_slots",
+    "pkv_seq_step",
     "pkv_seq_fork", "pkv_seq_free", "pkv_seq_len", "pkv_seq_slots", "pkv_export_tables",
     "pkv_export_shared_tables",
     "pkv_alloc_set_host_blocks", "pkv_alloc_num_free_host", "pkv_alloc_free_list_host",
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "pkv_seq_allocate": ([P, i64, i32, P, P], ctypes.c_int),
             "pkv_seq_append_slot": ([P, i64, P, P, P], ctypes.c_int),
             "pkv_seq_append_slots": ([P, P, i32, P, P, P, P, P], ctypes.c_int),
+            "pkv_seq_step": ([P, P, i32, i32, P, P, P, P], ctypes.c_int),
             "pkv_seq_fork": ([P, i64, i64], ctypes.c_int),
             "pkv_seq_free": ([P, i64], ctypes.c_int),
             "pkv_seq_len": ([P, i64, P], ctypes.c_int),
@@ -219,6 +221,23 @@ class BlockAllocator:
         if with_src:
             return slots[:n], pairs[:ncow.value], src[:n]
         return slots[:n], pairs[:ncow.value]
+
+    def step(self, seqs, max_blocks: int, out=None):
+        """One decode step: append a token to each sequence (all or nothing)
+        and export the tables, lengths, copy sources and slots of the batch.
+        `out` (optional) is a dict of preallocated host arrays (tables, lens,
+        cow_src, slots) that is filled and returned."""
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = len(ids)
+        if out is None:
+            out = {"tables": np.empty((max(n, 1), max_blocks), np.int32),
+                   "lens": np.empty(max(n, 1), np.int32),
+                   "cow_src": np.empty(max(n, 1), np.int32),
+                   "slots": np.empty(max(n, 1), np.int64)}
+        _check(lib().pkv_seq_step(self._h, _np_ptr(ids), n, max_blocks, _np_ptr(out["slots"]),
+                                  _np_ptr(out["cow_src"]), _np_ptr(out["tables"]),
+                                  _np_ptr(out["lens"])), "pkv_seq_step")
+        return out
 
     def fork(self, parent: int, child: int):
         _check(lib().pkv_seq_fork(self._h, parent, child), "pkv_seq_fork")

@@ -159,6 +159,48 @@ int grow(pkv_alloc *a, int64_t seq_id, int32_t n, bool create, int32_t *cow_src,
   return PKV_OK;
 }
 
+// The check that makes a batch of appends all or nothing: what the whole
+// batch takes is found before anything changes.  A sequence's append takes a
+// new block at a block boundary; its first append of the batch copies a
+// partly filled tail that is shared (counting the copies earlier sequences of
+// the batch made of the same block); after that its tail is its own.  Appends
+// only take blocks (a copied tail keeps another holder, and partly filled
+// blocks are never cached), so the batch succeeds exactly when the free list
+// plus the evictable cached blocks cover the total.  With max_blocks > 0 every
+// sequence's table must also still fit that width afterwards.
+int check_append_batch(const pkv_alloc *a, const int64_t *seq_ids, int32_t n,
+                       int32_t max_blocks) {
+  try {
+    int64_t need = 0;
+    std::unordered_map<int64_t, int32_t> seen;   // appends per sequence so far
+    std::unordered_map<int32_t, int32_t> moved;  // references copies have taken off a block
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = a->seqs.find(seq_ids[i]);
+      if (it == a->seqs.end()) return PKV_ENOENT;
+      if (it->second.on_host) return PKV_EINVAL;
+      int32_t &k = seen[seq_ids[i]];
+      const int64_t pos = (int64_t)it->second.len + k;
+      if (pos >= INT32_MAX) return PKV_EINVAL;
+      if (max_blocks > 0 && a->blocks_for((int32_t)pos + 1) > max_blocks) return PKV_EINVAL;
+      if (pos % a->block_size == 0) {
+        ++need;
+      } else if (k == 0) {
+        const int32_t tail = it->second.blocks.back();
+        int32_t &mv = moved[tail];
+        if (a->ref[tail] - mv > 1) {
+          ++need;
+          ++mv;
+        }
+      }
+      ++k;
+    }
+    if ((int64_t)a->count + (int64_t)a->lru.size() < need) return PKV_ENOMEM;
+  } catch (...) {
+    return PKV_ENOMEM;
+  }
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,11 +303,13 @@ int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_
   if (num_cow) *num_cow = 0;
   if (!a || n < 0 || (n > 0 && (!seq_ids || !slots || !cow_pairs || !num_cow)))
     return PKV_EINVAL;
+  const int chk = check_append_batch(a, seq_ids, n, 0);
+  if (chk != PKV_OK) return chk;
   int32_t ncow = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t src, dst;
     const int st = pkv_seq_append_slot(a, seq_ids[i], &slots[i], &src, &dst);
-    if (st != PKV_OK) return st;
+    if (st != PKV_OK) return st;   // not reached: the batch was checked above
     if (cow_src) cow_src[i] = src;
     if (src >= 0) {
       cow_pairs[2 * ncow] = src;
@@ -276,6 +320,24 @@ int pkv_seq_append_slots(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int64_
     if (num_done) *num_done = i + 1;
   }
   return PKV_OK;
+}
+
+int pkv_seq_step(pkv_alloc *a, const int64_t *seq_ids, int32_t n, int32_t max_blocks_per_seq,
+                 int64_t *slots, int32_t *cow_src, int32_t *out_block_tables,
+                 int32_t *out_seq_lens) {
+  if (!a || n < 0 || max_blocks_per_seq <= 0 ||
+      (n > 0 && (!seq_ids || !cow_src || !out_block_tables || !out_seq_lens)))
+    return PKV_EINVAL;
+  const int chk = check_append_batch(a, seq_ids, n, max_blocks_per_seq);
+  if (chk != PKV_OK) return chk;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t slot;
+    int32_t dst;
+    const int st = pkv_seq_append_slot(a, seq_ids[i], &slot, &cow_src[i], &dst);
+    if (st != PKV_OK) return st;   // not reached: the batch was checked above
+    if (slots) slots[i] = slot;
+  }
+  return pkv_export_tables(a, seq_ids, n, max_blocks_per_seq, out_block_tables, out_seq_lens);
 }
 
 int pkv_seq_fork(pkv_alloc *a, int64_t parent, int64_t child) {

@@ -143,3 +143,80 @@ def test_workload_scripts_give_identical_tables(make):
     st_, rows, lens = model.export(w.decode_seqs, w.max_blocks_per_seq)
     assert np.array_equal(t, np.asarray(rows, np.int32)) and l.tolist() == lens
     model.check_invariants()
+
+
+def _state(a, seqs, maxb=8):
+    t, l = a.export_tables(seqs, maxb)
+    return (list(a.free_list()), [a.refcount(b) for b in range(a.num_blocks)], t.tolist(),
+            l.tolist())
+
+
+def test_batched_append_is_all_or_nothing():
+    """A batch whose later appends find no block fails as a whole: nothing of
+    its earlier appends (blocks taken, copy-on-write swaps) stays."""
+    a = pkv.BlockAllocator(8, 16)
+    a.allocate(1, 15)
+    a.fork(1, 2)          # 1 and 2 share a partly filled tail: the first writer copies
+    a.allocate(3, 32)     # full: its next token takes a new block
+    a.allocate(4, 64)     # 4 blocks; 8 - 1 - 2 - 4 = 1 block free
+    before = _state(a, [1, 2, 3, 4])
+    # 1 copies its tail (the only free block), 3 would need another
+    with pytest.raises(pkv.PkvError) as e:
+        a.append_slots([1, 2, 3])
+    assert e.value.status == pkv.ENOMEM
+    assert _state(a, [1, 2, 3, 4]) == before
+    # unknown sequence late in the batch: nothing applied either
+    with pytest.raises(pkv.PkvError) as e:
+        a.append_slots([1, 99])
+    assert e.value.status == pkv.ENOENT
+    assert _state(a, [1, 2, 3, 4]) == before
+    # 1 copies, then 2 writes in place (the copy left it the only holder)
+    slots, pairs = a.append_slots([1, 2])
+    assert len(pairs) == 1 and a.num_free == 0
+
+
+def test_batched_append_counts_repeats_and_shared_tails():
+    a = pkv.BlockAllocator(6, 16)
+    a.allocate(1, 14)
+    a.fork(1, 2)
+    a.fork(1, 3)          # three holders of one tail block (5 blocks free)
+    # 1 copies, 2 copies (3 is then the last holder and writes in place), and
+    # 1's second and third appends reach position 16: a new block
+    slots, pairs = a.append_slots([1, 2, 3, 1, 1])
+    assert len(pairs) == 2 and a.num_free == 2
+    # exactly enough blocks: 2 needed (two boundaries), 2 free
+    a2 = pkv.BlockAllocator(4, 16)
+    a2.allocate(1, 16)
+    a2.allocate(2, 16)
+    a2.append_slots([1, 2])
+    assert a2.num_free == 0
+    before = _state(a2, [1, 2])
+    with pytest.raises(pkv.PkvError):
+        a2.append_slots([1] * 16 + [2] * 1)   # 1 fills its block, then needs one more
+    assert _state(a2, [1, 2]) == before
+
+
+def test_step_equals_append_then_export():
+    """pkv_seq_step gives the same slots, copy sources, tables and lengths as
+    append_slots followed by export_tables, over steps that cross block
+    boundaries and copy shared tails; it is all or nothing, also for a table
+    that would outgrow the requested width."""
+    a, b = pkv.BlockAllocator(64, 16), pkv.BlockAllocator(64, 16)
+    for x in (a, b):
+        x.allocate(1, 15)
+        x.fork(1, 2)
+        x.allocate(3, 30)
+        x.allocate(4, 1)
+    seqs = [1, 2, 3, 4]
+    for _ in range(40):
+        out = a.step(seqs, 8)
+        slots, pairs, src = b.append_slots(seqs, with_src=True)
+        t, l = b.export_tables(seqs, 8)
+        assert out["slots"].tolist() == slots.tolist()
+        assert out["cow_src"].tolist() == src.tolist()
+        assert np.array_equal(out["tables"], t) and out["lens"].tolist() == l.tolist()
+    before = _state(a, seqs)
+    with pytest.raises(pkv.PkvError) as e:     # seq 3 is at 70 tokens: 5 blocks > 4
+        a.step(seqs, 4)
+    assert e.value.status == pkv.EINVAL
+    assert _state(a, seqs) == before
