@@ -156,20 +156,58 @@ def cpu_baseline(w, budget_s: float = 10.0):
                                    f"in {el1:.1f} s"}}
 
 
-def read_ceiling(torch, pkv, nbytes: int = 2 << 30, reps: int = 10):
-    """Achievable streaming-read bandwidth (GB/s) of this device: the library's
-    plain read kernel over nbytes, best of a few grid sizes."""
+BENCH_KERNELS_SRC = os.path.join(ROOT, "bench_kernels.hip")
+BENCH_KERNELS_LIB = os.path.join(ROOT, "libpkv_bench.so")
+_bench_lib = None
+
+
+def build_bench_kernels() -> str:
+    """Compile the benchmark's bandwidth-diagnostic kernels (bench_kernels.hip,
+    not part of libpkv) into libpkv_bench.so beside this file."""
+    import subprocess
+    from paged_kv_cache_387_amd import build as B
+    tmp = BENCH_KERNELS_LIB + f".tmp{os.getpid()}"
+    subprocess.run([B.HIPCC, *B.HIP_FLAGS, "-shared", BENCH_KERNELS_SRC, "-o", tmp], check=True,
+                   capture_output=True)
+    os.replace(tmp, BENCH_KERNELS_LIB)
+    return BENCH_KERNELS_LIB
+
+
+def bench_lib():
+    global _bench_lib
+    if _bench_lib is None:
+        if not os.path.exists(BENCH_KERNELS_LIB):
+            raise ImportError(f"{BENCH_KERNELS_LIB} is not built (bench.build_bench_kernels)")
+        L = ctypes.CDLL(BENCH_KERNELS_LIB)
+        P, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        L.bench_stream_read.argtypes = [P, sz, P, i32, P]
+        L.bench_stream_copy.argtypes = [P, P, sz, i32, i32, P]
+        L.bench_stream_read.restype = L.bench_stream_copy.restype = ctypes.c_int
+        _bench_lib = L
+    return _bench_lib
+
+
+def _stream(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def read_ceiling(torch, nbytes: int = 2 << 30, reps: int = 10):
+    """Achievable streaming-read bandwidth (GB/s) of this device: a plain
+    non-temporal read over nbytes, the best of a sweep of grid sizes."""
+    L = bench_lib()
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     best = 0.0
-    for wgs in (2048, 8192, 32768):
+    for wgs in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536):
         sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
-        pkv.stream_read(buf, sink, wgs)
+        args = (ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs,
+                _stream(torch))
+        assert L.bench_stream_read(*args) == 0
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            pkv.stream_read(buf, sink, wgs)
+            L.bench_stream_read(*args)
         e1.record()
         torch.cuda.synchronize()
         best = max(best, nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
@@ -177,18 +215,21 @@ def read_ceiling(torch, pkv, nbytes: int = 2 << 30, reps: int = 10):
     return round(best, 1)
 
 
-def pmc_copy(nbytes: int = 1 << 30, reps: int = 5) -> int:
-    """Run the library's plain copy kernel on nbytes a few times: the known-size
-    reference for scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE)."""
+def pmc_copy(nbytes: int = 1 << 30, reps: int = 5, nontemporal: bool = True) -> int:
+    """Run a plain copy of nbytes a few times: the known-size reference for
+    scaling hardware byte counters (FETCH_SIZE / WRITE_SIZE).  Non-temporal
+    loads and stores by default, as the decode kernel reads K/V."""
     import torch
-    import paged_kv_cache_387_amd as pkv
+    L = bench_lib()
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(3)
     dst = torch.empty_like(src)
     for _ in range(reps):
-        pkv.stream_copy(dst, src, 4096)
+        assert L.bench_stream_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                   nbytes, 4096, int(nontemporal), _stream(torch)) == 0
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_copy_bytes": nbytes, "launches": reps}), flush=True)
+    print(json.dumps({"pmc_copy_bytes": nbytes, "launches": reps,
+                      "nontemporal": bool(nontemporal)}), flush=True)
     return 0
 
 
@@ -313,6 +354,34 @@ def summarize_trace(workload, trace_csv, stats_csv, commands):
         f"decode_{workload}_kernel_trace.txt"
     path = os.path.join(ROOT, "profiles", name)
     os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+    return 0
+
+
+def summarize_counters(name, csv_path, commands, kernels=("decode_kernel", "prefix32_kernel",
+                                                         "merge_kernel")):
+    """Write profiles/<name>_sq_counters.txt from a rocprofv3 --pmc counter CSV:
+    each library kernel's counters averaged over its dispatches."""
+    import csv
+    import collections
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        k = r["Kernel_Name"]
+        if any(x in k for x in kernels):
+            short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "")
+            short = short.split("(pkv::")[0]
+            agg[short][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = [f"# rocprofv3 counters per dispatch (averages), {name}",
+           "# commands (run from the repository root on the GPU host):"]
+    out += [f"#   {c}" for c in commands]
+    out.append(f"# source={decode_source_hash()}  (hash of the decode sources)")
+    for k, v in sorted(agg.items()):
+        n = max(len(x) for x in v.values())
+        out.append(f"{k}  ({n} dispatches)")
+        for c, vals in sorted(v.items()):
+            out.append(f"  {c:28s} {sum(vals) / len(vals):18.1f}")
+    path = os.path.join(ROOT, "profiles", f"{name}_sq_counters.txt")
     open(path, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
     return 0
@@ -838,6 +907,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
                     help="write profiles/decode_<workload>_kernel_trace.txt from rocprofv3 "
                          "kernel-trace CSVs (no GPU needed)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("NAME", "COUNTER_CSV"),
+                    help="write profiles/<NAME>_sq_counters.txt from a rocprofv3 --pmc CSV "
+                         "(no GPU needed)")
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize-*: command line that produced a CSV")
     args = ap.parse_args()
@@ -845,6 +917,8 @@ def main():
     workload = args.workload or "c2"
     if args.summarize_traffic:
         return summarize_traffic(workload, *args.summarize_traffic, args.command)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, args.command)
     if args.summarize_trace:
         wl = workload + ("_shared" if args.shared else "")
         return summarize_trace(wl, *args.summarize_trace, args.command)
@@ -855,7 +929,8 @@ def main():
 
     import torch
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import hip_replay as driver   # the test side's replay of workload scripts
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -882,7 +957,7 @@ def main():
               "dtype": res.pop("dtype"), "data": "synthetic", "config": res.pop("config")}
     result.update(res)
     result["cpu_baseline"] = None
-    result["hbm_read_ceiling_gbs"] = None if args.no_ceiling else read_ceiling(torch, pkv)
+    result["hbm_read_ceiling_gbs"] = None if args.no_ceiling else read_ceiling(torch)
     if default_run and not args.no_configs:
         configs, memos = {}, {}
         for name, kw in DEFAULT_CONFIGS:

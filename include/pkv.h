@@ -536,24 +536,6 @@ int paged_attention_prefill(void *out, int32_t out_dtype, const void *query, int
                             int32_t block_size, float scale, int32_t partition_size,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-/* ========================================================================
- * Bandwidth diagnostics (measurement helpers, not part of the method)
- *
- * A plain streaming read and a plain copy of `bytes` contiguous bytes with
- * 16-byte accesses over `workgroups` workgroups of 256 threads (grid-stride).
- * They measure the achievable HBM bandwidth next to the decode kernel's, and
- * give a copy of known size for scaling hardware byte counters.  src and dst
- * are device pointers, 16-byte aligned, bytes a multiple of 16; sink is a
- * device uint32 array of `workgroups` entries that the read writes only in
- * the astronomically unlikely case that the XOR of the data hits a fixed
- * value (it exists so the loads cannot be optimized away).  The buffers of a
- * copy must not overlap.  Asynchronous on `stream`.
- * ======================================================================== */
-int pkv_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups,
-                    void *stream);
-int pkv_stream_copy(void *dst, const void *src, size_t bytes, int32_t workgroups,
-                    void *stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,6 @@ EXPORTS = [
     "paged_attention_decode_noalloc", "paged_decode_step",
     "paged_attention_shared_workspace_bytes", "paged_attention_decode_shared",
     "paged_attention_prefill_workspace_bytes", "paged_attention_prefill",
-    "pkv_stream_read", "pkv_stream_copy",
 ]
 
 
@@ -129,8 +128,6 @@ def lib() -> ctypes.CDLL:
             "paged_attention_prefill": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32, P, P, i32,
                                          i32, i32, i32, i32, i32, i32, f32, i32, P, sz, P],
                                         ctypes.c_int),
-            "pkv_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
-            "pkv_stream_copy": ([P, P, sz, i32, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -833,25 +830,3 @@ def paged_attention_prefill(query, cache: PagedKVCache, block_tables, seq_lens, 
         cache.num_kv_heads, D, cache.block_size, float(scale), partition_size, ws_ptr, ws_len,
         _stream_ptr(stream)), "paged_attention_prefill")
     return out
-
-
-# ---------------------------------------------------------------------------
-# bandwidth diagnostics
-# ---------------------------------------------------------------------------
-
-def stream_read(src, sink, workgroups: int, stream=None):
-    """Plain streaming read of the bytes of `src` (measurement helper)."""
-    torch = _torch()
-    n = src.numel() * src.element_size()
-    _check(lib().pkv_stream_read(_dev(src, "src"), n,
-                                 _dev(sink, "sink", torch.int32, workgroups), workgroups,
-                                 _stream_ptr(stream)), "pkv_stream_read")
-
-
-def stream_copy(dst, src, workgroups: int, stream=None):
-    """Plain copy of the bytes of `src` into `dst` (measurement helper)."""
-    n = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < n:
-        raise ValueError("dst is smaller than src")
-    _check(lib().pkv_stream_copy(_dev(dst, "dst"), _dev(src, "src"), n, workgroups,
-                                 _stream_ptr(stream)), "pkv_stream_copy")

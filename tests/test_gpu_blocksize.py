@@ -64,7 +64,7 @@ DECODE = [(dt, D, H, Hkv) for dt, D, H, Hkv in
 @pytest.mark.parametrize("bs", BS)
 @pytest.mark.parametrize("dt,D,H,Hkv", DECODE)
 def test_decode_small(pkv, bs, dt, D, H, Hkv):
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = _ragged(dt, bs, D, H, Hkv)
     w.memo = {}
     say(f"decode {w.name}: S={w.num_seqs} H={H}/{Hkv} D={D} {dt} bs={bs}")
@@ -101,7 +101,7 @@ def _c5_e4m3():
 @pytest.mark.parametrize("bs", BS)
 @pytest.mark.parametrize("name", list(STEP))
 def test_fused_step(pkv, bs, name):
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = STEP[name](bs)
     w.memo = {}
     ro = oracle_replay(w)
@@ -125,7 +125,7 @@ def test_fused_step(pkv, bs, name):
     (32, lambda: workloads.c4_quantized("i8")),
 ])
 def test_full_size(pkv, bs, make):
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = workloads.with_block_size(make(), bs)
     w.memo = {}
     say(f"full size {w.name}: S={w.num_seqs} pool={w.num_blocks} bs={bs}")

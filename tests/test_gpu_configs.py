@@ -27,7 +27,7 @@ CONFIGS = ["c1", "c2", "c3", "c4_i8", "c4_e4m3", "c5", "c5_cow"]
 @pytest.mark.parametrize("name", CONFIGS)
 def test_config_full_size(name):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = workloads.CONFIGS[name]()
     w.memo = {}

@@ -45,7 +45,7 @@ def _batch(dt, src=None):
 
 def _lib():
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     return driver
 

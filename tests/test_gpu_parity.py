@@ -24,7 +24,7 @@ from gpu_helpers import check_close, check_pools_equal, say  # noqa: E402
 @pytest.fixture(scope="module")
 def pkv():
     import paged_kv_cache_387_amd as m
-    from paged_kv_cache_387_amd import driver  # noqa: F401
+    import hip_replay as driver  # noqa: F401
     assert torch.cuda.is_available()
     m.lib()
     return m
@@ -153,7 +153,7 @@ PARTS = [0, 16, 64, 128, 1 << 20]
 
 @pytest.mark.parametrize("name", list(DECODE_CASES))
 def test_decode_small(pkv, name):
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = DECODE_CASES[name]()
     w.memo = {}
     say(f"decode {name}: S={w.num_seqs} H={w.num_heads}/{w.num_kv_heads} D={w.head_dim} "
@@ -179,7 +179,7 @@ def test_decode_small(pkv, name):
 
 def test_decode_single_token_returns_v(pkv):
     """seq_len 1: the output is v_0 itself (weight exactly 1), after fp16 rounding."""
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = workloads.custom("one", [1, 1, 1], 16, 2, 128, "f16", seed=5)
     rg = driver.replay(w)
     out = driver.decode(rg, w)
@@ -192,7 +192,7 @@ def test_decode_single_token_returns_v(pkv):
 def test_decode_out_of_range_entries_stay_in_bounds(pkv):
     """Table entries outside the pool and lengths beyond the table are clamped or
     skipped (memory-safe); the other sequences of the batch are unaffected."""
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = workloads.custom("guard", [40, 40, 40], 16, 2, 128, "f16", seed=6)
     ro = oracle_replay(w)
     rg = driver.replay(w)
@@ -212,7 +212,7 @@ def test_decode_output_with_element_alignment_only(pkv, odt):
     """The ABI asks only for element alignment of `out`: an output view that
     starts one element into its buffer (not 8- or 16-byte aligned) gets the
     same values as an aligned one, single-pass and split."""
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     w = _ragged("f16", lens=(1, 16, 17, 100, 257, 700))()
     w.memo = {}
     ro = oracle_replay(w)

@@ -54,7 +54,7 @@ def _workload(name, lens=LENS, step=False):
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_runs(name):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = _workload(name)
     w.memo = {}
@@ -79,7 +79,7 @@ def test_fused_step_runs(name):
     """The fused step's write-behind token and copy-on-write with the tail tile
     in the last partition of a run."""
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = _workload(name, lens=(1025, 1607, 2075, 64, 65, 127, 531), step=True)
     w.memo = {}

@@ -60,7 +60,7 @@ CASES = {
 
 def _run(name, step, part, min_prefix=0):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = CASES[name]()
     if step and not any(op[0] == "step" for op in w.ops):
@@ -112,7 +112,7 @@ def test_shared_full_size(name):
     an 8192-token prefix), fused step, every output against the oracle."""
     import time
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = W.CONFIGS[name]()
     w.memo = {}

@@ -56,7 +56,7 @@ def _c5_quant(dt):
 @pytest.mark.parametrize("name", list(STEP_CASES))
 def test_fused_step_matches_oracle(name, part):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = STEP_CASES[name]()
     w.memo = {}

@@ -35,7 +35,7 @@ OFF = 1 << 24      # sequence-id offset of batch r (as the benchmark uses)
 
 def test_c2_fused_step_rotating_batches():
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     R, rounds = 8, 2
     ws = [W.c2_qwen3_32b_layer(seed_offset=r) for r in range(R)]
@@ -101,7 +101,7 @@ def test_c2_fused_step_rotating_batches():
 
 def _full_step(w, parts):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = W.with_decode_step(w)
     w.memo = {}

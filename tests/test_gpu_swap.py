@@ -23,7 +23,7 @@ def _block_view(t, num_blocks):
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_swap_round_trip(dtype, bs):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     w = W.forked_groups("swap", [(96, 3), (250, 4)], singles=[1, 17, 300], keep_parents=True,
                         cache_dtype=dtype)

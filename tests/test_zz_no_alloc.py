@@ -28,7 +28,7 @@ CALLS = [
 @pytest.mark.parametrize("dt", ["f16", "i8"])
 def test_noalloc_matches_decode_on_consecutive_calls(dt):
     import paged_kv_cache_387_amd as pkv
-    from paged_kv_cache_387_amd import driver
+    import hip_replay as driver
     pkv.lib()
     for name, lens, H, Hkv, _, part in CALLS:
         w = W.custom(f"noalloc_{name}_{dt}", lens, H, Hkv, 128, dt, seed=13,
