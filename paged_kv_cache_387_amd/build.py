@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-HIP_SOURCES = ["api.hip", "decode.hip", "decode_runs.hip", "prefix.hip", "cache_ops.hip"]
+HIP_SOURCES = ["api.hip", "decode.hip", "decode_runs.hip", "decode_stream.hip", "prefix.hip",
+               "cache_ops.hip"]
 CXX_SOURCES = ["allocator.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -70,55 +70,102 @@ int32_t choose_part_tiles(int32_t max_blocks, int32_t block_size, int32_t reques
   return pt >= mt ? (int32_t)mt : (int32_t)pt;
 }
 
-int32_t num_parts_of(int32_t max_blocks, int32_t block_size, int32_t part_tiles) {
-  const int64_t mt = max_tiles_of(max_blocks, block_size);
-  return odd_up((int32_t)((mt + part_tiles - 1) / part_tiles));
-}
+// The decode plan for a table width and partition request: how the kernel's
+// waves share the tiles (see decode_kernel.h) and the partition slots of the
+// workspace.
+//  * An automatic choice that splits the table, with no shared-prefix
+//    partials to merge: the stream walk, equal shares of the batch's tiles
+//    per wave, whatever the lengths.
+//  * Explicit partitions that are whole multiples of the wave count: the runs
+//    walk, one workgroup walking run_parts consecutive partitions of its
+//    unit, keeping its load ring primed across their boundaries and ending
+//    each in its own partial.  A run spans about as many tiles as an
+//    automatic partition would, so small explicit partitions keep the long
+//    per-workgroup walks that stream well; its finished partials wait in LDS
+//    (stage_floats) until its last load has been issued.
+//  * Otherwise one workgroup per partition (the split walk), which for a
+//    table of one partition is the single pass.
+// Stream grid.  Two workgroups that share a compute unit do not stream at
+// the same rate: the hardware favours the older one's waves, the younger
+// one's first tiles arrive late and it finishes last.  Where every share is
+// one long piece (few units), a grid of one workgroup per compute unit
+// (kWavesOneRound waves) finishes first; where shares hold the short pieces
+// of many units, a second workgroup per compute unit hides the start of each
+// piece and pays for itself.
+constexpr int64_t kWavesOneRound = 1024;   // 4 waves on each of 256 compute units
+constexpr int64_t kFewUnits = 256;
 
-// Runs of partitions.  A partition sets the granularity of the partial
-// results; a workgroup need not stop at its end.  When partitions are whole
-// multiples of the wave count, one workgroup walks `run_parts` consecutive
-// partitions of its unit, keeping its load ring primed across their
-// boundaries and emitting one partial per partition: a run spans about as
-// many tiles as an automatic partition would, so small explicit partitions
-// keep the long per-workgroup walks that stream well.  The run's finished
-// partials wait in LDS (stage_floats) until its last load has been issued.
-int32_t choose_run_parts(int32_t max_blocks, int32_t block_size, int32_t part_tiles,
-                         int32_t group, int32_t head_dim) {
-  if (part_tiles <= 0 || part_tiles % kDecodeWaves) return 1;
-  const int64_t mt = max_tiles_of(max_blocks, block_size);
-  const int64_t parts = (mt + part_tiles - 1) / part_tiles;
-  int64_t rp = choose_part_tiles(max_blocks, block_size, 0) / part_tiles;
-  const int64_t cap = 1 + stage_floats(head_dim) / ((int64_t)group * (head_dim + 4));
-  if (rp > cap) rp = cap;
-  if (rp > parts) rp = parts;
-  return rp < 1 ? 1 : (int32_t)rp;
-}
+struct DecodePlan {
+  int walk = kWalkSplit;
+  int32_t part_tiles = 0;      // tiles per partition (split and runs walks)
+  int32_t num_parts = 0;       // partition slots per (sequence, head) row
+  int32_t run_parts = 1;       // runs walk
+  int32_t num_runs = 0;        // workgroup slots per unit (split and runs walks)
+  int32_t stream_waves = 0;    // stream walk: waves the batch's tiles are dealt to
+};
 
-int32_t num_runs_of(int32_t max_blocks, int32_t block_size, int32_t part_tiles,
-                    int32_t run_parts) {
+DecodePlan plan_decode(int64_t num_units, int32_t max_blocks, int32_t block_size,
+                       int32_t requested, int32_t extra_parts, int32_t group,
+                       int32_t head_dim) {
+  DecodePlan pl;
   const int64_t mt = max_tiles_of(max_blocks, block_size);
-  const int64_t parts = (mt + part_tiles - 1) / part_tiles;
-  return odd_up((int32_t)((parts + run_parts - 1) / run_parts));
+  pl.part_tiles = choose_part_tiles(max_blocks, block_size, requested);
+  const int64_t parts = (mt + pl.part_tiles - 1) / pl.part_tiles;
+  pl.num_parts = odd_up((int32_t)parts);
+  if (requested == 0 && extra_parts == 0 && parts > 1) {
+    pl.walk = kWalkStream;
+    pl.stream_waves = num_units <= kFewUnits ? (int32_t)kWavesOneRound : kStreamWaves;
+    return pl;
+  }
+  if (pl.part_tiles % kDecodeWaves == 0 && parts > 1) {
+    int64_t rp = choose_part_tiles(max_blocks, block_size, 0) / pl.part_tiles;
+    const int64_t cap = 1 + stage_floats(head_dim) / ((int64_t)(group > 1 ? group : 1) * (head_dim + 4));
+    rp = rp < cap ? rp : cap;
+    rp = rp < parts ? rp : parts;
+    if (rp > 1) {
+      pl.walk = kWalkRuns;
+      pl.run_parts = (int32_t)rp;
+      pl.num_runs = odd_up((int32_t)((parts + rp - 1) / rp));
+      return pl;
+    }
+  }
+  pl.num_runs = pl.num_parts;
+  return pl;
 }
 
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace: [partial outputs][partial lse], each part 256-byte aligned.
+// Workspace: [partial outputs][partial lse][stream walk: unit records], each
+// part 256-byte aligned.
 struct WorkspaceLayout {
-  size_t o_off, lse_off, total;
+  size_t o_off, lse_off, info_off, total;
 };
 
-// A row of partials per (sequence, head): num_parts suffix (or whole-sequence)
-// partitions, then `extra` shared-prefix partitions.
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                 int32_t num_parts, int32_t extra = 0) {
-  WorkspaceLayout w{0, 0, 0};
+// Split and runs walks: a row of partials per (sequence, head), num_parts
+// suffix (or whole-sequence) partitions, then `extra` shared-prefix
+// partitions.  Stream walk: two partial slots per wave (a unit's first piece,
+// and a piece that began in an earlier share), each holding the rows of a
+// kv head's group of query heads, and per unit its first wave and piece count.
+WorkspaceLayout rows_layout(int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                            int32_t num_parts, int32_t extra = 0) {
+  WorkspaceLayout w{0, 0, 0, 0};
   if (num_parts <= 1 && extra == 0) return w;
-  const size_t rows = (size_t)num_seqs * num_heads * (num_parts + extra);
-  w.o_off = 0;
+  const size_t rows = (size_t)num_rows * num_heads * (num_parts + extra);
   w.lse_off = round256(rows * head_dim * sizeof(float));
   w.total = w.lse_off + rows * sizeof(float);
+  w.info_off = w.total;
+  return w;
+}
+
+WorkspaceLayout workspace_layout(const DecodePlan &pl, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t extra = 0) {
+  if (pl.walk != kWalkStream)
+    return rows_layout(num_seqs, num_heads, head_dim, pl.num_parts, extra);
+  WorkspaceLayout w{0, 0, 0, 0};
+  const size_t rows = (size_t)2 * kStreamWaves * (num_heads / num_kv_heads);
+  w.lse_off = round256(rows * head_dim * sizeof(float));
+  w.info_off = round256(w.lse_off + rows * sizeof(float));
+  w.total = w.info_off + (size_t)num_seqs * num_kv_heads * 2 * sizeof(int32_t);
   return w;
 }
 
@@ -237,9 +284,10 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
       max_blocks_per_seq <= 0 || !valid_block_size(block_size) ||
       !valid_partition(partition_size, block_size))
     return 0;
-  const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
-  const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
-  return workspace_layout(num_seqs, num_heads, head_dim, parts).total;
+  const DecodePlan pl = plan_decode((int64_t)num_seqs * num_kv_heads, max_blocks_per_seq,
+                                    block_size, partition_size, 0, num_heads / num_kv_heads,
+                                    head_dim);
+  return workspace_layout(pl, num_seqs, num_heads, num_kv_heads, head_dim).total;
 }
 
 size_t paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens,
@@ -255,7 +303,7 @@ size_t paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_que
   const PrefillPlan pl = plan_prefill(num_seqs, num_heads, num_kv_heads, max_query_len,
                                       max_blocks_per_seq, block_size, partition_size);
   if (pl.num_pparts <= 1) return 0;
-  return workspace_layout(num_query_tokens, num_heads, head_dim, pl.num_pparts).total;
+  return rows_layout(num_query_tokens, num_heads, head_dim, pl.num_pparts).total;
 }
 
 size_t paged_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads,
@@ -267,10 +315,12 @@ size_t paged_attention_shared_workspace_bytes(int32_t num_seqs, int32_t num_head
       num_heads % num_kv_heads || max_blocks_per_seq <= 0 || !valid_block_size(block_size) ||
       !valid_partition(partition_size, block_size) || !valid_groups(groups, block_size))
     return 0;
-  const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
-  const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
-  const PrefixPlan pl = plan_prefix(groups, num_heads, num_kv_heads, block_size);
-  return workspace_layout(num_seqs, num_heads, head_dim, parts, pl.num_pparts).total;
+  const PrefixPlan pre = plan_prefix(groups, num_heads, num_kv_heads, block_size);
+  const DecodePlan pl = plan_decode((int64_t)num_seqs * num_kv_heads, max_blocks_per_seq,
+                                    block_size, partition_size, pre.num_pparts,
+                                    num_heads / num_kv_heads, head_dim);
+  return workspace_layout(pl, num_seqs, num_heads, num_kv_heads, head_dim, pre.num_pparts)
+      .total;
 }
 
 }  // extern "C"
@@ -311,12 +361,17 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   if (is_quant(cache_dtype) && (!aligned(k_scale, 8) || !aligned(v_scale, 8)))
     return PKV_EINVAL;
 
-  const int32_t pt = choose_part_tiles(max_blocks_per_seq, block_size, partition_size);
-  const int32_t parts = num_parts_of(max_blocks_per_seq, block_size, pt);
-  if ((int64_t)num_seqs * num_heads > INT32_MAX || (int64_t)num_seqs * num_kv_heads > INT32_MAX ||
-      decode_grid(num_seqs * num_kv_heads, parts) > INT32_MAX)
+  const DecodePlan pl = plan_decode((int64_t)num_seqs * num_kv_heads, max_blocks_per_seq,
+                                    block_size, partition_size, extra_parts,
+                                    num_heads / num_kv_heads, head_dim);
+  const int32_t pt = pl.part_tiles;
+  const int32_t parts = pl.num_parts;
+  if ((int64_t)num_seqs * num_heads > INT32_MAX ||
+      (int64_t)num_seqs * num_kv_heads * 2 > INT32_MAX ||
+      (pl.walk != kWalkStream && decode_grid(num_seqs * num_kv_heads, pl.num_runs) > INT32_MAX))
     return PKV_ENOTSUP;
-  const WorkspaceLayout wl = workspace_layout(num_seqs, num_heads, head_dim, parts, extra_parts);
+  const WorkspaceLayout wl =
+      workspace_layout(pl, num_seqs, num_heads, num_kv_heads, head_dim, extra_parts);
   const size_t need = wl.total;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PKV_EINVAL;
@@ -335,6 +390,8 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   char *ws = static_cast<char *>(workspace);
   p.ws_o = need ? reinterpret_cast<float *>(ws + wl.o_off) : nullptr;
   p.ws_lse = need ? reinterpret_cast<float *>(ws + wl.lse_off) : nullptr;
+  p.ws_info = need && pl.walk == kWalkStream ? reinterpret_cast<int32_t *>(ws + wl.info_off)
+                                             : nullptr;
   p.num_blocks = num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.num_seqs = num_seqs;
@@ -344,10 +401,16 @@ int prepare_decode(DecodeParams *pp, void *out, int32_t out_dtype, const void *q
   p.block_size = block_size;
   p.part_tiles = pt;
   p.num_parts = parts;
-  p.run_parts = choose_run_parts(max_blocks_per_seq, block_size, pt, num_heads / num_kv_heads,
-                                 head_dim);
-  p.num_runs = num_runs_of(max_blocks_per_seq, block_size, pt, p.run_parts);
-  p.ws_stride = parts + extra_parts;
+  p.walk = pl.walk;
+  p.run_parts = pl.run_parts;
+  p.num_runs = pl.num_runs;
+  p.stream_waves = pl.stream_waves;
+  p.min_share = kStreamMinShare;
+  // stream walk: a unit's piece count is known on the device only; the merge
+  // sizes its partial groups for about one piece per 64 tiles of the table
+  p.ws_stride = pl.walk == kWalkStream
+                    ? (int32_t)((max_tiles_of(max_blocks_per_seq, block_size) + 63) / 64 + 2)
+                    : parts + extra_parts;
   p.ws_pre = parts;
   p.num_units = num_seqs * num_kv_heads;
   p.qk_scale = scale * 1.4426950408889634f;
@@ -616,7 +679,7 @@ int paged_attention_prefill(void *out, int32_t out_dtype, const void *query, int
     return PKV_ENOTSUP;
   WorkspaceLayout wl{0, 0, 0};
   if (pl.num_pparts > 1) {
-    wl = workspace_layout(num_query_tokens, num_heads, head_dim, pl.num_pparts);
+    wl = rows_layout(num_query_tokens, num_heads, head_dim, pl.num_pparts);
     if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return PKV_EINVAL;
   }
   const int dev = check_device();

@@ -1,15 +1,17 @@
 // PagedAttention decode for gfx950 (CDNA4): launches, and the log-sum-exp
 // merge of split sequences.  The decode kernel itself (decode_kernel.h) is
-// built here for workgroups that each walk one partition; the variant whose
-// workgroups walk runs of several partitions is built in decode_runs.hip.
+// built here for the split walk (a workgroup per partition); the runs and
+// stream walks are built in decode_runs.hip and decode_stream.hip.
 #include "decode_kernel.h"
 
 namespace pkv {
 namespace {
 
 // Log-sum-exp merge of the partials of sequences that used more than one
-// partition (and of a sequence's suffix partials with its shared-prefix
-// partials).  A thread owns 4 output elements of one (sequence, head) row and
+// partition or stream piece (and of a sequence's suffix partials with its
+// shared-prefix partials).  After the stream walk it also writes the zero rows
+// of empty sequences, which no wave visits.  A thread owns 4 output elements
+// of one (sequence, head) row and
 // folds the partials q = qg, qg + QG, ... into a running (max, sum, weighted
 // sum) -- one pass, no separate maximum; the QG groups of a row are then
 // combined through LDS.  A workgroup of kMergeThreads holds 256 / (D/4 * QG)
@@ -30,29 +32,45 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const int dv = t % TPH;
   const int row = blockIdx.x * RPW + rl;           // s * H + h
   const bool live_row = row < p.num_seqs * p.num_heads;
-  int np = 0, npre = 0;
+  const bool stream = p.walk == kWalkStream;
+  int np = 0, npre = 0, fw = 0, hh = 0;
+  bool zero_row = false;
   if (live_row) {
     const int s = row / p.num_heads;
     int L = p.seq_lens[s];
-    L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
-    const int ntile = (L + kTile - 1) / kTile;
-    np = (ntile + p.part_tiles - 1) / p.part_tiles;
-    npre = prefix_parts_of(p, s);
+    if (stream) {
+      // a unit's pieces: slots 2 * fw + 1 (its first piece), then 2 * (fw + j);
+      // the record is read with the length (it is stale for an empty sequence)
+      const int h = row - s * p.num_heads;
+      hh = h % p.group;
+      const int u = s * p.num_kv_heads + h / p.group;
+      fw = p.ws_info[2 * u];
+      np = p.ws_info[2 * u + 1];
+      zero_row = L <= 0;
+      if (zero_row || fw < 0 || fw >= p.stream_waves) np = 0;
+      np = np < p.stream_waves - fw ? np : p.stream_waves - fw;
+    } else {
+      L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
+      const int ntile = (L + kTile - 1) / kTile;
+      np = (ntile + p.part_tiles - 1) / p.part_tiles;
+      npre = prefix_parts_of(p, s);
+    }
   }
-  // rows with one partition and no prefix were written by the decode kernel
-  const bool merge = live_row && (np > 1 || npre > 0);
-  const int nq = np + npre;
+  // rows with one partition (or piece) and no prefix were written by the
+  // decode kernel
+  const bool merge = live_row && (np > 1 || npre > 0 || zero_row);
+  const int nq = zero_row ? 0 : np + npre;
   float m = -INFINITY, z = 0.0f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   if (merge) {
     const size_t base = (size_t)row * p.ws_stride;
-    const float *lse = p.ws_lse + base;
-    const f4 *o = reinterpret_cast<const f4 *>(p.ws_o + base * D) + dv;
+    const f4 *o = reinterpret_cast<const f4 *>(p.ws_o) + dv;
 #pragma unroll 4
     for (int q = qg; q < nq; q += QG) {
-      const int sq = q < np ? q : p.ws_pre + (q - np);
-      const float lq = lse[sq];
-      const f4 oq = o[(size_t)sq * (D / 4)];
+      const size_t fi = stream ? (size_t)(2 * (fw + q) + (q == 0 ? 1 : 0)) * p.group + hh
+                               : base + (q < np ? q : p.ws_pre + (q - np));
+      const float lq = p.ws_lse[fi];
+      const f4 oq = o[fi * (D / 4)];
       const float mn = fmaxf(m, lq);
       const float a = exp2f(m - mn), b = exp2f(lq - mn);
       acc = acc * a + oq * b;
@@ -80,7 +98,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
     }
   }
   if (!merge) return;
-  const f4 r = acc * (1.0f / z);
+  const f4 r = zero_row ? f4{0.f, 0.f, 0.f, 0.f} : acc * (1.0f / z);
   const size_t oi = (size_t)row * D + 4 * dv;
   // out needs only element alignment; vector stores when it allows them
   if ((reinterpret_cast<uintptr_t>(p.out) & (OUT == PKV_F32 ? 15u : 7u)) == 0) {
@@ -125,16 +143,19 @@ hipError_t launch_merge_d(const DecodeParams &p, hipStream_t stream) {
 template <int KV, int D, int OUT, int SRC, int BS>
 hipError_t launch_typed(const DecodeParams &p, hipStream_t stream) {
   hipError_t err;
-  if (p.run_parts > 1) {
+  if (p.walk == kWalkRuns) {
     err = launch_decode_runs(p, KV, SRC >= 0, OUT, D, stream);
+  } else if (p.walk == kWalkStream) {
+    err = launch_decode_stream(p, KV, SRC >= 0, OUT, D, stream);
   } else {
     const int64_t grid = decode_grid(p.num_units, p.num_runs);
-    hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS, kWalkSplit>), dim3((unsigned)grid),
                        dim3(64 * kDecodeWaves), 0, stream, p);
     err = hipGetLastError();
   }
   // with shared prefixes the caller launches the merge after the prefix pass
-  if (err != hipSuccess || p.num_parts <= 1 || p.seq_group) return err;
+  if (err != hipSuccess || p.seq_group) return err;
+  if (p.walk != kWalkStream && p.num_parts <= 1) return err;
   return launch_merge_d<D, OUT>(p, stream);
 }
 

@@ -5,16 +5,29 @@
 // t < seq_len, with K/V reached through the block table (logical block t/16 ->
 // physical block; "KV Cache and PagedAttention (vllm-musa)", 7yue.com,
 // section 5; "KVcache-learning", fairy2021.github.io, s01 and s05).  Long
-// sequences are split into partitions whose partial results are merged with a
+// sequences are split into pieces whose partial results are merged with a
 // log-sum-exp reduction ("partial accumulate, then merge" of paged_attention_v2,
 // "vLLM PagedAttention deep dive", jsqmd.com, section 4.1).
 //
-// Work decomposition.  One workgroup = 4 wavefronts handles one (run of
-// partitions, kv head, sequence); a run is one partition, or several
-// consecutive ones when their size is a multiple of 4 tiles (each still ends
-// in its own partial).  Wave w takes blocks first+w, first+w+4, ... of the
-// run.  For one 16-token block a wave computes
-//   S^T[t][h] = K[t] . q[h]      one 16x16 MFMA tile: rows = the block's 16
+// Work decomposition: a unit is one (sequence, kv head); a workgroup is 4
+// wavefronts.  Three walks share the per-tile code below:
+//  * kWalkSplit: one workgroup per (unit, partition).  Wave w takes tiles
+//    first+w, first+w+4, ... of the partition; at the end the four wave states
+//    are combined through LDS into the output row (or the partition's partial).
+//  * kWalkRuns: one workgroup per (unit, run of consecutive partitions whose
+//    size is a multiple of 4 tiles): the waves interleave the run's tiles as
+//    in the split walk, every wave ends each partition at the same step, and
+//    the four states of a finished partition are combined through LDS into
+//    its partial, which waits in LDS until the run's last load is issued.
+//  * kWalkStream: the batch's tiles, in (sequence, kv head, tile) order, are
+//    dealt to the grid's waves in equal shares of whole blocks (each
+//    workgroup first scans seq_lens for the share boundaries).  A wave walks
+//    the pieces of the units its share covers, tile by tile, ending each piece
+//    itself: a unit wholly inside one share is written directly, the other
+//    pieces leave partials for the merge.  Every wave streams the same number
+//    of bytes however ragged the lengths are.
+// For one 16-token tile a wave computes
+//   S^T[t][h] = K[t] . q[h]      one 16x16 MFMA tile: rows = the tile's 16
 //                                 tokens, columns = the G <= 16 query heads of
 //                                 the GQA group (columns >= G have q = 0)
 //   online softmax per column (running max m, partial sum l, fp32, base 2)
@@ -59,10 +72,30 @@ namespace {
 #ifndef PKV_PREFETCH_Q8
 #define PKV_PREFETCH_Q8 4
 #endif
-template <int KV> struct Prefetch { static constexpr int NB = PKV_PREFETCH_F16; };
-template <> struct Prefetch<PKV_F32> { static constexpr int NB = PKV_PREFETCH_F32; };
-template <> struct Prefetch<PKV_I8> { static constexpr int NB = PKV_PREFETCH_Q8; };
-template <> struct Prefetch<PKV_E4M3> { static constexpr int NB = PKV_PREFETCH_Q8; };
+// Workgroups per compute unit the register budget is sized for (one wave per
+// SIMD each, so also waves per SIMD).
+#ifndef PKV_OCCUPANCY_F16
+#define PKV_OCCUPANCY_F16 2
+#endif
+#ifndef PKV_OCCUPANCY_Q8
+#define PKV_OCCUPANCY_Q8 2
+#endif
+template <int KV> struct Prefetch {
+  static constexpr int NB = PKV_PREFETCH_F16;
+  static constexpr int OCC = PKV_OCCUPANCY_F16;
+};
+template <> struct Prefetch<PKV_F32> {
+  static constexpr int NB = PKV_PREFETCH_F32;
+  static constexpr int OCC = 2;
+};
+template <> struct Prefetch<PKV_I8> {
+  static constexpr int NB = PKV_PREFETCH_Q8;
+  static constexpr int OCC = PKV_OCCUPANCY_Q8;
+};
+template <> struct Prefetch<PKV_E4M3> {
+  static constexpr int NB = PKV_PREFETCH_Q8;
+  static constexpr int OCC = PKV_OCCUPANCY_Q8;
+};
 
 // Four consecutive output elements (idx a multiple of 4).
 template <int OUT>
@@ -74,15 +107,44 @@ __device__ __forceinline__ void store_out4(void *out, size_t idx, f4 v) {
         h4{to_f16_out(v[0]), to_f16_out(v[1]), to_f16_out(v[2]), to_f16_out(v[3])};
 }
 
-// RUNS: the workgroup may walk several partitions (DecodeParams::run_parts >
-// 1); without it run_parts is taken as 1 and the walk carries no partition
-// ends.  SRC < 0: decode only.  SRC = PKV_F16 / PKV_F32: fused decode step, the new
-// token's K/V (of that type) is written first (see DecodeParams).  BS = block
-// size (8, 16 or 32 tokens).  The kernel works on 16-token tiles (the MFMA
-// row count): a 32-token block is two tiles stored one after the other, a
-// 16-token tile spans two 8-token blocks.
-template <int KV, int D, int OUT, int SRC, int BS, bool RUNS>
-__global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_kernel(DecodeParams p) {
+// Issue priority by progress.  Waves of the two workgroups that share a
+// compute unit compete for instruction issue, and the hardware favours the
+// older wave: without a hint the first workgroup on each unit streams at
+// nearly full speed while the second waits for its leftovers, and the kernel
+// ends with the second alone.  A wave lowers its priority as it works through
+// its tiles (3 for the first quarter, 0 for the last), so the one that is
+// behind wins.
+#ifndef PKV_WAVE_PRIO
+#define PKV_WAVE_PRIO 0
+#endif
+struct PrioSteps {
+  int q1, q2, q3;   // steps at which the priority drops
+  __device__ __forceinline__ explicit PrioSteps(int total)
+      : q1(total / 4), q2(total / 2), q3(total - total / 4) {}
+  __device__ __forceinline__ void at(int k) const {
+    if constexpr (PKV_WAVE_PRIO) {
+      if (k == q1) __builtin_amdgcn_s_setprio(2);
+      else if (k == q2) __builtin_amdgcn_s_setprio(1);
+      else if (k == q3) __builtin_amdgcn_s_setprio(0);
+    }
+  }
+};
+
+// 64-bit lane shift (the stream walk's scan of sequence lengths).
+__device__ __forceinline__ int64_t shfl_up64(int64_t x, int d) {
+  const int lo = __shfl_up((int)(uint32_t)x, d, 64);
+  const int hi = __shfl_up((int)(x >> 32), d, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// WALK: kWalkSplit, kWalkRuns or kWalkStream (see above).  SRC < 0: decode
+// only.  SRC = PKV_F16 / PKV_F32: fused decode step, the new token's K/V (of
+// that type) is written first (see DecodeParams).  BS = block size (8, 16 or
+// 32 tokens).  The kernel works on 16-token tiles (the MFMA row count): a
+// 32-token block is two tiles stored one after the other, a 16-token tile
+// spans two 8-token blocks.
+template <int KV, int D, int OUT, int SRC, int BS, int WALK>
+__global__ __launch_bounds__(64 * kDecodeWaves, Prefetch<KV>::OCC) void decode_kernel(DecodeParams p) {
   constexpr int EB = Kv<KV>::EB;
   constexpr bool QUANT = (KV == PKV_I8 || KV == PKV_E4M3);
   constexpr int SLICE = BS * D * EB;          // bytes of one (block, kv head) slice
@@ -94,55 +156,236 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   constexpr int E = 4 / EB;                   // head_dim elements per V word
   constexpr int LDS_ROW = D + 4;
   constexpr int NB = Prefetch<KV>::NB;
+  constexpr bool WAVE = WALK == kWalkStream;  // waves walk and end their pieces alone
+  constexpr int TS = WAVE ? 1 : kDecodeWaves; // tile stride of a wave's walk
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(WALK == kWalkSplit || WALK == kWalkRuns || WALK == kWalkStream, "walk");
 
-  __shared__ __attribute__((aligned(16))) float lds_o[kDecodeWaves][kMaxGroup][LDS_ROW];
-  __shared__ float lds_m[kDecodeWaves][kMaxGroup];
-  __shared__ float lds_l[kDecodeWaves][kMaxGroup];
-  // finished partials of the run's earlier partitions: [partition][head][D + 4]
-  // (the output row, then its log-sum-exp)
-  __shared__ __attribute__((aligned(16))) float lds_stage[RUNS ? stage_floats(D) : 1];
+  // the split and runs walks' combine of the four wave states (a token size
+  // otherwise), and the runs walk's finished partials of the run's earlier
+  // partitions: [partition][head][D + 4] (the output row, then its
+  // log-sum-exp)
+  __shared__ __attribute__((aligned(16)))
+      float lds_o[WAVE ? 1 : kDecodeWaves][WAVE ? 1 : kMaxGroup][WAVE ? 4 : LDS_ROW];
+  __shared__ float lds_m[WAVE ? 1 : kDecodeWaves][WAVE ? 1 : kMaxGroup];
+  __shared__ float lds_l[WAVE ? 1 : kDecodeWaves][WAVE ? 1 : kMaxGroup];
+  __shared__ __attribute__((aligned(16))) float lds_stage[WALK == kWalkRuns ? stage_floats(D) : 1];
+  // the fused step's staged new token (stored K, V rows and scales): one area
+  // per wave in the stream walk, where each wave may hold a tail tile
+  constexpr int NEWB = SRC >= 0 ? D * EB : 16;
+  constexpr int NEWW = WALK == kWalkStream ? kDecodeWaves : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_new_all[NEWW][2][NEWB];
+  __shared__ uint16_t lds_new_sc_all[NEWW][2];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int r = lane & 15;
   const int g = lane >> 4;
-
-  // Workgroup -> (unit, run of partitions).  Workgroups are dealt to the dies round
-  // robin, so unit u runs on die u % kXcds (with 8 kv heads: one kv head per
-  // die, whose L2 then serves the blocks that sequences share).  Ids go
-  // partition-major: workgroups resident together work on the same region of
-  // their sequences, so a shared prefix is read while it is still cached.
-  // The unit-group count is odd (unit_groups), so the runs of one unit land
-  // on different compute units.
   const int bid = blockIdx.x;
-  const int die_slot = bid / kXcds;
-  const int ugroups = unit_groups(p.num_units);
-  const int run = die_slot / ugroups;
-  const int u = (die_slot % ugroups) * kXcds + bid % kXcds;
-  if (u >= p.num_units) return;
-  const int s = u / p.num_kv_heads;
-  const int kvh = u - s * p.num_kv_heads;
   const int G = p.group;
   const int H = p.num_heads;
-  // A run of several partitions needs partitions of whole wave rounds (every
-  // wave then ends each partition but the last at the same step) and room
-  // for its staged partials; the host only sets up such runs.
-  const int rp = RUNS ? p.run_parts : 1;      // partitions of the run
-  if (RUNS && (rp < 1 || p.part_tiles % kDecodeWaves != 0 ||
-               (rp - 1) * G * (D + 4) > stage_floats(D)))
-    return;
+  const int Hkv = p.num_kv_heads;
+  const int cap_tokens = p.max_blocks * BS;
+  uint8_t (*lds_new)[NEWB] = lds_new_all[WALK == kWalkStream ? w : 0];
+  uint16_t *lds_new_sc = lds_new_sc_all[WALK == kWalkStream ? w : 0];
+  // Tiles one unit of a sequence of `len` tokens spans in the stream walk's
+  // order: whole blocks (a 32-token block counts two tiles even when only its
+  // first holds tokens), so that every share boundary is a block boundary.
+  auto span_of = [&](int len) {
+    len = len < 0 ? 0 : (len > cap_tokens ? cap_tokens : len);
+    return TPB > 1 ? (len + BS - 1) / BS * TPB : (len + kTile - 1) / kTile;
+  };
 
-  const int part0 = run * rp;                 // first partition of the run
-  const int first = part0 * p.part_tiles;     // first tile of the run
+  // ---- the stream walk: where this wave's share starts ----
+  // Each workgroup scans the spans of all sequences (thread t sums a
+  // contiguous slice; wave scans, then the four wave totals), derives the
+  // share (the same in every workgroup) and finds the sequence that holds the
+  // first tile of each of its four waves.
+  int64_t sg = 0, sg_end = 0;   // this wave's share [sg, sg_end) of the batch's tiles
+  int64_t sc = 0;               // tiles (per kv head) of the sequences before ss
+  int64_t share = 1;
+  int ss = 0, sspan = 0;        // the sequence holding tile sg, and its span
+  int wave_id = 0;
+  if constexpr (WALK == kWalkStream) {
+    __shared__ int64_t lds_tot[kDecodeWaves];
+    __shared__ int64_t lds_c[kDecodeWaves];
+    __shared__ int lds_s[kDecodeWaves];
+    const int S = p.num_seqs;
+    constexpr int NT = 64 * kDecodeWaves;
+    const int per = (S + NT - 1) / NT;
+    const int s_lo = min(S, (int)threadIdx.x * per), s_hi = min(S, s_lo + per);
+    int64_t mine = 0;
+    for (int s = s_lo; s < s_hi; ++s) mine += span_of(p.seq_lens[s]);
+    int64_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t v = shfl_up64(inc, o);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) lds_tot[w] = inc;
+    if (threadIdx.x < kDecodeWaves) lds_s[threadIdx.x] = -1;
+    __syncthreads();
+    int64_t before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kDecodeWaves; ++i) {
+      const int64_t t = lds_tot[i];
+      before += i < w ? t : 0;
+      total += t;
+    }
+    const int64_t T = total * Hkv;   // tiles of the batch
+    int64_t nw = (T + p.min_share - 1) / p.min_share;
+    nw = nw < p.stream_waves ? nw : p.stream_waves;
+    nw = nw < 1 ? 1 : nw;
+    share = (T + nw - 1) / nw;
+    share = (share + TPB - 1) / TPB * TPB;
+    share = share < 1 ? 1 : share;
+    int64_t c = before + inc - mine;   // spans of the sequences before s_lo
+    const int64_t g0 = (int64_t)bid * kDecodeWaves * share;
+    for (int s = s_lo; s < s_hi; ++s) {
+      const int sp = span_of(p.seq_lens[s]);
+#pragma unroll
+      for (int i = 0; i < kDecodeWaves; ++i) {
+        const int64_t gs = g0 + i * share;
+        if (Hkv * c <= gs && gs < Hkv * (c + sp)) {
+          lds_s[i] = s;
+          lds_c[i] = c;
+        }
+      }
+      c += sp;
+    }
+    __syncthreads();
+    wave_id = bid * kDecodeWaves + w;
+    sg = g0 + w * share;
+    sg_end = sg + share < T ? sg + share : T;
+    ss = __builtin_amdgcn_readfirstlane(lds_s[w]);
+    if (ss < 0) return;                   // a share beyond the batch: nothing to do
+    sc = lds_c[w];
+    sspan = span_of(p.seq_lens[ss]);
+  }
+
+  // out needs only element alignment; vector stores when it allows them
+  const bool out_vec =
+      (reinterpret_cast<uintptr_t>(p.out) & (OUT == PKV_F32 ? 15u : 7u)) == 0;
+
+  // ---- wave walks: finished outputs wait in LDS for the wave's last load ----
+  // A wave's loads and stores complete in order, so a store issued among the
+  // walk's loads makes the next wait for a tile a wait for the store as
+  // well.  A wave's outputs other than its last (a partition of a run, a
+  // piece of a share) therefore go to its LDS slots (KST of them; a full set
+  // is stored on the spot) and are stored after its last load.  Lane (r, g)
+  // stages its NACC quads of head r (see emit) in quad-major order, each quad
+  // of the 64 lanes one contiguous 1 KiB.
+  constexpr int KST = 2;
+  __shared__ __attribute__((aligned(16)))
+      f4 lds_st[WAVE ? kDecodeWaves : 1][WAVE ? KST : 1][WAVE ? NACC : 1][WAVE ? 64 : 1];
+  __shared__ float lds_st_lse[WAVE ? kDecodeWaves : 1][WAVE ? KST : 1][kMaxGroup];
+  struct Staged {
+    size_t base;        // direct: element offset of the unit's head-0 row in `out`;
+                        // partial: row of head 0
+    size_t rstride;     // partial: rows between consecutive heads
+    int direct;         // rows of `out` (else partial rows of the workspace)
+    int info_u;         // stream walk: the unit whose record to store (-1: none)
+    int info_fw, info_n;
+  };
+  __shared__ Staged lds_st_dst[WAVE ? kDecodeWaves : 1][WAVE ? KST : 1];   // where each goes
+  int nst = 0;
+  // Stores one output (quads q[c] of lane (r, g), head r's log-sum-exp lse)
+  // where `d` says; lanes r >= G hold no head.
+  auto store_output = [&](const Staged &d, const f4 *q, float lse) __attribute__((always_inline)) {
+    if (r < G) {
+#pragma unroll
+      for (int c = 0; c < NACC; ++c) {
+        const int i = c / E, j = c % E;
+        const int d0 = E * (16 * i + 4 * g) + 4 * j;
+        if (d.direct) {
+          const size_t idx = d.base + (size_t)r * D + d0;
+          if (out_vec) {
+            store_out4<OUT>(p.out, idx, q[c]);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) store_out<OUT>(p.out, idx + k, q[c][k]);
+          }
+        } else {
+          *reinterpret_cast<f4 *>(p.ws_o + (d.base + r * d.rstride) * D + d0) = q[c];
+        }
+      }
+      if (!d.direct && g == 0) p.ws_lse[d.base + r * d.rstride] = lse;
+    }
+    if (d.info_u >= 0 && lane == 0) {
+      p.ws_info[2 * d.info_u] = d.info_fw;
+      p.ws_info[2 * d.info_u + 1] = d.info_n;
+    }
+  };
+  auto flush_staged = [&]() __attribute__((always_inline)) {
+    if constexpr (WAVE) {
+      for (int k = 0; k < nst; ++k) {
+        f4 q[NACC];
+#pragma unroll
+        for (int c = 0; c < NACC; ++c) q[c] = lds_st[w][k][c][lane];
+        const Staged d = lds_st_dst[w][k];
+        store_output(d, q, lds_st_lse[w][k][r]);
+      }
+      nst = 0;
+    }
+  };
+
+  // ---- one pass per piece of a unit (a stream share may hold several) ----
+  for (;;) {
+  int s, kvh;
+  int first, last;        // the tiles [first, last) of the workgroup (split) or wave
+  int part0 = 0;          // split / runs: first partition of the workgroup
+  int piece_end = 0;      // stream: the piece's end in span tiles
+  bool piece_head = true, piece_tail = true;   // stream: the piece starts / ends its unit
+  if constexpr (WALK == kWalkStream) {
+    if (sg >= sg_end || ss >= p.num_seqs) {
+      flush_staged();
+      break;
+    }
+    const int64_t off = sg - Hkv * sc;
+    kvh = (int)(off / sspan);
+    const int a = (int)(off - (int64_t)kvh * sspan);
+    const int64_t rem = sg_end - sg;
+    piece_end = rem < sspan - a ? a + (int)rem : sspan;
+    s = ss;
+    first = a;
+    last = piece_end;
+    piece_head = a == 0;
+    piece_tail = piece_end == sspan;
+  } else {
+    // Workgroup -> (unit, partition or run).  Workgroups are dealt to the dies
+    // round robin, so unit u runs on die u % kXcds (with 8 kv heads: one kv
+    // head per die, whose L2 then serves the blocks that sequences share).
+    // Ids go partition-major: workgroups resident together work on the same
+    // region of their sequences, so a shared prefix is read while it is still
+    // cached.  The unit-group count is odd (unit_groups), so the partitions
+    // of one unit land on different compute units.
+    const int die_slot = bid / kXcds;
+    const int ugroups = unit_groups(p.num_units);
+    const int run = die_slot / ugroups;
+    const int u = (die_slot % ugroups) * kXcds + bid % kXcds;
+    if (u >= p.num_units) return;
+    s = u / Hkv;
+    kvh = u - s * Hkv;
+    // A run of several partitions needs partitions of whole wave rounds (every
+    // wave then ends each partition but the last at the same step) and room
+    // for its staged partials; the host only sets up such runs.
+    const int rp = WALK == kWalkRuns ? p.run_parts : 1;
+    if (WALK == kWalkRuns && (rp < 1 || p.part_tiles % kDecodeWaves != 0 ||
+                              (rp - 1) * G * (D + 4) > stage_floats(D)))
+      return;
+    part0 = run * rp;
+    first = part0 * p.part_tiles;
+    last = 0;   // set once the length is known
+  }
   const int32_t *trow = p.block_tables + (size_t)s * p.max_blocks;
+  // the wave's first tile
+  int wfirst = WAVE ? first : first + w;
 
-  // Table entries of this wave's tiles first + w + j * kDecodeWaves, 64 at a time,
-  // one per lane (readlane picks entry j): the tile's block (the first of its
-  // two blocks when SPLIT; tvb holds the second).  Entries are clamped to
-  // `lim` blocks.
+  // Table entries of this wave's walk steps c0 + lane (one per lane; readlane
+  // picks entry j): the tile's block (the first of its two blocks when SPLIT;
+  // tvb holds the second).  Entries are clamped to `lim` blocks.
   auto load_tv = [&](int c0, int lim, int *tvb) {
-    const int tile = first + w + (c0 + lane) * kDecodeWaves;
+    const int tile = wfirst + (c0 + lane) * TS;
     int e = SPLIT ? 2 * tile : tile / TPB;
     e = e < lim ? e : lim - 1;
     if constexpr (SPLIT) {
@@ -152,11 +395,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     return trow[e];
   };
 
-  // Loads that do not depend on the sequence length go first, so that they
-  // overlap with the read of seq_lens: the table entries of the wave's first
-  // 64 tiles (clamped to the row) and the q fragment (B operand of the q.K
-  // MFMAs, column r = head kvh*G+r; columns r >= G repeat head kvh*G and
-  // their results are never stored).
+  // The piece's first loads are all issued before any is waited for, the
+  // ones needed first first (a wave's loads complete in order, so waiting for
+  // one leaves the later ones in flight; the empty asm statements keep the
+  // compiler from reordering them): the sequence length and, in the fused
+  // step, the copy source (read without a branch: any readable word stands in
+  // for a null cow_src); then the table entries of the wave's first 64 tiles
+  // (clamped to the row), the q fragment (B operand of the q.K MFMAs, column
+  // r = head kvh*G+r; columns r >= G repeat head kvh*G and their results are
+  // never stored) and, in the fused step, the unit's new token (every wave
+  // loads it, only the one with the tail tile uses it: the same loads on
+  // every path keep the waits exact).
+  const int L_raw = p.seq_lens[s];
+  int cow_raw = -1;
+  if constexpr (SRC >= 0) cow_raw = *(p.cow_src ? p.cow_src + s : p.seq_lens + s);
+  asm volatile("" ::: "memory");
   int tvb_next = 0;
   int tv_next = load_tv(0, p.max_blocks, &tvb_next);
   const size_t qrow = ((size_t)s * H + kvh * G + (r < G ? r : 0)) * D;
@@ -180,36 +433,55 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     }
   }
 
-  int cow_req = -1;   // fused step: the block to copy into the tail block, if any
-  if constexpr (SRC >= 0) cow_req = p.cow_src ? p.cow_src[s] : -1;
-  int L = p.seq_lens[s];
-  L = L < 0 ? 0 : (L > p.max_blocks * BS ? p.max_blocks * BS : L);
+  TokenRaw<SRC >= 0 ? SRC : PKV_F16, D> new_raw;
+  if constexpr (SRC >= 0) {
+    constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
+    const size_t row = ((size_t)s * Hkv + kvh) * D * esz;
+    load_token_raw<SRC, D>(static_cast<const uint8_t *>(p.key_new) + row,
+                           static_cast<const uint8_t *>(p.value_new) + row, new_raw, lane);
+  }
+  asm volatile("" ::: "memory");
+
+  // fused step: the block to copy into the tail block, if any
+  const int cow_req = SRC >= 0 && p.cow_src ? cow_raw : -1;
+  int L = L_raw;
+  L = L < 0 ? 0 : (L > cap_tokens ? cap_tokens : L);
   const int nblk = (L + BS - 1) / BS;                 // blocks in use
   const int ntile = (L + kTile - 1) / kTile;          // tiles in use
-  const int nparts_s = (ntile + p.part_tiles - 1) / p.part_tiles;
+  const int nparts_s = WALK == kWalkStream ? 1 : (ntile + p.part_tiles - 1) / p.part_tiles;
   const int npre = prefix_parts_of(p, s);   // shared-prefix partials (merged later)
-  if (first >= ntile) {
-    if (run == 0 && npre == 0) {  // empty sequence: zero output rows
-      for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves)
-        store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
+  if constexpr (WALK == kWalkStream) {
+    last = last < ntile ? last : ntile;       // a block's second tile past the length
+  } else {
+    if (first >= ntile) {
+      if (first == 0 && npre == 0) {  // empty sequence: zero output rows
+        for (int e = threadIdx.x; e < G * D; e += 64 * kDecodeWaves)
+          store_out<OUT>(p.out, ((size_t)s * H + kvh * G + e / D) * D + e % D, 0.0f);
+      }
+      return;
     }
-    return;
+    const int rp = WALK == kWalkRuns ? p.run_parts : 1;
+    last = min(first + rp * p.part_tiles, ntile);
   }
-  const int last = min(first + rp * p.part_tiles, ntile);
-
-  // Tiles of this wave: first + w + k * kDecodeWaves, k < nt_w.
-  const int nt_part = last - first;
-  const int nt_w = nt_part > w ? (nt_part - w + kDecodeWaves - 1) / kDecodeWaves : 0;
-  // Partitions of the run.  Every one but the last is full, and with
-  // part_tiles a multiple of the wave count each wave walks exactly
+  // The wave's tiles: wfirst + k * TS, k < nt_w.
+  int nt_w;
+  if constexpr (WAVE) {
+    nt_w = last - first;
+  } else {
+    const int nt_part = last - first;
+    nt_w = nt_part > w ? (nt_part - w + kDecodeWaves - 1) / kDecodeWaves : 0;
+  }
+  // Runs: the partitions of the run.  Every one but the last is full, and
+  // with part_tiles a multiple of the wave count each wave walks exactly
   // tpw = part_tiles / kDecodeWaves of its tiles: partition j of the run ends
   // for every wave after its step (j + 1) * tpw - 1.
-  const int nparts_run = RUNS ? (nt_part + p.part_tiles - 1) / p.part_tiles : 1;
+  const int nparts_run = WALK == kWalkRuns ? (last - first + p.part_tiles - 1) / p.part_tiles : 1;
   const int tpw = p.part_tiles / kDecodeWaves;
+  const int wlast = WAVE ? wfirst + nt_w : last;   // end of the wave's tiles (wave walks)
 
   // ---- fused step: the new token, written behind ----
-  // The partition that holds a sequence's tail tile also stores the new token
-  // at position L - 1, after giving the tail block the contents of block
+  // The piece that holds a sequence's tail tile also stores the new token at
+  // position L - 1, after giving the tail block the contents of block
   // cow_src[s] when that names another block.  Nothing waits for these stores:
   //  * the tail block's tiles are read from the copy source, whose bytes the
   //    copy reproduces;
@@ -221,43 +493,51 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   //    token's own stores meet they write equal bytes and their order does
   //    not matter.  (Stores issued among the walk's loads would make every
   //    later wait for a load a wait for all memory operations.)
-  // Other sequences may read the copy source concurrently; nothing else
-  // writes these bytes.
+  // Pieces and partitions are whole blocks, so the tail block lies within the
+  // piece of its tail tile.  Other sequences may read the copy source
+  // concurrently; nothing else writes these bytes.
   const int tail_tile = ntile - 1;
   const int tail_blk = nblk - 1;
   const int new_row = (L - 1) % kTile;   // row of the new token in the tail tile
   const int new_slot = (L - 1) % BS;     // its slot in the tail block
   // The first loads of K/V depend on nothing here but cow_src[s] (read with
-  // seq_lens): the tail block's own table entry is read after they are issued.
-  const bool tail_here = SRC >= 0 && tail_tile >= first && tail_tile < last;
+  // seq_lens); the tail block's own table entry is taken from the table
+  // entries of the chunk of steps that holds the tail tile, and the new
+  // token's bits, loaded with the piece's first loads, are first used after
+  // the ring's loads are issued.
+  const bool tail_here = SRC >= 0 && tail_tile >= (WAVE ? wfirst : first) &&
+                         tail_tile < (WAVE ? wlast : last);
   const int cow_from = tail_here && (unsigned)cow_req < (unsigned)p.num_blocks ? cow_req : -1;
-  const bool step_wave = tail_here && w == (tail_tile - first) % kDecodeWaves;
+  const bool step_wave = tail_here && (WAVE || w == (tail_tile - first) % kDecodeWaves);
   bool tail_ok = false;                  // the tail block's table entry is in the pool
   int tail_phys = 0;
   size_t tail_slice = 0, tail_sc = 0;
-  constexpr int NEWB = SRC >= 0 ? D * EB : 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_new[2][NEWB];   // stored K, V rows
-  __shared__ uint16_t lds_new_sc[2];
-  float new_x[2][D / 64];
-  if constexpr (SRC >= 0) {
-    if (step_wave) {
-      constexpr size_t esz = SRC == PKV_F32 ? 4 : 2;
-      const size_t row = ((size_t)s * p.num_kv_heads + kvh) * D * esz;
-      load_token<SRC, D>(static_cast<const uint8_t *>(p.key_new) + row,
-                         static_cast<const uint8_t *>(p.value_new) + row, new_x, lane);
-    }
-  }
-  // Right after the wave's first loads: encode the new token and keep its
-  // row-order bytes in LDS.  (A tail entry outside the pool writes nothing;
-  // its tile is skipped.)
-  auto step_write = [&]() {
+  // The tail tile's step in the wave's walk: its chunk (c0) and entry j in it.
+  const int tail_step = step_wave ? (tail_tile - wfirst) / TS : -1;
+  const int tail_c0 = tail_step >= 0 ? tail_step / 64 * 64 : -1;
+  // At the start of the tail tile's chunk, right after the ring's first loads:
+  // encode the new token and keep its row-order bytes in LDS.  The tail
+  // block's entry is lane j of the chunk's entries (tvb: the second block of
+  // a SPLIT tile).  (A tail entry outside the pool writes nothing; its tile
+  // is skipped.)
+  auto step_write = [&](int tv, int tvb, int j) {
     if constexpr (SRC >= 0) {
       constexpr int PER = D / 64;
-      tail_phys = trow[tail_blk];
+      tail_phys = SPLIT && tail_blk == 2 * tail_tile + 1 ? __builtin_amdgcn_readlane(tvb, j)
+                                                          : __builtin_amdgcn_readlane(tv, j);
       tail_ok = (unsigned)tail_phys < (unsigned)p.num_blocks;
       if (!tail_ok) return;
-      tail_slice = ((size_t)tail_phys * p.num_kv_heads + kvh) * SLICE;
-      tail_sc = ((size_t)tail_phys * p.num_kv_heads + kvh) * BS;
+      tail_slice = ((size_t)tail_phys * Hkv + kvh) * SLICE;
+      tail_sc = ((size_t)tail_phys * Hkv + kvh) * BS;
+      // first use of the token's bits: here, not hoisted above the ring's
+      // loads (which would wait for the token and then issue the ring)
+      TokenRaw<SRC, D> raw = new_raw;
+#pragma unroll
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int k = 0; k < TokenRaw<SRC, D>::RW; ++k) asm volatile("" : "+v"(raw.w[which][k]));
+      float new_x[2][D / 64];
+      token_from_raw<SRC, D>(raw, new_x);
       const TokenCodes<D> tc = encode_token<KV, D>(new_x);
 #pragma unroll
       for (int which = 0; which < 2; ++which)
@@ -302,7 +582,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     if constexpr (SRC >= 0) {
       // copy the slice 16 bytes at a time; chunks that hold bytes of slot
       // new_slot take them from the staged row
-      const size_t sslice = ((size_t)cow_from * p.num_kv_heads + kvh) * SLICE;
+      const size_t sslice = ((size_t)cow_from * Hkv + kvh) * SLICE;
       constexpr int CHUNKS = SLICE / 16;
       constexpr int TILE_CH = TB * D * EB / 16;   // chunks per stored tile
       constexpr int ROUND = 4;                    // chunks per lane in flight
@@ -349,7 +629,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
         }
       }
       if constexpr (QUANT) {
-        const size_t ssc = ((size_t)cow_from * p.num_kv_heads + kvh) * BS;
+        const size_t ssc = ((size_t)cow_from * Hkv + kvh) * BS;
         if (lane < BS) {
           const uint16_t ksc = lane == new_slot ? lds_new_sc[0] : p.k_scale_w[ssc + lane];
           const uint16_t vsc = lane == new_slot ? lds_new_sc[1] : p.v_scale_w[ssc + lane];
@@ -371,7 +651,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   float vlim = kFoldMax / kVBoost0;    // largest V scale it admits (weights <= 1)
 
   const size_t kv_head_off = (size_t)kvh * SLICE;
-  const size_t block_stride = (size_t)p.num_kv_heads * SLICE;
+  const size_t block_stride = (size_t)Hkv * SLICE;
 
   struct Tile {
     u4 k[NL];
@@ -419,7 +699,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
         t.v[i] = load16_stream(vb + (size_t)((16 * i + r) * TB + tv0) * 4);
     }
     if constexpr (QUANT) {
-      const size_t so = ((size_t)pv * p.num_kv_heads + kvh) * BS + tq * kTile + tv0;
+      const size_t so = ((size_t)pv * Hkv + kvh) * BS + tq * kTile + tv0;
       t.ks = *reinterpret_cast<const u2 *>(p.k_scale + so);
       t.vs = *reinterpret_cast<const u2 *>(p.v_scale + so);
     }
@@ -596,21 +876,73 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     }
   };
 
-  // ---- ends of partitions ----
-  // The waves' states go to LDS (the barrier waits for LDS only: loads and
-  // the fused step's stores may be in flight), and combine() merges the four
-  // of element (head hh, dim d) into the normalized output and its base-2
-  // log-sum-exp (M + log2 den).
-  auto publish = [&]() __attribute__((always_inline)) {
+  // The accumulators as true sums of weight times value: the int8 bias taken
+  // out and the wave's V-scale boost undone (a power of two: exact).
+  auto unbias = [&]() __attribute__((always_inline)) {
     if constexpr (KV == PKV_I8) {
 #pragma unroll
       for (int a = 0; a < NACC; ++a) acc[a] -= kI8Bias * accp;
     }
-    if constexpr (QUANT) {   // undo the wave's V-scale boost (a power of two: exact)
+    if constexpr (QUANT) {
       const float ib = 1.0f / vboost;
 #pragma unroll
       for (int a = 0; a < NACC; ++a) acc[a] *= ib;
     }
+  };
+
+  // ---- wave walks: a wave ends its piece (or partition) alone ----
+  // Lane (r, g) holds head r's elements E*(16i + 4g + v) + e in acc[E*i + e][v]:
+  // for each i the 4E consecutive elements from E*(16i + 4g), the E quads
+  // c = E*i + j (j < E).  The normalized row goes to `out` (direct) or, with
+  // its base-2 log-sum-exp m + log2(l), to partial row row0 + r * rstride of
+  // the workspace: at once for the wave's last output, else through an LDS
+  // slot.  Then the state restarts.
+  auto emit = [&](bool direct, size_t row0, size_t rstride, bool last_out, int info_u, int info_fw,
+                  int info_n) __attribute__((always_inline)) {
+    unbias();
+    float lt = l + xor16(l);
+    lt += xor32(lt);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    f4 q[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC / E; ++i) {
+      float vals[4 * E];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < E; ++e) vals[v * E + e] = acc[E * i + e][v] * inv;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        q[E * i + j] = f4{vals[4 * j], vals[4 * j + 1], vals[4 * j + 2], vals[4 * j + 3]};
+    }
+    const float lse = m + log2f(lt);
+    const Staged d{direct ? ((size_t)s * H + kvh * G) * D : row0, rstride, direct ? 1 : 0, info_u,
+                   info_fw, info_n};
+    if (last_out) {
+      store_output(d, q, lse);
+    } else {
+      if (nst == KST) flush_staged();
+#pragma unroll
+      for (int c = 0; c < NACC; ++c) lds_st[w][nst][c][lane] = q[c];
+      if (g == 0) lds_st_lse[w][nst][r] = lse;
+      if (lane == 0) lds_st_dst[w][nst] = d;
+      ++nst;
+    }
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[a] = f4{0.f, 0.f, 0.f, 0.f};
+    accp = f4{0.f, 0.f, 0.f, 0.f};
+    vboost = kVBoost0;
+    vlim = kFoldMax / kVBoost0;
+  };
+  // ---- split and runs walks: the four wave states through LDS ----
+  // The waves' states go to LDS (the barrier waits for LDS only: loads and
+  // the fused step's stores may be in flight), and combine() merges the four
+  // of element quad (head hh, dims d0..d0+3) into the normalized output and
+  // its base-2 log-sum-exp (M + log2 den).
+  auto publish = [&]() __attribute__((always_inline)) {
+    unbias();
     float lt = l + xor16(l);
     lt += xor32(lt);
     if (g == 0) {
@@ -627,7 +959,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  // Elements d0 .. d0+3 of head hh (one LDS row read per wave).
   auto combine = [&](int hh, int d0, f4 &o, float &M, float &den) __attribute__((always_inline)) {
     M = lds_m[0][hh];
 #pragma unroll
@@ -642,14 +973,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     }
     o = num / den;
   };
-  // A partition of the run other than its last ends: its partial goes to
+  // Runs: a partition other than the run's last ends.  Its partial goes to
   // lds_stage (thread t keeps element quads t, t + 64 * kDecodeWaves, ... and
   // stores them itself after the walk), and the state restarts.  All waves
   // reach this at the same step; the second barrier frees lds_o for the next.
-  int flush_at = nparts_run > 1 ? tpw - 1 : -1;   // step that ends partition `staged`
-  int staged = 0;
-  auto end_partition = [&](int k) __attribute__((always_inline)) {
-    if constexpr (!RUNS) return;
+  int flush_at = WALK == kWalkRuns && nparts_run > 1 ? tpw - 1 : -1;   // step that ends
+  int staged = 0;                                                      // partition `staged`
+  auto end_step = [&](int k) __attribute__((always_inline)) {
+    if constexpr (WALK != kWalkRuns) return;
     if (__builtin_expect(k != flush_at, 1)) return;
     publish();
     for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
@@ -671,6 +1002,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     flush_at = staged < nparts_run - 1 ? flush_at + tpw : -1;
   };
 
+  const PrioSteps prio(nt_w);
+  if constexpr (PKV_WAVE_PRIO) __builtin_amdgcn_s_setprio(3);
   // ---- tile loop: a ring of NB tiles, each refilled right after use ----
   // The wave's tiles are walked in chunks of up to 64 (one table entry per
   // lane).  Within a chunk the steady-state rounds issue every load
@@ -680,36 +1013,41 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
   for (int c0 = 0; c0 < nt_w; c0 += 64) {
     const int nc = min(64, nt_w - c0);
     const int tv = tv_next, tvb = tvb_next;
-    const int t0 = first + w + c0 * kDecodeWaves;   // tile of chunk entry 0
+    const int t0 = wfirst + c0 * TS;   // tile of chunk entry 0
     Tile ring[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int jj = j < nc ? j : nc - 1;
-      issue(tv, tvb, jj, t0 + jj * kDecodeWaves, ring[j]);
+      issue(tv, tvb, jj, t0 + jj * TS, ring[j]);
     }
-    if (c0 == 0 && step_wave) step_write();   // the ring's loads are in flight
+    if (c0 == tail_c0) step_write(tv, tvb, tail_step - c0);   // the ring's loads are in flight
     int k0 = 0;
     for (; k0 + 2 * NB <= nc; k0 += NB) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        consume(t0 + (k0 + j) * kDecodeWaves, ring[j]);
-        issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kDecodeWaves, ring[j]);
-        end_partition(c0 + k0 + j);
+        consume(t0 + (k0 + j) * TS, ring[j]);
+        issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * TS, ring[j]);
+        end_step(c0 + k0 + j);
+        prio.at(c0 + k0 + j);
       }
     }
     // last round: the ring holds entries k0 .. k0+NB-1 (those < nc), at most
     // NB - 1 further entries remain to be loaded
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (k0 + j < nc) consume(t0 + (k0 + j) * kDecodeWaves, ring[j]);
-      if (k0 + j + NB < nc) issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * kDecodeWaves, ring[j]);
-      if (k0 + j < nc) end_partition(c0 + k0 + j);
+      if (k0 + j < nc) consume(t0 + (k0 + j) * TS, ring[j]);
+      if (k0 + j + NB < nc) issue(tv, tvb, k0 + j + NB, t0 + (k0 + j + NB) * TS, ring[j]);
+      if (k0 + j < nc) {
+        end_step(c0 + k0 + j);
+        prio.at(c0 + k0 + j);
+      }
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (k0 + NB + j < nc) {
-        consume(t0 + (k0 + NB + j) * kDecodeWaves, ring[j]);
-        end_partition(c0 + k0 + NB + j);
+        consume(t0 + (k0 + NB + j) * TS, ring[j]);
+        end_step(c0 + k0 + NB + j);
+        prio.at(c0 + k0 + NB + j);
       }
     }
     if (c0 + 64 < nt_w) tv_next = load_tv(c0 + 64, p.max_blocks, &tvb_next);
@@ -720,45 +1058,69 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void decode_ke
     if (cow_from >= 0 && cow_from != tail_phys) cow_copy();
   }
 
-  // ---- the run's last partition: combine the waves through LDS ----
-  publish();
-  const bool direct = nparts_s == 1 && npre == 0;
-  const int part = part0 + nparts_run - 1;
-  // out needs only element alignment; vector stores when it allows them
-  const bool out_vec =
-      (reinterpret_cast<uintptr_t>(p.out) & (OUT == PKV_F32 ? 15u : 7u)) == 0;
-  for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
-    const int hh = 4 * qd / D, d0 = 4 * qd % D;
-    f4 o;
-    float M, den;
-    combine(hh, d0, o, M, den);
-    const int h = kvh * G + hh;
-    if (direct) {
-      const size_t idx = ((size_t)s * H + h) * D + d0;
-      if (out_vec) {
-        store_out4<OUT>(p.out, idx, o);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_out<OUT>(p.out, idx + i, o[i]);
-      }
-    } else {
-      const size_t row = ((size_t)s * H + h) * p.ws_stride + part;
-      *reinterpret_cast<f4 *>(p.ws_o + row * D + d0) = o;
-      if (d0 == 0) p.ws_lse[row] = M + log2f(den);
+  if constexpr (WALK == kWalkStream) {
+    // The piece's output: direct when it is the whole unit, else a partial in
+    // slot 2 * wave + 1 (a unit's first piece, which continues in the next
+    // share) or 2 * wave (a piece that began in an earlier share).  The first
+    // piece also records the unit's first wave and piece count for the merge.
+    const int u = s * Hkv + kvh;
+    const bool direct = piece_head && piece_tail;
+    const int slot = 2 * wave_id + (piece_head ? 1 : 0);
+    const int64_t last_wave = (sg + sspan - 1) / share;   // sg: the unit's first tile
+    const bool last_out = sg + (piece_end - first) >= sg_end;
+    emit(direct, (size_t)slot * G, 1, last_out, piece_head ? u : -1, wave_id,
+         (int)(last_wave - wave_id + 1));
+    // past the piece; after a sequence's last kv head, on to the next
+    // sequence that has tiles
+    sg += piece_end - first;
+    if (piece_tail && kvh == Hkv - 1) {
+      do {
+        sc += sspan;
+        ++ss;
+        sspan = ss < p.num_seqs ? span_of(p.seq_lens[ss]) : 1;
+      } while (sspan == 0);
     }
-  }
-  // the staged partials of the run's earlier partitions (each thread stores
-  // the elements it staged)
-  if constexpr (RUNS)
-  for (int j = 0; j < nparts_run - 1; ++j) {
+    continue;
+  } else {
+    // ---- the run's last partition (the split walk's only one) ----
+    publish();
+    const bool direct = nparts_s == 1 && npre == 0;
+    const int part = part0 + nparts_run - 1;
     for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
       const int hh = 4 * qd / D, d0 = 4 * qd % D;
-      const float *src = lds_stage + (j * G + hh) * (D + 4);
-      const size_t row = ((size_t)s * H + kvh * G + hh) * p.ws_stride + part0 + j;
-      *reinterpret_cast<f4 *>(p.ws_o + row * D + d0) = *reinterpret_cast<const f4 *>(src + d0);
-      if (d0 == 0) p.ws_lse[row] = src[D];
+      f4 o;
+      float M, den;
+      combine(hh, d0, o, M, den);
+      const int h = kvh * G + hh;
+      if (direct) {
+        const size_t idx = ((size_t)s * H + h) * D + d0;
+        if (out_vec) {
+          store_out4<OUT>(p.out, idx, o);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) store_out<OUT>(p.out, idx + i, o[i]);
+        }
+      } else {
+        const size_t row = ((size_t)s * H + h) * p.ws_stride + part;
+        *reinterpret_cast<f4 *>(p.ws_o + row * D + d0) = o;
+        if (d0 == 0) p.ws_lse[row] = M + log2f(den);
+      }
     }
+    // the staged partials of the run's earlier partitions (each thread stores
+    // the elements it staged)
+    if constexpr (WALK == kWalkRuns)
+    for (int j = 0; j < nparts_run - 1; ++j) {
+      for (int qd = threadIdx.x; qd < G * D / 4; qd += 64 * kDecodeWaves) {
+        const int hh = 4 * qd / D, d0 = 4 * qd % D;
+        const float *src = lds_stage + (j * G + hh) * (D + 4);
+        const size_t row = ((size_t)s * H + kvh * G + hh) * p.ws_stride + part0 + j;
+        *reinterpret_cast<f4 *>(p.ws_o + row * D + d0) = *reinterpret_cast<const f4 *>(src + d0);
+        if (d0 == 0) p.ws_lse[row] = src[D];
+      }
+    }
+    return;
   }
+  }   // pieces
 }
 
 }  // namespace

@@ -1,8 +1,8 @@
 // PagedAttention decode for gfx950: the kernel of decode_kernel.h built for
-// workgroups that walk runs of several consecutive partitions
-// (DecodeParams::run_parts > 1), each partition still ending in its own
-// partial.  It has a translation unit of its own so that the one-partition
-// kernels in decode.hip carry none of the partition-end code.
+// the runs walk (a workgroup walks a run of consecutive partitions, each
+// ending in its own partial).  A translation unit of its own keeps the
+// builds in parallel and the one-partition kernels in decode.hip free of the
+// partition-end code.
 #include "decode_kernel.h"
 
 namespace pkv {
@@ -11,7 +11,7 @@ namespace {
 template <int KV, int D, int OUT, int SRC, int BS>
 hipError_t runs_typed(const DecodeParams &p, hipStream_t stream) {
   const int64_t grid = decode_grid(p.num_units, p.num_runs);
-  hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS, true>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((decode_kernel<KV, D, OUT, SRC, BS, kWalkRuns>), dim3((unsigned)grid),
                      dim3(64 * kDecodeWaves), 0, stream, p);
   return hipGetLastError();
 }

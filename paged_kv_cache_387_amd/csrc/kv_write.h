@@ -76,24 +76,62 @@ template <int D> struct TokenCodes {
   uint16_t sc[2];          // [K, V] fp16 scale bits (quantized caches)
 };
 
+// Loads the bits of lane l's elements of the source rows k_row / v_row (D
+// elements of SRC type) as they are stored: RW 32-bit words per row (fp16
+// pairs share a word; a single fp16 sits in the low half).  Nothing is done
+// to them until token_from_raw, so the loads stay in flight until then.
+template <int SRC, int D> struct TokenRaw {
+  static constexpr int PER = D / 64;
+  static constexpr int RW = SRC == PKV_F32 ? PER : (PER + 1) / 2;
+  uint32_t w[2][RW];
+};
+
+template <int SRC, int D>
+__device__ __forceinline__ void load_token_raw(const void *k_row, const void *v_row,
+                                               TokenRaw<SRC, D> &raw, int lane) {
+  constexpr int PER = D / 64;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint8_t *src = static_cast<const uint8_t *>(which ? v_row : k_row);
+    if constexpr (SRC == PKV_F32) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        raw.w[which][k] = reinterpret_cast<const uint32_t *>(src)[lane * PER + k];
+    } else if constexpr (PER == 1) {
+      raw.w[which][0] = reinterpret_cast<const uint16_t *>(src)[lane];
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER / 2; ++k)
+        raw.w[which][k] = reinterpret_cast<const uint32_t *>(src)[lane * (PER / 2) + k];
+    }
+  }
+}
+
+template <int SRC, int D>
+__device__ __forceinline__ void token_from_raw(const TokenRaw<SRC, D> &raw,
+                                               float (&xs)[2][D / 64]) {
+  constexpr int PER = D / 64;
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if constexpr (SRC == PKV_F32) {
+        xs[which][k] = __uint_as_float(raw.w[which][k]);
+      } else {
+        const uint32_t h = (raw.w[which][k / 2] >> (16 * (k % 2))) & 0xFFFFu;
+        xs[which][k] = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+      }
+    }
+}
+
 // Loads lane l's elements of the source rows k_row / v_row (D elements of
 // SRC type) as fp32.
 template <int SRC, int D>
 __device__ __forceinline__ void load_token(const void *k_row, const void *v_row,
                                            float (&xs)[2][D / 64], int lane) {
-  constexpr int PER = D / 64;
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const void *src = which ? v_row : k_row;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int d = lane * PER + k;
-      if constexpr (SRC == PKV_F32)
-        xs[which][k] = reinterpret_cast<const float *>(src)[d];
-      else
-        xs[which][k] = (float)reinterpret_cast<const _Float16 *>(src)[d];
-    }
-  }
+  TokenRaw<SRC, D> raw;
+  load_token_raw<SRC, D>(k_row, v_row, raw, lane);
+  token_from_raw<SRC, D>(raw, xs);
 }
 
 // Converts (fp32 / fp16 caches) or quantizes (int8 / E4M3, one scale per

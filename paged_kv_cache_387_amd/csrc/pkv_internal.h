@@ -22,6 +22,19 @@ constexpr int kDecodeWaves = PKV_DECODE_WAVES;   // wavefronts per decode workgr
 constexpr int kMaxGroup = 16;    // query heads per kv head (MFMA column count)
 constexpr int kXcds = 8;         // accelerator complex dies: workgroup i runs on die i % 8
 
+// How the decode kernel's waves share the tiles (see decode_kernel.h).
+constexpr int kWalkSplit = 0;    // one workgroup per (unit, partition), waves interleave tiles
+constexpr int kWalkRuns = 1;     // one workgroup per (unit, run of partitions), waves interleave tiles
+constexpr int kWalkStream = 2;   // equal shares of the batch's tiles per wave
+// Waves the stream walk deals the batch's tiles to: two 4-wave workgroups on
+// each of 256 compute units (also fixes the stream workspace's size).
+#ifndef PKV_STREAM_WAVES
+#define PKV_STREAM_WAVES 2048
+#endif
+constexpr int kStreamWaves = PKV_STREAM_WAVES;
+// Fewest tiles in a stream share (a smaller batch uses fewer waves).
+constexpr int kStreamMinShare = 16;
+
 inline int elem_bytes(int dtype) {
   return dtype == PKV_F32 ? 4 : dtype == PKV_F16 ? 2 : 1;
 }
@@ -35,8 +48,11 @@ struct DecodeParams {
   const uint16_t *v_scale;
   const int32_t *block_tables;
   const int32_t *seq_lens;
-  float *ws_o;      // [S][H][num_parts][D] normalized partial outputs
-  float *ws_lse;    // [S][H][num_parts] base-2 log-sum-exp of the partial
+  float *ws_o;      // [S][H][ws_stride][D] normalized partial outputs (stream walk:
+                    // [2 * stream_waves][group][D])
+  float *ws_lse;    // [S][H][ws_stride] base-2 log-sum-exp of the partial (stream walk:
+                    // [2 * stream_waves][group])
+  int32_t *ws_info; // stream walk: [num_units][2] first wave and piece count of each unit
   int num_blocks;
   int max_blocks;
   int num_seqs;
@@ -46,9 +62,12 @@ struct DecodeParams {
   int block_size;   // tokens per physical block: 8, 16 or 32
   int part_tiles;   // 16-token tiles per partition (whole blocks)
   int num_parts;    // partition slots per (sequence, head) workspace row (>= ceil(max tokens / 16 / part_tiles))
-  int run_parts;    // consecutive partitions one workgroup walks (>= 1; > 1 only when
-                    // part_tiles is a multiple of kDecodeWaves)
-  int num_runs;     // run slots per unit in the grid (>= ceil(partitions / run_parts))
+  int walk;         // kWalkSplit, kWalkRuns or kWalkStream
+  int run_parts;    // runs walk: consecutive partitions one workgroup walks (> 1, with
+                    // part_tiles a multiple of kDecodeWaves)
+  int num_runs;     // split / runs walks: workgroup slots per unit in the grid
+  int stream_waves; // stream walk: waves the batch's tiles are dealt to
+  int min_share;    // stream walk: fewest tiles per share
   int num_units;    // num_seqs * num_kv_heads
   float qk_scale;   // scale * log2(e): scores are kept in base 2
   // Fused decode step only: the new token of each sequence (row s of
@@ -148,7 +167,7 @@ inline int64_t decode_grid(int num_units, int num_runs) {
   return (int64_t)unit_groups(num_units) * kXcds * num_runs;
 }
 
-// LDS floats a decode workgroup sets aside for the finished partials of a
+// LDS floats a runs-walk workgroup sets aside for the finished partials of a
 // run (all but its last partition, which is stored directly): a row of
 // D + 4 floats (the normalized output, its log-sum-exp, padding to 16 bytes)
 // per query head and staged partition.  Room for 7 partitions of 8 heads.
@@ -186,10 +205,12 @@ hipError_t launch_decode(const DecodeParams &p, int cache_dtype, int out_dtype, 
                          hipStream_t stream);
 hipError_t launch_decode_step(const DecodeParams &p, int cache_dtype, int src_dtype,
                               int out_dtype, int head_dim, hipStream_t stream);
-// The decode kernel for run_parts > 1 (decode only, or the fused step when
-// `step`); the caller launches the merge.
+// The decode kernel of the runs and stream walks (decode only, or the fused
+// step when `step`); the caller launches the merge.
 hipError_t launch_decode_runs(const DecodeParams &p, int cache_dtype, bool step, int out_dtype,
                               int head_dim, hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeParams &p, int cache_dtype, bool step, int out_dtype,
+                                int head_dim, hipStream_t stream);
 // Columns (query vectors) one prefix workgroup handles: 16 per MFMA chunk.
 inline int prefix_chunks(int cache_dtype) { return cache_dtype == PKV_F32 ? 2 : 4; }
 inline int64_t prefix_grid(const PrefixParams &p) {
