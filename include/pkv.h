@@ -330,14 +330,39 @@ int paged_swap_blocks(void *k_cache, void *v_cache, void *k_scale, void *v_scale
 
 /* Partition size (tokens) paged_attention_decode uses for these shapes when
  * asked for `requested` (0 = the library's choice); a value >=
- * max_blocks_per_seq*block_size means one pass per (sequence, kv head). */
+ * max_blocks_per_seq*block_size means one pass per (sequence, kv head).
+ * With requested = 0 and a smaller value the call does not cut fixed
+ * partitions: it deals the batch's tiles to the GPU's waves in equal shares
+ * (PKV_WALK_STREAM below), and the value only records that it splits. */
 int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t requested);
 
+/* How paged_attention_decode (and paged_decode_step) spreads the work for
+ * these shapes; returns one of the values below, or PKV_EINVAL.
+ *   PKV_WALK_SPLIT:  one workgroup per (sequence, kv head, partition); a
+ *                    table of one partition is the single pass.
+ *   PKV_WALK_RUNS:   explicit partitions of a multiple of 64 tokens: one
+ *                    workgroup walks a run of consecutive partitions of a
+ *                    (sequence, kv head), each ending in its own partial.
+ *   PKV_WALK_STREAM: the library's choice for tables of several partitions:
+ *                    the batch's 16-token tiles, in (sequence, kv head, tile)
+ *                    order, are dealt to the waves in equal shares of whole
+ *                    blocks, so ragged lengths still give every wave the same
+ *                    bytes; a (sequence, kv head) split between shares is
+ *                    merged by the log-sum-exp reduction.
+ * The results do not depend on the walk beyond fp32 rounding order. */
+#define PKV_WALK_SPLIT 0
+#define PKV_WALK_RUNS 1
+#define PKV_WALK_STREAM 2
+int32_t paged_attention_decode_walk(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_size);
+
 /* Bytes of device workspace paged_attention_decode needs for these shapes
  * (0 when every sequence fits one partition): the partial outputs and their
- * log-sum-exps, fp32. */
+ * log-sum-exps, fp32 (PKV_WALK_STREAM: two slots of a kv head's query rows
+ * per wave, and an 8-byte record per (sequence, kv head)). */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                        int32_t num_kv_heads, int32_t head_dim,
                                        int32_t max_blocks_per_seq, int32_t block_size,
@@ -371,6 +396,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *            size is a multiple of 64 tokens, one workgroup may walk several
  *            consecutive partitions of a sequence (up to the library's own
  *            partition size); that changes the schedule, not the partials.
+ *            The library's choice splits at share boundaries instead of
+ *            fixed partitions (paged_attention_decode_walk).
  *   workspace: device, >= paged_attention_workspace_bytes(...) bytes,
  *            256-byte aligned (may be NULL when that size is 0); its contents
  *            on entry do not matter.  Calls that share a workspace must not
@@ -398,7 +425,7 @@ int paged_attention_decode(void *out, int32_t out_dtype, const void *query, int3
  * streams, not otherwise ordered) race and must not be issued; calls on one
  * stream are ordered and safe.  The array's contents on entry do not matter.
  * Other arguments and errors as paged_attention_decode. */
-#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define PKV_NOALLOC_SCRATCH_BYTES (48u << 20)
 int paged_attention_decode_noalloc(void *out, int32_t out_dtype, const void *query,
                                    int32_t q_dtype, const void *k_cache, const void *v_cache,
                                    const void *k_scale, const void *v_scale,

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 OK, EINVAL, ENOMEM, ENOENT, EEXIST, EDEVICE, ENOTSUP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
-NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 48 << 20   # PKV_NOALLOC_SCRATCH_BYTES
+WALK_SPLIT, WALK_RUNS, WALK_STREAM = 0, 1, 2   # PKV_WALK_*
 F32, F16, I8, E4M3 = 0, 1, 3, 4
 DTYPE = {"f32": F32, "f16": F16, "i8": I8, "e4m3": E4M3}
 ELEM_BYTES = {F32: 4, F16: 2, I8: 1, E4M3: 1}
@@ -37,6 +38,7 @@ EXPORTS = [
     "pkv_seq_allocate_cached", "pkv_seq_cache_blocks", "pkv_prefix_cache_evict",
     "pkv_prefix_cache_size", "pkv_prefix_cache_evictable", "paged_swap_blocks",
     "paged_kv_write", "paged_copy_blocks", "paged_attention_partition_size",
+    "paged_attention_decode_walk",
     "paged_attention_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_noalloc", "paged_decode_step",
     "paged_attention_shared_workspace_bytes", "paged_attention_decode_shared",
@@ -109,6 +111,7 @@ def lib() -> ctypes.CDLL:
             "paged_copy_blocks": ([P, P, P, P, i32, i32, P, i32, i32, i32, i32, P],
                                   ctypes.c_int),
             "paged_attention_partition_size": ([i32, i32, i32, i32, i32], i32),
+            "paged_attention_decode_walk": ([i32, i32, i32, i32, i32, i32, i32], i32),
             "paged_attention_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32], sz),
             "paged_attention_decode": ([P, i32, P, i32, P, P, P, P, i32, i32, P, i32, P, i32,
                                         i32, i32, i32, i32, f32, i32, P, sz, P], ctypes.c_int),
@@ -530,6 +533,17 @@ def partition_size(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int,
     v = lib().paged_attention_partition_size(num_seqs, num_kv_heads, max_blocks_per_seq,
                                              block_size, requested)
     _check(min(v, 0), "paged_attention_partition_size")
+    return v
+
+
+def decode_walk(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                max_blocks_per_seq: int, partition_size: int = 0,
+                block_size: int = BLOCK_SIZE) -> int:
+    """How paged_attention_decode spreads the work for these shapes:
+    WALK_SPLIT, WALK_RUNS or WALK_STREAM."""
+    v = lib().paged_attention_decode_walk(num_seqs, num_heads, num_kv_heads, head_dim,
+                                          max_blocks_per_seq, block_size, partition_size)
+    _check(min(v, 0), "paged_attention_decode_walk")
     return v
 
 

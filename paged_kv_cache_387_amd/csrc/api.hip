@@ -276,6 +276,21 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_kv_heads,
   return choose_part_tiles(max_blocks_per_seq, block_size, requested) * kTile;
 }
 
+int32_t paged_attention_decode_walk(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+      head_dim <= 0 || max_blocks_per_seq <= 0 || !valid_block_size(block_size) ||
+      !valid_partition(partition_size, block_size))
+    return PKV_EINVAL;
+  const DecodePlan pl = plan_decode((int64_t)num_seqs * num_kv_heads, max_blocks_per_seq,
+                                    block_size, partition_size, 0, num_heads / num_kv_heads,
+                                    head_dim);
+  return pl.walk == kWalkStream ? PKV_WALK_STREAM
+         : pl.walk == kWalkRuns ? PKV_WALK_RUNS
+                                : PKV_WALK_SPLIT;
+}
+
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                        int32_t num_kv_heads, int32_t head_dim,
                                        int32_t max_blocks_per_seq, int32_t block_size,

@@ -63,6 +63,34 @@ def test_partition_and_workspace_sizes():
         assert pkv.partition_size(8, 8, mb, block_size=bs) == 4096
 
 
+def test_decode_walk_choice_and_stream_workspace():
+    # the library's choice over tables of several partitions: equal shares
+    assert pkv.decode_walk(64, 64, 8, 128, 512) == pkv.WALK_STREAM
+    assert pkv.decode_walk(1, 8, 8, 64, 65) == pkv.WALK_STREAM
+    # a table of one partition (at most 1024 tokens): one pass per (sequence, kv head)
+    assert pkv.decode_walk(32, 64, 8, 128, 48) == pkv.WALK_SPLIT
+    assert pkv.decode_walk(32, 64, 8, 128, 64) == pkv.WALK_SPLIT
+    # explicit 512-token partitions over 32K-token tables: runs of partitions
+    assert pkv.decode_walk(8, 64, 8, 128, 2048, partition_size=512) == pkv.WALK_RUNS
+    # explicit partitions that are not whole wave rounds (one tile): one workgroup each
+    assert pkv.decode_walk(8, 64, 8, 128, 2048, partition_size=16) == pkv.WALK_SPLIT
+    # an explicit partition as long as the table: a single pass
+    assert pkv.decode_walk(8, 64, 8, 128, 256, partition_size=4096) == pkv.WALK_SPLIT
+    L = pkv.lib()
+    assert L.paged_attention_decode_walk(8, 9, 2, 128, 256, 16, 0) == pkv.EINVAL
+    assert L.paged_attention_decode_walk(8, 8, 2, 128, 256, 12, 0) == pkv.EINVAL
+    assert L.paged_attention_decode_walk(8, 8, 2, 128, 256, 16, 24) == pkv.EINVAL
+    # stream workspace: two partial slots of a kv head's query rows (fp32 D) per
+    # wave of the largest grid, their log-sum-exps, and 8 bytes per unit
+    r256 = lambda n: (n + 255) // 256 * 256
+    rows = 2 * 2048 * 8
+    lse_off = r256(rows * 128 * 4)
+    info_off = r256(lse_off + rows * 4)
+    assert pkv.workspace_bytes(64, 64, 8, 128, 512) == info_off + 64 * 8 * 8
+    # it fits the allocation-free entry point's scratch up to groups of 16
+    assert pkv.workspace_bytes(64, 128, 8, 128, 512) <= pkv.NOALLOC_SCRATCH_BYTES
+
+
 def _decode_status(**kw):
     args = dict(out=1 << 20, out_dtype=pkv.F16, query=1 << 20, q_dtype=pkv.F16,
                 k_cache=1 << 20, v_cache=1 << 20, k_scale=None, v_scale=None,

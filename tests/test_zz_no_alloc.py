@@ -19,9 +19,11 @@ from gpu_helpers import check_close, say  # noqa: E402
 
 CALLS = [
     # (name, lens, H, Hkv, cache dtype, partition): split-K with runs, then a
-    # smaller ragged batch with other partitions
+    # smaller ragged batch with other partitions, then the library's choice
+    # (equal shares of the batch's tiles, per-unit records in the scratch)
     ("big", [4096] * 8, 64, 8, "f16", 512),
     ("small", [100, 1500, 2999], 16, 2, "f16", 256),
+    ("shares", [3000, 17, 0, 1200, 500], 32, 4, "f16", 0),
 ]
 
 
