@@ -28,10 +28,7 @@ constexpr int kWalkRuns = 1;     // one workgroup per (unit, run of partitions),
 constexpr int kWalkStream = 2;   // equal shares of the batch's tiles per wave
 // Waves the stream walk deals the batch's tiles to: two 4-wave workgroups on
 // each of 256 compute units (also fixes the stream workspace's size).
-#ifndef PKV_STREAM_WAVES
-#define PKV_STREAM_WAVES 2048
-#endif
-constexpr int kStreamWaves = PKV_STREAM_WAVES;
+constexpr int kStreamWaves = 2048;
 // Fewest tiles in a stream share (a smaller batch uses fewer waves).
 constexpr int kStreamMinShare = 16;
 
