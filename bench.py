@@ -235,8 +235,8 @@ def pmc_copy(nbytes: int = 1 << 30, reps: int = 5, nontemporal: bool = True) -> 
 
 # Sources that determine what one paged_attention_decode call moves: the
 # counter-based traffic figure is used only while these are unchanged.
-DECODE_SOURCES = ("decode_kernel.h", "decode.hip", "decode_runs.hip", "api.hip",
-                  "pkv_internal.h")
+DECODE_SOURCES = ("decode_kernel.h", "decode.hip", "decode_runs.hip", "decode_stream.hip",
+                  "api.hip", "pkv_internal.h", "attn_common.h", "kv_write.h")
 
 
 def decode_source_hash() -> str:
