@@ -112,7 +112,8 @@ def kv_read_bytes(lens, w) -> int:
 def cpu_baseline(w, budget_s: float = 10.0):
     """Time the oracle (as it stands) on a bounded sample of one batch: the
     first k sequences (k grown until one pass takes at least 0.5 s, or the
-    whole batch), passed over repeatedly until budget_s seconds have gone."""
+    whole batch), passed over repeatedly until budget_s seconds have gone (at
+    least three passes); the rate is that of the median pass."""
     import oracle
     from oracle.replay import replay as oracle_replay
     ro = oracle_replay(w)
@@ -127,28 +128,28 @@ def cpu_baseline(w, budget_s: float = 10.0):
         if dt >= 0.5 or k >= n:
             break
         k = min(n, k * 4)
-    reps, elapsed = 1, dt
-    while elapsed < budget_s:
+    passes = [dt]
+    while sum(passes) < budget_s or len(passes) < 3:
         t0 = time.perf_counter()
         oracle.decode(ro.pools, ro.q[:k], ro.block_tables[:k], lens[:k], np.float32(w.scale))
-        elapsed += time.perf_counter() - t0
-        reps += 1
-    per = elapsed / reps
+        passes.append(time.perf_counter() - t0)
+    reps, elapsed = len(passes), sum(passes)
+    per = float(np.median(passes))
     b = kv_read_bytes(lens[:k], w)
     # the same oracle on one thread (after the timing above: the thread count
     # set here stays for the rest of the process), first sequence only
-    reps1, el1 = 0, 0.0
-    while el1 < min(3.0, budget_s) or reps1 == 0:
+    passes1 = []
+    while sum(passes1) < min(3.0, budget_s) or len(passes1) < 3:
         t0 = time.perf_counter()
         oracle.decode(ro.pools, ro.q[:1], ro.block_tables[:1], lens[:1], np.float32(w.scale),
                       num_threads=1)
-        el1 += time.perf_counter() - t0
-        reps1 += 1
-    per1 = el1 / reps1
+        passes1.append(time.perf_counter() - t0)
+    reps1, el1 = len(passes1), sum(passes1)
+    per1 = float(np.median(passes1))
     return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle",
             "sample": f"{k} of {n} sequences of one batch ({int(lens[:k].sum())} tokens), "
-                      f"fp64, {reps} pass(es) in {elapsed:.1f} s, {per:.3f} s per pass",
+                      f"fp64, {reps} pass(es) in {elapsed:.1f} s, median {per:.3f} s per pass",
             "seqs_per_s": round(k / per, 3),
             "one_core": {"value": round(kv_read_bytes(lens[:1], w) / per1 / 1e9, 4),
                          "unit": "GB/s", "cores": 1,
