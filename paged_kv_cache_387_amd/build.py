@@ -17,6 +17,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 HIP_SOURCES = ["api.hip", "decode.hip", "decode_runs.hip", "decode_stream.hip", "prefix.hip",
+               "prefix_pipe.hip",
                "cache_ops.hip"]
 CXX_SOURCES = ["allocator.cpp"]
 ARCH = "gfx950"

@@ -208,10 +208,11 @@ PrefixPlan plan_prefix(const pkv_prefix_groups *gr, int32_t num_heads, int32_t n
 }
 
 // Multi-token queries: partitions of the table's tokens.  One pass per
-// (sequence, kv head, 64-column block) when there are enough of them for the
+// (sequence, kv head, column block) when there are enough of them for the
 // compute units, else partitions of at least 32 tiles; explicit sizes must
-// be whole 32-token steps and whole blocks.
-constexpr int kPrefillCols = 64;
+// be whole 32-token steps and whole blocks.  The partitions are planned for
+// the pipelined pass's 256-column blocks whatever the cache type, so that the
+// workspace size does not depend on it.
 
 struct PrefillPlan {
   int64_t col_blocks = 0;
@@ -228,7 +229,7 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_heads, int32_t num_kv_hea
                          int32_t requested) {
   PrefillPlan pl;
   const int64_t cols = (int64_t)max_query_len * (num_heads / num_kv_heads);
-  pl.col_blocks = (cols + kPrefillCols - 1) / kPrefillCols;
+  pl.col_blocks = (cols + kPipeCols - 1) / kPipeCols;
   const int64_t tiles = max_tiles_of(max_blocks, block_size);
   int64_t pt;
   if (requested > 0) {
@@ -688,8 +689,11 @@ int paged_attention_prefill(void *out, int32_t out_dtype, const void *query, int
   const PrefillPlan pl = plan_prefill(num_seqs, num_heads, num_kv_heads, max_query_len,
                                       max_blocks_per_seq, block_size, partition_size);
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int wg_cols = cache_dtype == PKV_F16 ? kPipeCols : kPrefixCols;
+  const int64_t col_blocks =
+      ((int64_t)max_query_len * (num_heads / num_kv_heads) + wg_cols - 1) / wg_cols;
   if ((int64_t)num_query_tokens * num_heads > INT32_MAX || units > INT32_MAX ||
-      (int64_t)unit_groups((int)std::min<int64_t>(units, INT32_MAX)) * kXcds * pl.col_blocks *
+      (int64_t)unit_groups((int)std::min<int64_t>(units, INT32_MAX)) * kXcds * col_blocks *
               pl.num_pparts > INT32_MAX)
     return PKV_ENOTSUP;
   WorkspaceLayout wl{0, 0, 0};
@@ -714,7 +718,7 @@ int paged_attention_prefill(void *out, int32_t out_dtype, const void *query, int
   pp.num_kv_heads = num_kv_heads;
   pp.group = num_heads / num_kv_heads;
   pp.num_units = (int)units;
-  pp.col_blocks = (int)pl.col_blocks;
+  pp.col_blocks = (int)col_blocks;
   pp.pp_tiles = pl.pp_tiles;
   pp.num_pparts = pl.num_pparts;
   pp.ws_stride = pl.num_pparts;

@@ -15,6 +15,10 @@ constexpr int kTile = 16;        // tokens per decode tile (the MFMA row count)
 #define PKV_WAVES 4
 #endif
 constexpr int kWaves = PKV_WAVES;  // wavefronts per workgroup of the multi-query passes
+// Modes of the multi-query passes: queries of a shared prefix's group
+// (partials out), or a sequence's own query tokens with causal limits.
+constexpr int kModeShared = 0;
+constexpr int kModePrefill = 1;
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 4
 #endif
@@ -216,6 +220,14 @@ inline int64_t prefix_grid(const PrefixParams &p) {
 hipError_t launch_prefix(const PrefixParams &p, int cache_dtype, int head_dim, int block_size,
                          hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipStream_t stream);
+// The pipelined pass of fp16 caches (shared prefixes or multi-token
+// queries): 64 * 4 / token_groups columns per workgroup, token_groups 1 or 2.
+hipError_t launch_pipe(const PrefixParams &p, bool prefill, int out_dtype, int head_dim,
+                       int block_size, int token_groups, hipStream_t stream);
+// Columns of a workgroup of the pipelined pass with one token group, and of
+// prefix32_kernel (quantized caches).
+constexpr int kPipeCols = 256;
+constexpr int kPrefixCols = 64;
 // Multi-token queries: the pass (and, with several partitions, the merge).
 hipError_t launch_prefill(const PrefixParams &p, int cache_dtype, int out_dtype, int head_dim,
                           int block_size, hipStream_t stream);

@@ -24,50 +24,12 @@
 // K and V operands of a tile are prepared once and reused by every column, so
 // the MFMA work per byte loaded is the column count times that of decode.
 #include "attn_common.h"
+#include "lds_ring.h"
 
 namespace pkv {
 namespace {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
-
-// Wait until at most N vector-memory operations of the wave are outstanding
-// (loads complete in issue order), and keep the compiler from moving memory
-// accesses across the wait.  Loads straight into LDS are not tracked by the
-// compiler's own wait counts, so the ring below waits for them explicitly.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void load16_to_lds(const uint8_t *src, u4 *lds_row) {
-  __builtin_amdgcn_global_load_lds(
-      (const __attribute__((address_space(1))) void *)src,
-      (__attribute__((address_space(3))) void *)lds_row, 16, 0, 0);
-}
-
-// 16-byte LDS read at byte address `addr` + OFF (an LDS offset).  Issued as
-// inline assembly: the compiler would otherwise wait for every load in flight
-// into LDS before any LDS read (it cannot tell the ring's slots apart).  The
-// caller waits with lds_wait before using the value.
-template <int OFF>
-__device__ __forceinline__ u4 lds_read16(uint32_t addr) {
-  u4 x;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(addr), "i"(OFF));
-  return x;
-}
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// Makes later uses of x depend on the preceding lds_wait.
-__device__ __forceinline__ void after_wait(u4 &x) { asm volatile("" : "+v"(x)); }
-
-template <int I, int N, int STRIDE>
-__device__ __forceinline__ void lds_read_row(uint32_t addr, u4 *out) {
-  if constexpr (I < N) {
-    out[I] = lds_read16<I * STRIDE>(addr);
-    lds_read_row<I + 1, N, STRIDE>(addr, out);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // fp32 caches: 16x16 MFMA blocks (fp32 operands have no 32x32x16 form).
@@ -411,9 +373,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefix_kernel(PrefixParams p) 
 // are (sequence, kv head), columns its query tokens' heads with causal
 // limits; `out` (of type OUT) is written directly when there is one
 // partition, else partials.
-constexpr int kModeShared = 0;
-constexpr int kModePrefill = 1;
-
 template <int KV, int D, int BS, int MODE, int OUT>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefix32_kernel(PrefixParams p) {
   constexpr int EB = Kv<KV>::EB;
@@ -1124,12 +1083,6 @@ template <int KV, int D, int BS, int OUT>
 hipError_t launch_prefill_typed(const PrefixParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((prefix32_kernel<KV, D, BS, kModePrefill, OUT>),
                      dim3((unsigned)prefix_grid(p)), dim3(64 * kWaves), 0, stream, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.num_pparts <= 1) return err;
-  constexpr int RPW = 256 / (D / 4);
-  const int rows = p.num_query_tokens * p.num_heads;
-  hipLaunchKernelGGL((prefill_merge_kernel<D, OUT>), dim3((rows + RPW - 1) / RPW), dim3(256), 0,
-                     stream, p);
   return hipGetLastError();
 }
 
@@ -1156,15 +1109,33 @@ hipError_t launch_prefill_o(const PrefixParams &p, int out_dtype, int head_dim, 
                               : launch_prefill_d<KV, PKV_F16>(p, head_dim, block_size, stream);
 }
 
+template <int D, int OUT>
+hipError_t launch_prefill_merge_typed(const PrefixParams &p, hipStream_t stream) {
+  constexpr int RPW = 256 / (D / 4);
+  const int rows = p.num_query_tokens * p.num_heads;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, OUT>), dim3((rows + RPW - 1) / RPW), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefixParams &p, int cache_dtype, int out_dtype, int head_dim,
                           int block_size, hipStream_t stream) {
+  hipError_t err;
   switch (cache_dtype) {
-    case PKV_F16: return launch_prefill_o<PKV_F16>(p, out_dtype, head_dim, block_size, stream);
-    case PKV_I8: return launch_prefill_o<PKV_I8>(p, out_dtype, head_dim, block_size, stream);
-    default: return launch_prefill_o<PKV_E4M3>(p, out_dtype, head_dim, block_size, stream);
+    case PKV_F16:
+      err = launch_pipe(p, true, out_dtype, head_dim, block_size, 1, stream);
+      break;
+    case PKV_I8: err = launch_prefill_o<PKV_I8>(p, out_dtype, head_dim, block_size, stream); break;
+    default: err = launch_prefill_o<PKV_E4M3>(p, out_dtype, head_dim, block_size, stream); break;
   }
+  if (err != hipSuccess || p.num_pparts <= 1) return err;
+  if (out_dtype == PKV_F32)
+    return head_dim == 64 ? launch_prefill_merge_typed<64, PKV_F32>(p, stream)
+                          : launch_prefill_merge_typed<128, PKV_F32>(p, stream);
+  return head_dim == 64 ? launch_prefill_merge_typed<64, PKV_F16>(p, stream)
+                        : launch_prefill_merge_typed<128, PKV_F16>(p, stream);
 }
 
 hipError_t launch_prefix(const PrefixParams &p, int cache_dtype, int head_dim, int block_size,
