@@ -170,12 +170,13 @@ WorkspaceLayout workspace_layout(const DecodePlan &pl, int32_t num_seqs, int32_t
 }
 
 // Shared-prefix partitioning: enough (group, kv head, column block,
-// partition) workgroups to give every compute unit one (each holds 64 query
-// columns in 4 waves, one wave per SIMD), with partitions of at least 16
-// tiles and a multiple of the wave count.
+// partition) workgroups to give every compute unit one, with partitions of
+// at least 16 tiles and a multiple of the wave count.  Planned for the
+// 128-column blocks of the pipelined pass (fp16 caches) whatever the cache
+// type, so that the workspace size does not depend on it.
 constexpr int64_t kPrefixTargetWgs = 256;
 constexpr int64_t kPrefixMinTiles = 16;
-constexpr int kPrefixNominalCols = 64;
+constexpr int kPrefixNominalCols = kPipeSharedCols;
 
 struct PrefixPlan {
   int32_t pp_tiles = 0, num_pparts = 0;
@@ -594,9 +595,9 @@ int paged_attention_decode_shared(void *out, int32_t out_dtype, const void *quer
   PrefixParams pp{};
   if (gr.num_groups > 0 && pl.num_pparts > 0) {
     const int64_t units = (int64_t)gr.num_groups * num_kv_heads;
-    const int chunks = prefix_chunks(cache_dtype);
+    const int wg_cols = cache_dtype == PKV_F16 ? kPipeSharedCols : 16 * prefix_chunks(cache_dtype);
     const int64_t cols = (int64_t)gr.max_group_size * (num_heads / num_kv_heads);
-    const int64_t col_blocks = (cols + 16 * chunks - 1) / (16 * chunks);
+    const int64_t col_blocks = (cols + wg_cols - 1) / wg_cols;
     if (units > INT32_MAX || col_blocks > INT32_MAX ||
         (int64_t)unit_groups((int)units) * kXcds * col_blocks * pl.num_pparts > INT32_MAX)
       return PKV_ENOTSUP;

@@ -224,9 +224,11 @@ hipError_t launch_merge(const DecodeParams &p, int out_dtype, int head_dim, hipS
 // queries): 64 * 4 / token_groups columns per workgroup, token_groups 1 or 2.
 hipError_t launch_pipe(const PrefixParams &p, bool prefill, int out_dtype, int head_dim,
                        int block_size, int token_groups, hipStream_t stream);
-// Columns of a workgroup of the pipelined pass with one token group, and of
+// Columns of a workgroup of the pipelined pass with one token group
+// (multi-token queries) and with two (shared prefixes), and of
 // prefix32_kernel (quantized caches).
 constexpr int kPipeCols = 256;
+constexpr int kPipeSharedCols = 128;
 constexpr int kPrefixCols = 64;
 // Multi-token queries: the pass (and, with several partitions, the merge).
 hipError_t launch_prefill(const PrefixParams &p, int cache_dtype, int out_dtype, int head_dim,

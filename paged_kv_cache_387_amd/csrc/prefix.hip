@@ -1142,7 +1142,7 @@ hipError_t launch_prefix(const PrefixParams &p, int cache_dtype, int head_dim, i
                          hipStream_t stream) {
   switch (cache_dtype) {
     case PKV_F32: return launch_prefix_d<PKV_F32>(p, head_dim, block_size, stream);
-    case PKV_F16: return launch_prefix_d<PKV_F16>(p, head_dim, block_size, stream);
+    case PKV_F16: return launch_pipe(p, false, PKV_F32, head_dim, block_size, 2, stream);
     case PKV_I8: return launch_prefix_d<PKV_I8>(p, head_dim, block_size, stream);
     default: return launch_prefix_d<PKV_E4M3>(p, head_dim, block_size, stream);
   }

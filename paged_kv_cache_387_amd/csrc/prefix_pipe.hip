@@ -199,18 +199,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   const size_t block_stride = (size_t)p.num_kv_heads * (BS * D * EB);
   u4(*ring)[LPS][64] = reinterpret_cast<u4(*)[LPS][64]>(&lds_raw[0]) + tgi * NR;
 
-  // Table entries of this group's steps kb + lane (TPS per step), clamped.
-  auto load_tv = [&](int kb, int *tv) {
-    const int k = kb + lane;
-    const int gs = tgi + TG * (k < ns_g ? k : 0);
+  // Table entries of the group's step k (TPS of them, clamped to the row),
+  // read with scalar loads: the row is never written during the pass.  They
+  // are read one issue ahead (unconditionally, so that no register value is
+  // merged from two paths), which hides their latency under a step and keeps
+  // them out of the vector-memory count the ring's waits rely on.
+  const __attribute__((address_space(4))) int32_t *trow_s =
+      (const __attribute__((address_space(4))) int32_t *)trow;
+  auto entries = [&](int k, int *e) {
+    const int gs = tgi + TG * k;
     const int e0 = (first / 2 + gs) * TPS;
 #pragma unroll
-    for (int e = 0; e < TPS; ++e) tv[e] = trow[e0 + e < tlim ? e0 + e : tlim - 1];
+    for (int q = 0; q < TPS; ++q) e[q] = trow_s[e0 + q < tlim ? e0 + q : tlim - 1];
   };
-  int tv_base = 0;
-  int tv_cur[TPS], tv_nxt[TPS];
-  load_tv(0, tv_cur);
-  load_tv(64, tv_nxt);
+  int ent[TPS];   // entries of the next step to issue
 
   // Block (and tile within it) of token tt (0..31) of a step whose table
   // entries are e[]; *row receives the token's row in the stored tile.
@@ -254,14 +256,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   // This wave's rows of the group's step k into ring slot `slot`.  Entries
   // past the data (padding) are replaced by the step's first; a missing
   // second tile is read from the first (its weights are zero).
-  auto issue = [&](int k, int slot) {
-    if (k - tv_base >= 64) {   // the next 64 steps' entries
-#pragma unroll
-      for (int e = 0; e < TPS; ++e) tv_cur[e] = tv_nxt[e];
-      tv_base += 64;
-      load_tv(tv_base + 64, tv_nxt);
-    }
-    const int j = k - tv_base;
+  auto issue = [&](int k, int slot, const int *ek) {
     const int st = first + 2 * (tgi + TG * k);
     const bool half = st + 1 >= last;
     const int left = ltok - st * kTile;
@@ -272,7 +267,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     int e[TPS];
 #pragma unroll
     for (int q = 0; q < TPS; ++q) {
-      e[q] = __builtin_amdgcn_readlane(tv_cur[q < used ? q : 0], j);
+      e[q] = ek[q < used ? q : 0];
       e[q] = (unsigned)e[q] < (unsigned)p.num_blocks ? e[q] : 0;
     }
     const int tmask = half ? 15 : 31;
@@ -434,7 +429,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   };
 #pragma unroll
   for (int j = 0; j < NR - 1; ++j)
-    if (j < ns_g) issue(j, j);
+    if (j < ns_g) {
+      entries(j, ent);
+      issue(j, j, ent);
+    }
+  entries(NR - 1, ent);
   if (ns_g > 0) wait_step(min(NR - 2, ns_g - 1));
   barrier();
   f16v S[NB2];
@@ -450,7 +449,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     const int fslot = slot == 0 ? NR - 1 : slot - 1;   // slot of step k-1, refilled now
     if (k + 1 < ns_g) wait_step(min(NR - 3, ns_g - 2 - k));
     barrier();
-    if (k + NR - 1 < ns_g) issue(k + NR - 1, fslot);
+    if (k + NR - 1 < ns_g) issue(k + NR - 1, fslot, ent);
+    entries(k + NR, ent);
   };
   // Steps 0 .. nfast-1 have a next step and no masks: the last steps of a
   // walk are the only ones that can hold a missing second tile (the last) or,
@@ -490,7 +490,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   };
   int k = 0, slot = 0;
   f16v S2[NB2];
-  // two steps per iteration, so that the scores alternate between S and S2
+  // four steps per iteration (two where fewer are left): the scores
+  // alternate between S and S2, and the loop's fixed costs spread further
+  for (; k + 4 <= nfast; k += 4) {
+    slot = fast_step(k, slot, S, S2);
+    slot = fast_step(k + 1, slot, S2, S);
+    slot = fast_step(k + 2, slot, S, S2);
+    slot = fast_step(k + 3, slot, S2, S);
+  }
   for (; k + 2 <= nfast; k += 2) {
     slot = fast_step(k, slot, S, S2);
     slot = fast_step(k + 1, slot, S2, S);

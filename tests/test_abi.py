@@ -201,12 +201,13 @@ def test_shared_argument_validation(groups, kw, status):
 
 def test_shared_workspace_sizes():
     # 64 sequences sharing an 8192-token prefix, suffix tables 65 blocks wide:
-    # suffix partitions (64 tiles each: 2, padded to 3) then 4 prefix
-    # partitions of 128 tiles per (sequence, head) row
+    # suffix partitions (64 tiles each: 2, padded to 3) then 8 prefix
+    # partitions of 64 tiles per (sequence, head) row (8 kv heads x 4 blocks
+    # of 128 columns x 8 partitions = 256 workgroups)
     g = _groups(num_groups=1, num_members=64, max_group_size=64, max_prefix_blocks=512)
     ws = pkv.lib().paged_attention_shared_workspace_bytes(64, 64, 8, 128, 65, 16, 0,
                                                           ctypes.byref(g))
-    rows = 64 * 64 * (3 + 4)
+    rows = 64 * 64 * (3 + 8)
     assert ws == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
     # no groups: the plain decode's workspace
     g0 = _groups(num_groups=0)
