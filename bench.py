@@ -240,12 +240,22 @@ DECODE_SOURCES = ("decode_kernel.h", "decode.hip", "decode_runs.hip", "decode_st
                   "api.hip", "pkv_internal.h", "attn_common.h", "kv_write.h")
 
 
-def decode_source_hash() -> str:
+# Sources of the multi-query passes (shared prefixes, multi-token queries).
+PASS_SOURCES = ("prefix.hip", "prefix_pipe.hip", "lds_ring.h", "api.hip", "pkv_internal.h",
+                "attn_common.h")
+
+
+def decode_source_hash(files=DECODE_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in files:
         h.update(open(os.path.join(ROOT, "paged_kv_cache_387_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def source_line() -> str:
+    return (f"# source={decode_source_hash()}  (hash of the decode sources); "
+            f"pass_source={decode_source_hash(PASS_SOURCES)}  (of the multi-query passes)")
 
 
 def read_traffic(workload: str):
@@ -335,11 +345,12 @@ def summarize_trace(workload, trace_csv, stats_csv, commands):
         agg[(short, r["Grid_Size_X"], r["Grid_Size_Y"])].append(
             int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     out = [f"# rocprofv3 kernel trace summary, workload {workload}: kernels of the library "
-           f"(decode_kernel<KV, D, OUT, SRC, BS>: SRC >= 0 is the fused step, -1 the plain "
-           f"decode; prefix32_kernel<KV, D, BS, MODE, OUT>: MODE 0 shared prefix, 1 prefill)",
+           f"(decode_kernel<KV, D, OUT, SRC, BS, WALK>: SRC >= 0 is the fused step, -1 the plain "
+           f"decode; prefix32_kernel<KV, D, BS, MODE, OUT> and pipe32_kernel<D, BS, MODE, OUT, "
+           f"TG>: MODE 0 shared prefix, 1 prefill)",
            "# commands (run from the repository root on the GPU host):"]
     out += [f"#   {c}" for c in commands]
-    out.append(f"# source={decode_source_hash()}  (hash of the decode sources)")
+    out.append(source_line())
     out.append("# run_kernel_stats.csv (durations in ns; the bench setup's bulk cache writes and "
                "host copies are included):")
     out += [line.rstrip("\n") for line in open(stats_csv)]
@@ -361,13 +372,15 @@ def summarize_trace(workload, trace_csv, stats_csv, commands):
 
 
 def summarize_counters(name, csv_path, commands, kernels=("decode_kernel", "prefix32_kernel",
-                                                         "merge_kernel")):
-    """Write profiles/<name>_sq_counters.txt from a rocprofv3 --pmc counter CSV:
-    each library kernel's counters averaged over its dispatches."""
+                                                         "pipe32_kernel", "merge_kernel")):
+    """Write profiles/<name>_sq_counters.txt from rocprofv3 --pmc counter CSVs
+    (one per pass, comma-separated): each library kernel's counters averaged
+    over its dispatches."""
     import csv
     import collections
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
-    for r in csv.DictReader(open(csv_path)):
+    rows = [r for path in csv_path.split(",") for r in csv.DictReader(open(path))]
+    for r in rows:
         k = r["Kernel_Name"]
         if any(x in k for x in kernels):
             short = k.replace("void ", "").replace("pkv::(anonymous namespace)::", "")
@@ -376,7 +389,7 @@ def summarize_counters(name, csv_path, commands, kernels=("decode_kernel", "pref
     out = [f"# rocprofv3 counters per dispatch (averages), {name}",
            "# commands (run from the repository root on the GPU host):"]
     out += [f"#   {c}" for c in commands]
-    out.append(f"# source={decode_source_hash()}  (hash of the decode sources)")
+    out.append(source_line())
     for k, v in sorted(agg.items()):
         n = max(len(x) for x in v.values())
         out.append(f"{k}  ({n} dispatches)")

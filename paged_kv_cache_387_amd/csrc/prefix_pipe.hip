@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   // each lane's 16 bytes as the lane reads them.  With two token groups the
   // same memory then holds group 1's accumulators for the combine.
   constexpr int kRingU4 = TG * NR * LPS * 64;
-  constexpr int kAccU4 = TG > 1 ? CG * NB2 * NT * 64 * 4 : 0;
+  constexpr int kAccU4 = TG > 1 ? CG * NB2 * NT * 4 * 64 : 0;
   __shared__ u4 lds_raw[kRingU4 > kAccU4 ? kRingU4 : kAccU4];
   __shared__ float lds_m[TG > 1 ? CG * CW : 1];
   __shared__ float lds_l[TG > 1 ? CG * CW : 1];
@@ -546,7 +546,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     l[nb] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   }
   if constexpr (TG > 1) {
-    f16v(*lds_acc)[NB2][NT][64] = reinterpret_cast<f16v(*)[NB2][NT][64]>(&lds_raw[0]);
+    // [column group][block][tile][piece][lane]: a lane's 16-byte pieces
+    // next to its neighbours', free of bank conflicts
+    f4(*lds_acc)[NB2][NT][4][64] = reinterpret_cast<f4(*)[NB2][NT][4][64]>(&lds_raw[0]);
     barrier();   // every wave is done with the ring
     if (tgi == 1 && !idle) {
 #pragma unroll
@@ -556,7 +558,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
           lds_l[cgi * CW + 32 * nb + n] = l[nb];
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) lds_acc[cgi][nb][t][lane] = acc[nb][t];
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            lds_acc[cgi][nb][t][q][lane] = f4{acc[nb][t][4 * q], acc[nb][t][4 * q + 1],
+                                              acc[nb][t][4 * q + 2], acc[nb][t][4 * q + 3]};
       }
     }
     __syncthreads();
@@ -569,7 +575,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
       const float f0 = m[nb] == -INFINITY ? 0.0f : exp2f(m[nb] - M);
       const float f1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[nb][t] = acc[nb][t] * f0 + lds_acc[cgi][nb][t][lane] * f1;
+      for (int t = 0; t < NT; ++t) {
+        const f4 *o = &lds_acc[cgi][nb][t][0][lane];
+        const f16v other = f16v{o[0][0], o[0][1], o[0][2], o[0][3], o[64][0], o[64][1],
+                                o[64][2], o[64][3], o[128][0], o[128][1], o[128][2],
+                                o[128][3], o[192][0], o[192][1], o[192][2], o[192][3]};
+        acc[nb][t] = acc[nb][t] * f0 + other * f1;
+      }
       l[nb] = l[nb] * f0 + l1 * f1;
       m[nb] = M;
     }
