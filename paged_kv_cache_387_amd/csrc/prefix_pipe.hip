@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   constexpr int NT = 2 * NG;                   // output tiles (32 rows) per column block
   constexpr int LPS = NKK + VLD;               // 16-byte rows (x 64 lanes) of a step
   constexpr int LPW = LPS / CG;                // of them loaded by each wave
-  constexpr int NR = TG == 1 ? 6 : 4;          // ring depth (steps)
+  constexpr int NR = 4;                        // ring depth (steps)
   constexpr int NB2 = 2;                       // column blocks of 32 per wave
   constexpr int CW = 32 * NB2;                 // columns per wave
   constexpr int EB = 2;
@@ -407,7 +407,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   };
 
   // ---- the walk.  Ring slot of step k: k % NR.  The prologue issues steps
-  // 0 .. NR-2.  Iteration k waits for step k+1 (loads issued after it: those
+  // 0 .. NR-2.  (In the pipelined loop the refill of iteration k goes out
+  // after step k+1's q.K MFMAs instead, which keeps the load instructions
+  // off the head of the step; the order of the loads is the same.)  Iteration k waits for step k+1 (loads issued after it: those
   // of steps k+2 .. k+NR-2 that exist, issued earlier), meets the group at a barrier (every wave
   // has then finished iteration k-1, so slot (k-1) % NR is free, and every
   // wave's rows of step k+1 are in LDS), issues step k+NR-1 into the freed
@@ -471,7 +473,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   auto fast_step = [&](int k, int slot, f16v *si, f16v *so) {
     const int nslot = slot + 1 == NR ? 0 : slot + 1;
     const int t0 = (first + 2 * (tgi + TG * k)) * kTile;
-    advance(k, slot);
+    if (k + 1 < ns_g) wait_step(min(NR - 3, ns_g - 2 - k));
+    barrier();
     u4 kr[NKK], vr[VLD];
     lds_read_row<0, NKK, 1024>(ring_addr(nslot), kr);
     h8 pb[NB2][2];
@@ -482,6 +485,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     lds_read_row<0, VLD, 1024>(ring_addr(slot) + NKK * 1024, vr);
     __builtin_amdgcn_sched_barrier(0);   // the V reads go out before the work they hide under
     qk(kr, so);
+    {
+      const int fslot = slot == 0 ? NR - 1 : slot - 1;
+      if (k + NR - 1 < ns_g) issue(k + NR - 1, fslot, ent);
+      entries(k + NR, ent);
+    }
     lds_wait();
 #pragma unroll
     for (int i = 0; i < VLD; ++i) after_wait(vr[i]);
