@@ -71,6 +71,25 @@ def test_prefill_f32_output():
     _run("ragged", 0, out_dtype=torch.float32)
 
 
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+@pytest.mark.parametrize("name", ["ragged", "i8"])
+def test_prefill_scale_sign(name, scale):
+    """A negative scale (the fp16 pass folds its sign into q) and a zero scale
+    (uniform weights over each query's causal prefix)."""
+    import paged_kv_cache_387_amd as pkv
+    import hip_replay as driver
+    pkv.lib()
+    w = CASES[name]()
+    w.scale = scale
+    w.memo = {}
+    say(f"prefill {name} scale={scale}")
+    ro = oracle_replay(w)
+    rg = driver.replay(w)
+    out = driver.prefill(rg, w, partition_size=0)
+    torch.cuda.synchronize()
+    check_close(out, oracle_prefill_output(ro, w), w.cache_dtype, f"{name} scale={scale}")
+
+
 def test_prefill_one_token_is_the_decode():
     """One query token per sequence gives paged_attention_decode's output."""
     import paged_kv_cache_387_amd as pkv

@@ -58,13 +58,15 @@ CASES = {
 }
 
 
-def _run(name, step, part, min_prefix=0):
+def _run(name, step, part, min_prefix=0, scale=None):
     import paged_kv_cache_387_amd as pkv
     import hip_replay as driver
     pkv.lib()
     w = CASES[name]()
     if step and not any(op[0] == "step" for op in w.ops):
         w = W.with_decode_step(w)
+    if scale is not None:
+        w.scale = scale
     w.memo = {}
     if part == "min":   # the smallest partition: one tile, or one block if larger
         part = max(16, w.block_size)
@@ -92,6 +94,15 @@ def _run(name, step, part, min_prefix=0):
 @pytest.mark.parametrize("name", list(CASES))
 def test_shared_matches_oracle(name, step, part):
     sh = _run(name, step, part)
+    assert sh["num_groups"] >= 1
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+@pytest.mark.parametrize("name", ["big_group", "i8"])
+def test_shared_scale_sign(name, scale):
+    """A negative scale (the fp16 prefix pass folds its sign into q) and a
+    zero scale (uniform weights), through the suffix, prefix and merge."""
+    sh = _run(name, False, 0, scale=scale)
     assert sh["num_groups"] >= 1
 
 

@@ -10,7 +10,10 @@ objects of the in-tree build (_build/*.o, written by
 paged_kv_cache_387_amd.build) with the ROCm LLVM tools and requires:
   * no scratch in any fp16 / int8 / E4M3 decode kernel, nor in the merge;
   * at most 32 bytes per lane in the fp32-cache kernels of head_dim 128, whose
-    register budget is full (a few spilled scalars, not the ring).
+    register budget is full (a few spilled scalars, not the ring);
+  * no scratch in any build of the pipelined fp16 multi-query pass (its
+    accumulators, q and the scores of two steps fill both register files; a
+    spill there reloads q from scratch at every MFMA).
 Skipped when the build objects or the tools are absent.
 """
 import os
@@ -64,3 +67,13 @@ def test_decode_kernels_keep_their_state_in_registers(src, tmp_path):
             assert nbytes <= limit, f"{src}: {name} uses {nbytes} bytes of scratch per lane"
         elif "merge_kernel" in name:
             assert nbytes == 0, f"{src}: {name} uses {nbytes} bytes of scratch per lane"
+
+
+def test_multi_query_pass_keeps_its_state_in_registers(tmp_path):
+    scratch = _kernel_scratch(os.path.join(OBJ_DIR, "prefix_pipe.hip.o"), tmp_path)
+    pipe = {k: v for k, v in scratch.items() if "pipe32_kernel" in k}
+    # 2 head sizes x 3 block sizes x (shared prefix, token groups 1 and 2 +
+    # prefill, fp32 and fp16 output, token groups 1 and 2)
+    assert len(pipe) == 36, f"expected 36 pipelined-pass kernels, found {len(pipe)}"
+    spilled = {k: v for k, v in pipe.items() if v}
+    assert not spilled, f"scratch per lane: {spilled}"
