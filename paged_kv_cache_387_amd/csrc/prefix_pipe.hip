@@ -483,11 +483,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
 #pragma unroll
     for (int i = 0; i < NKK; ++i) after_wait(kr[i]);
     lds_read_row<0, VLD, 1024>(ring_addr(slot) + NKK * 1024, vr);
-    __builtin_amdgcn_sched_barrier(0);   // the V reads go out before the work they hide under
     qk(kr, so);
     {
+      // Unconditional, so that no branch splits the step's instructions
+      // (the exponentials then interleave with the q.K MFMAs): past the
+      // walk's end it reloads a clamped, in-pool block into the slot just
+      // freed, which no step reads again.  Loads issued after the step a
+      // wait is for only lengthen that wait.
       const int fslot = slot == 0 ? NR - 1 : slot - 1;
-      if (k + NR - 1 < ns_g) issue(k + NR - 1, fslot, ent);
+      issue(k + NR - 1, fslot, ent);
       entries(k + NR, ent);
     }
     lds_wait();
