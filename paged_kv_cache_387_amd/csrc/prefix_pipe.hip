@@ -406,15 +406,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     asm volatile("" ::: "memory");
   };
 
-  // ---- the walk.  Ring slot of step k: k % NR.  The prologue issues steps
-  // 0 .. NR-2.  (In the pipelined loop the refill of iteration k goes out
-  // after step k+1's q.K MFMAs instead, which keeps the load instructions
-  // off the head of the step; the order of the loads is the same.)  Iteration k waits for step k+1 (loads issued after it: those
-  // of steps k+2 .. k+NR-2 that exist, issued earlier), meets the group at a barrier (every wave
-  // has then finished iteration k-1, so slot (k-1) % NR is free, and every
-  // wave's rows of step k+1 are in LDS), issues step k+NR-1 into the freed
-  // slot, then computes step k's softmax and P.V and step k+1's q.K.
-  // Every wave runs ns_max iterations, so that the barriers match.
+  // ---- the walk.  Ring slot of step k: k % NR.  Iteration k waits for
+  // step k+1's rows, meets the group at a barrier (every wave has then
+  // finished iteration k-1, so slot (k-1) % NR is free, and every wave's rows
+  // of step k+1 are in LDS), issues step k+NR-1 into the freed slot (in the
+  // pipelined loop after step k+1's q.K MFMAs, which keeps the load
+  // instructions off the head of the step), then computes step k's softmax
+  // and P.V and step k+1's q.K.  The prologue issues steps 0 .. NR-2 and
+  // each pipelined iteration one step, whether or not they exist, so that
+  // there the loads behind step k+1 are always one step's; the masked tail
+  // issues only real steps and counts them exactly.  Every wave runs ns_max
+  // iterations, so that the barriers match.
   // Waits for a step whose rows have `after` later steps' rows issued behind
   // them (loads complete in issue order; table loads issued since only make
   // the wait longer).  The count must not exceed what was really issued
@@ -429,14 +431,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
       default: wait_vmcnt<4 * LPW>(); break;
     }
   };
+  // The prologue issues its NR - 1 steps unconditionally: a step past the
+  // walk reloads an in-pool block into a slot no step reads.
 #pragma unroll
-  for (int j = 0; j < NR - 1; ++j)
-    if (j < ns_g) {
-      entries(j, ent);
-      issue(j, j, ent);
-    }
+  for (int j = 0; j < NR - 1; ++j) {
+    entries(j, ent);
+    issue(j, j, ent);
+  }
   entries(NR - 1, ent);
-  if (ns_g > 0) wait_step(min(NR - 2, ns_g - 1));
+  wait_vmcnt<(NR - 2) * LPW>();
   barrier();
   f16v S[NB2];
   if (!idle && ns_g > 0) {
@@ -473,7 +476,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   auto fast_step = [&](int k, int slot, f16v *si, f16v *so) {
     const int nslot = slot + 1 == NR ? 0 : slot + 1;
     const int t0 = (first + 2 * (tgi + TG * k)) * kTile;
-    if (k + 1 < ns_g) wait_step(min(NR - 3, ns_g - 2 - k));
+    // the prologue issues NR - 1 steps and every pipelined iteration one,
+    // whether or not they exist: one step's loads are always behind step
+    // k+1's here
+    wait_vmcnt<(NR - 3) * LPW>();
     barrier();
     u4 kr[NKK], vr[VLD];
     lds_read_row<0, NKK, 1024>(ring_addr(nslot), kr);
