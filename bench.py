@@ -419,7 +419,7 @@ def bench_prefill(args, torch, pkv, driver) -> int:
     (paged_kv_write) and its queries' causal attention over the cache
     (paged_attention_prefill), captured in a graph."""
     from synth import workloads as W
-    w = W.chunked_prefill()
+    w = W.chunked_prefill(cache_dtype=args.kv_dtype)
     if args.block_size != 16:
         w = W.with_block_size(w, args.block_size)
     K, Wm = args.steps, args.warmup
@@ -897,6 +897,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="rotating batches (0: default)")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="tokens per physical block (the pool keeps its token capacity)")
+    ap.add_argument("--kv-dtype", default="f16", choices=("f16", "i8", "e4m3"),
+                    help="cache dtype of the prefill workload")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--shared", action="store_true",
                     help="decode through paged_attention_decode_shared: sequences that "

@@ -28,6 +28,12 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I" + INCL
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE]
+# The multi-query passes keep their accumulators, q and scores in the unified
+# register file: with the MFMA results in VGPRs (the instruction's VGPR form)
+# the softmax reads the scores without a copy per element, and the quantized
+# passes fit without scratch.  The decode kernels hold no AGPRs either way.
+SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+                for src in ("prefix.hip", "prefix_pipe.hip")}
 
 
 def _run(cmd):
@@ -42,7 +48,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OBJ_DIR, src + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(OBJ_DIR, src + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])

@@ -13,7 +13,10 @@ paged_kv_cache_387_amd.build) with the ROCm LLVM tools and requires:
     register budget is full (a few spilled scalars, not the ring);
   * no scratch in any build of the pipelined fp16 multi-query pass (its
     accumulators, q and the scores of two steps fill both register files; a
-    spill there reloads q from scratch at every MFMA).
+    spill there reloads q from scratch at every MFMA);
+  * no scratch in the int8 / E4M3 multi-query pass and the fp32-cache one
+    (with their MFMA results in VGPRs they fit; built with AGPR results the
+    head-dim-128 ones spilled 140-200 bytes per lane).
 Skipped when the build objects or the tools are absent.
 """
 import os
@@ -76,4 +79,14 @@ def test_multi_query_pass_keeps_its_state_in_registers(tmp_path):
     # prefill, fp32 and fp16 output, token groups 1 and 2)
     assert len(pipe) == 36, f"expected 36 pipelined-pass kernels, found {len(pipe)}"
     spilled = {k: v for k, v in pipe.items() if v}
+    assert not spilled, f"scratch per lane: {spilled}"
+
+
+def test_quantized_multi_query_pass_keeps_its_state_in_registers(tmp_path):
+    scratch = _kernel_scratch(os.path.join(OBJ_DIR, "prefix.hip.o"), tmp_path)
+    passes = {k: v for k, v in scratch.items() if "prefix32_kernel" in k or "prefix_kernel" in k}
+    # prefix32_kernel: 2 cache dtypes x 2 head sizes x 3 block sizes x (shared
+    # prefix, prefill); prefill once per output dtype; prefix_kernel: fp32 caches
+    assert len(passes) == 42, f"expected 42 multi-query kernels, found {len(passes)}"
+    spilled = {k: v for k, v in passes.items() if v}
     assert not spilled, f"scratch per lane: {spilled}"
