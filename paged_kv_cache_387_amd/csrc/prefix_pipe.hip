@@ -455,7 +455,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     if (k + 1 < ns_g) wait_step(min(NR - 3, ns_g - 2 - k));
     barrier();
     if (k + NR - 1 < ns_g) issue(k + NR - 1, fslot, ent);
-    entries(k + NR, ent);
   };
   // Steps 0 .. nfast-1 have a next step and no masks: the last steps of a
   // walk are the only ones that can hold a missing second tile (the last) or,
@@ -498,11 +497,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
       // wait is for only lengthen that wait.
       const int fslot = slot == 0 ? NR - 1 : slot - 1;
       issue(k + NR - 1, fslot, ent);
-      entries(k + NR, ent);
     }
     lds_wait();
 #pragma unroll
     for (int i = 0; i < VLD; ++i) after_wait(vr[i]);
+    // Scalar and LDS loads share one wait counter: the next entries are
+    // requested after the wait for the V rows, so that the next wait on that
+    // counter (the next step's K rows) is a step away.
+    entries(k + NR, ent);
     pv(IC<0>{}, vr, pb, t0);
     return nslot;
   };
@@ -552,6 +554,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
         qk(kr, S);
       }
     }
+    entries(k + NR, ent);   // after this step's LDS waits (see the pipelined step)
     slot = nslot;
   }
 
