@@ -103,13 +103,15 @@ def test_prefill_one_token_is_the_decode():
     check_close(a, b.double().cpu().numpy(), "f16", "prefill(q_len=1) vs decode")
 
 
-def test_prefill_full_size_sampled():
+@pytest.mark.parametrize("cache_dtype", ["f16", "i8", "e4m3"])
+def test_prefill_full_size_sampled(cache_dtype):
     """8 sequences of 1536 cached + 512 new tokens (64/8 heads, d 128): the
-    benchmark's shape; 64 query rows checked against the oracle."""
+    benchmark's shape, over each cache dtype it times; 64 query rows checked
+    against the oracle."""
     import paged_kv_cache_387_amd as pkv
     import hip_replay as driver
     pkv.lib()
-    w = W.chunked_prefill()
+    w = W.chunked_prefill(cache_dtype=cache_dtype)
     ro = oracle_replay(w)
     rg = driver.replay(w)
     out = driver.prefill(rg, w)
@@ -123,4 +125,5 @@ def test_prefill_full_size_sampled():
     lens = np.array([ro.seq_lens[s] - w.q_lens[s] + (r - offs[s]) + 1
                      for r, s in zip(rows, seq_of)], np.int32)
     ref, _ = oracle.decode(ro.pools, ro.q[rows], tables, lens, np.float32(w.scale))
-    check_close(out[torch.from_numpy(rows).cuda()], ref, "f16", "chunked prefill sampled rows")
+    check_close(out[torch.from_numpy(rows).cuda()], ref, cache_dtype,
+                f"chunked prefill sampled rows, {cache_dtype} cache")
