@@ -165,20 +165,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
   // largest dot product.
   const float ks = fabsf(p.qk_scale);
   const uint32_t qneg = p.qk_scale < 0.0f ? 0x80008000u : 0u;
+  // q is requested here and moved into place after the ring's first steps
+  // are requested, so that the two round trips overlap.
+  u4 qraw[NB2][NKK];
   h8 qf[NB2][NKK];
 #pragma unroll
   for (int nb = 0; nb < NB2; ++nb) {
     const _Float16 *qr = reinterpret_cast<const _Float16 *>(p.q) +
                          ((size_t)col_seq[nb] * H + col_head[nb]) * D;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      u4 raw = load16(reinterpret_cast<const uint8_t *>(qr + 16 * kk + 8 * h));
-      raw ^= u4{qneg, qneg, qneg, qneg};
-      // q stays in accumulation registers (the MFMAs read their B operand
-      // from there), leaving the vector registers to the walk's working set
-      asm volatile("" : "+a"(raw));
-      qf[nb][kk] = __builtin_bit_cast(h8, raw);
-    }
+    for (int kk = 0; kk < NKK; ++kk)
+      qraw[nb][kk] = load16(reinterpret_cast<const uint8_t *>(qr + 16 * kk + 8 * h));
   }
 
   float m[NB2], l[NB2];
@@ -439,6 +436,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void pipe32_kernel(PrefixParams p) 
     issue(j, j, ent);
   }
   entries(NR - 1, ent);
+  // Every q load is issued before the first move: each move is a scheduling
+  // barrier, and a load after one would wait for the load before it.
+#pragma unroll
+  for (int nb = 0; nb < NB2; ++nb)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u4 r = qraw[nb][kk] ^ u4{qneg, qneg, qneg, qneg};
+      // q stays in accumulation registers (the MFMAs read their B operand
+      // from there), leaving the vector registers to the walk's working set
+      asm volatile("" : "+a"(r));
+      qf[nb][kk] = __builtin_bit_cast(h8, r);
+    }
   wait_vmcnt<(NR - 2) * LPW>();
   barrier();
   f16v S[NB2];
