@@ -35,25 +35,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const bool stream = p.walk == kWalkStream;
   int np = 0, npre = 0, fw = 0, hh = 0;
   bool zero_row = false;
+  // The row's records are requested together, not one after the other.
   if (live_row) {
     const int s = row / p.num_heads;
-    int L = p.seq_lens[s];
     if (stream) {
       // a unit's pieces: slots 2 * fw + 1 (its first piece), then 2 * (fw + j);
-      // the record is read with the length (it is stale for an empty sequence)
+      // the record (one 8-byte word: the workspace and the record's offset in
+      // it are 256-byte aligned) is read with the length (it is stale for an
+      // empty sequence)
       const int h = row - s * p.num_heads;
       hh = h % p.group;
       const int u = s * p.num_kv_heads + h / p.group;
-      fw = p.ws_info[2 * u];
-      np = p.ws_info[2 * u + 1];
+      const int L = p.seq_lens[s];
+      const int2 rec = *reinterpret_cast<const int2 *>(p.ws_info + 2 * u);
+      fw = rec.x;
       zero_row = L <= 0;
-      if (zero_row || fw < 0 || fw >= p.stream_waves) np = 0;
+      const bool none = zero_row | (fw < 0) | (fw >= p.stream_waves);
+      np = none ? 0 : rec.y;
       np = np < p.stream_waves - fw ? np : p.stream_waves - fw;
     } else {
+      int L = p.seq_lens[s];
+      const int g = p.seq_group != nullptr ? p.seq_group[s] : -1;
       L = L < 0 ? 0 : (L > p.max_blocks * p.block_size ? p.max_blocks * p.block_size : L);
       const int ntile = (L + kTile - 1) / kTile;
       np = (ntile + p.part_tiles - 1) / p.part_tiles;
-      npre = prefix_parts_of(p, s);
+      npre = prefix_parts_of_group(p, g);
     }
   }
   // rows with one partition (or piece) and no prefix were written by the
@@ -65,17 +71,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   if (merge) {
     const size_t base = (size_t)row * p.ws_stride;
     const f4 *o = reinterpret_cast<const f4 *>(p.ws_o) + dv;
-#pragma unroll 4
-    for (int q = qg; q < nq; q += QG) {
-      const size_t fi = stream ? (size_t)(2 * (fw + q) + (q == 0 ? 1 : 0)) * p.group + hh
-                               : base + (q < np ? q : p.ws_pre + (q - np));
-      const float lq = p.ws_lse[fi];
-      const f4 oq = o[fi * (D / 4)];
-      const float mn = fmaxf(m, lq);
-      const float a = exp2f(m - mn), b = exp2f(lq - mn);
-      acc = acc * a + oq * b;
-      z = z * a + b;
-      m = mn;
+    // kChunk partials at a time, their loads issued together (a guard per
+    // partial would make each load wait for the one before): a slot past the
+    // row's last partial reads that partial again and its term is dropped.
+    constexpr int kChunk = 8;
+    for (int q0 = qg; q0 < nq; q0 += kChunk * QG) {
+      float lq[kChunk];
+      f4 oq[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const int q = min(q0 + j * QG, nq - 1);
+        const size_t fi = stream ? (size_t)(2 * (fw + q) + (q == 0 ? 1 : 0)) * p.group + hh
+                                 : base + (q < np ? q : p.ws_pre + (q - np));
+        lq[j] = p.ws_lse[fi];
+        oq[j] = o[fi * (D / 4)];
+      }
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (q0 + j * QG < nq) {
+          const float mn = fmaxf(m, lq[j]);
+          const float a = exp2f(m - mn), b = exp2f(lq[j] - mn);
+          acc = acc * a + oq[j] * b;
+          z = z * a + b;
+          m = mn;
+        }
+      }
     }
   }
   if constexpr (QG > 1) {

@@ -139,16 +139,18 @@ struct PrefixParams {
 };
 
 // Prefix partials of sequence s (0: none).  Used identically by the decode
-// kernel (which then never writes `out` directly) and the merge.
-__device__ inline int prefix_parts_of(const DecodeParams &p, int s) {
-  if (p.seq_group == nullptr) return 0;
-  const int g = p.seq_group[s];
+// kernel (which then never writes `out` directly) and the merge; the merge
+// reads s's group (its seq_group entry, -1 for none) itself, with the length.
+__device__ inline int prefix_parts_of_group(const DecodeParams &p, int g) {
   if ((unsigned)g >= (unsigned)p.num_groups) return 0;
   int len = p.group_prefix_lens[g];
   const int cap = p.max_prefix_blocks * p.block_size;
   len = len < 0 ? 0 : (len > cap ? cap : len);
   const int tiles = len / kTile;
   return (tiles + p.pp_tiles - 1) / p.pp_tiles;
+}
+__device__ inline int prefix_parts_of(const DecodeParams &p, int s) {
+  return p.seq_group == nullptr ? 0 : prefix_parts_of_group(p, p.seq_group[s]);
 }
 
 // Workgroups land on a die's compute units roughly round robin by id, and
