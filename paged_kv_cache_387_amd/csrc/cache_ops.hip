@@ -39,6 +39,70 @@ __global__ __launch_bounds__(64) void write_kernel(WriteParams p) {
                                p.v_scale ? p.v_scale + sidx : nullptr, t, threadIdx.x);
 }
 
+// fp16 caches, sources on 16-byte rows: a workgroup takes TB = min(BS, 16)
+// consecutive tokens of one kv head.  When their slots fill one aligned tile
+// (a chunk of consecutive tokens, as a prefill writes) it gathers the tile's
+// 16-byte K columns and 4-byte V columns from the token rows and stores the
+// tile as whole 16-byte words, consecutive lanes on consecutive words (the
+// layout of k_byte / v_byte).  Otherwise it writes the tokens one by one as
+// write_kernel does.
+template <int D, int BS>
+__global__ __launch_bounds__(64) void write_tiles_kernel(WriteParams p) {
+  constexpr int TB = tile_rows<BS>();
+  constexpr int SLICE = BS * D * 2;     // bytes of a (block, kv head) slice
+  constexpr int TBYTES = TB * D * 2;    // bytes of a tile
+  constexpr int NW = TBYTES / 16 / 64;  // 16-byte words per lane, K and V each
+  static_assert(NW >= 1 && TBYTES % (16 * 64) == 0, "tile words");
+  const int i0 = blockIdx.x * TB;
+  const int kvh = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int n = min(TB, p.num_tokens - i0);   // >= 1
+  const int64_t my = lane < n ? p.slots[i0 + lane] : -1;
+  const int64_t slot0 =
+      (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(my >> 32)) << 32) |
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)my));
+  const bool lane_ok = lane >= TB || my == slot0 + lane;
+  const bool full = n == TB && __builtin_amdgcn_ballot_w64(!lane_ok) == 0 && slot0 >= 0 &&
+                    slot0 % TB == 0 && slot0 + TB <= (int64_t)p.num_blocks * BS;
+  if (full) {
+    const size_t base = ((size_t)(slot0 / BS) * p.num_kv_heads + kvh) * SLICE +
+                        (size_t)((slot0 % BS) / TB) * TBYTES;
+    const size_t kst = (size_t)p.key_stride * 2, vst = (size_t)p.value_stride * 2;
+    const uint8_t *k0 = static_cast<const uint8_t *>(p.key) + (size_t)i0 * kst + (size_t)kvh * D * 2;
+    const uint8_t *v0 = static_cast<const uint8_t *>(p.value) + (size_t)i0 * vst + (size_t)kvh * D * 2;
+    u4 kw[NW], vw[NW];
+#pragma unroll
+    for (int r = 0; r < NW; ++r) {
+      const int e = lane + 64 * r;
+      // K word e: 16-byte column e / TB of token e % TB
+      kw[r] = *reinterpret_cast<const u4 *>(k0 + (size_t)(e % TB) * kst + 16 * (e / TB));
+      // V word e: 4-byte column e / (TB/4) of tokens 4 (e % (TB/4)) .. + 3
+      const int pc = e / (TB / 4), u = 4 * (e % (TB / 4));
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        vw[r][k] = *reinterpret_cast<const uint32_t *>(v0 + (size_t)(u + k) * vst + 4 * pc);
+    }
+#pragma unroll
+    for (int r = 0; r < NW; ++r) {
+      reinterpret_cast<u4 *>(p.k_cache + base)[lane + 64 * r] = kw[r];
+      reinterpret_cast<u4 *>(p.v_cache + base)[lane + 64 * r] = vw[r];
+    }
+    return;
+  }
+  for (int j = 0; j < n; ++j) {
+    const int i = i0 + j;
+    const int64_t slot = p.slots[i];
+    if (slot < 0 || slot >= (int64_t)p.num_blocks * BS) continue;
+    const int64_t blk = slot / BS;
+    const int t = (int)(slot % BS);
+    const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * SLICE;
+    const uint8_t *k_row = static_cast<const uint8_t *>(p.key) + ((size_t)i * p.key_stride + (size_t)kvh * D) * 2;
+    const uint8_t *v_row = static_cast<const uint8_t *>(p.value) + ((size_t)i * p.value_stride + (size_t)kvh * D) * 2;
+    write_token_wave<PKV_F16, PKV_F16, D, BS>(k_row, v_row, p.k_cache + tile, p.v_cache + tile,
+                                              nullptr, nullptr, t, lane);
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
   const int32_t src = p.pairs[2 * blockIdx.x];
   const int32_t dst = p.pairs[2 * blockIdx.x + 1];
@@ -98,8 +162,25 @@ __global__ __launch_bounds__(256) void swap_kernel(SwapParams p) {
   }
 }
 
+template <int D>
+hipError_t launch_write_tiles(const WriteParams &p, hipStream_t stream) {
+  const int tb = p.block_size < 16 ? p.block_size : 16;
+  dim3 grid((p.num_tokens + tb - 1) / tb, p.num_kv_heads);
+  switch (p.block_size) {
+    case 8: hipLaunchKernelGGL((write_tiles_kernel<D, 8>), grid, dim3(64), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((write_tiles_kernel<D, 32>), grid, dim3(64), 0, stream, p); break;
+    default: hipLaunchKernelGGL((write_tiles_kernel<D, 16>), grid, dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 template <int SRC, int KV, int D>
 hipError_t launch_write_bs(const WriteParams &p, hipStream_t stream) {
+  if constexpr (SRC == PKV_F16 && KV == PKV_F16) {
+    const auto on16 = [](const void *a) { return (reinterpret_cast<uintptr_t>(a) & 15u) == 0; };
+    if (on16(p.key) && on16(p.value) && p.key_stride % 8 == 0 && p.value_stride % 8 == 0)
+      return launch_write_tiles<D>(p, stream);
+  }
   dim3 grid(p.num_tokens, p.num_kv_heads);
   switch (p.block_size) {
     case 8: hipLaunchKernelGGL((write_kernel<SRC, KV, D, 8>), grid, dim3(64), 0, stream, p); break;
