@@ -64,6 +64,39 @@ def test_write_bit_exact(pkv, src, cache_dt, D, Hkv):
     check_pools_equal(cache, pools, f"write {src}->{cache_dt}")
 
 
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("D,Hkv", [(64, 2), (128, 8)])
+def test_write_whole_tiles(pkv, bs, D, Hkv):
+    """fp16 writes whose slots fill whole tiles (stored a tile at a time) next
+    to runs that do not: a tile-aligned run of three tiles, a run starting
+    inside a tile, a run whose middle slot is -1, a run reaching past the
+    pool, and a tile-aligned run in reverse order."""
+    say(f"whole-tile writes bs={bs} D={D} Hkv={Hkv}")
+    tb = min(bs, 16)
+    nb = 12
+    cap = nb * bs
+    rng = np.random.default_rng(7 * bs + D)
+    runs = [np.arange(2 * tb, 5 * tb),                   # three aligned tiles
+            np.arange(6 * tb + 3, 7 * tb + 3),           # one tile's worth, unaligned
+            np.arange(8 * tb, 9 * tb),                   # aligned, with a hole below
+            np.arange(cap - tb // 2, cap + tb // 2),     # half past the pool
+            np.arange(10 * tb, 11 * tb)[::-1]]           # aligned, reversed
+    slots = np.concatenate(runs).astype(np.int64)
+    hole = 3 * tb + tb + 5                               # inside the third run
+    slots[hole] = -1
+    T = len(slots)
+    key = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    val = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pools = oracle.Pools(nb, Hkv, D, "f16", block_size=bs)
+    n = oracle.write(pools, key.astype(np.float32), val.astype(np.float32), slots)
+    assert n == T - 1 - tb // 2
+    cache = pkv.PagedKVCache(nb, Hkv, D, "f16", block_size=bs, fill_byte=0xFF)
+    pkv.paged_kv_write(torch.from_numpy(key).cuda(), torch.from_numpy(val).cuda(),
+                       torch.from_numpy(slots).cuda(), cache)
+    torch.cuda.synchronize()
+    check_pools_equal(cache, pools, f"whole-tile writes bs={bs} D={D}")
+
+
 def test_quantizer_exhaustive_fp16_values(pkv):
     """Every finite fp16 value, quantized in rows with several amax values."""
     say("quantizer exhaustive over fp16")
